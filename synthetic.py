@@ -1,0 +1,72 @@
+"""Seeded synthetic inputs for the q6_K x int8 prefill GEMM.
+
+Shared by the tests, the smoke check and the benchmark; it holds none of the method's
+arithmetic: it only draws random bytes and floats with the shapes and value distributions of the
+workloads (uniform ql/qh bytes, int8 sub-block scales in [-32, 31], f16 d = |N(0,1)| * 1e-2, and
+N(0,1) activations, optionally with outlier channels or a post-SwiGLU-like product).
+
+Draw order for a weight set: ql bytes, qh bytes, scales, d.  Activations are drawn from a separate
+generator seeded with ``seed + 10**6`` so weights and activations can be regenerated independently.
+"""
+import numpy as np
+
+QK = 256
+BLOCK_BYTES = 210
+
+# Workloads (N tokens, M output rows, K reduction) and their seeds.
+WORKLOADS = {
+    "tiny": dict(n=64, m=256, k=512, seed=1, x="normal"),
+    "attn_v_n512": dict(n=512, m=4096, k=4096, seed=2, x="normal"),
+    "attn_v_n3314": dict(n=3314, m=4096, k=4096, seed=3, x="outlier"),
+    "ffn_down_n3314": dict(n=3314, m=4096, k=11008, seed=4, x="swiglu"),
+}
+
+
+def weights(m, k, seed, sc_lo=-32, sc_hi=31):
+    """Raw q6_K blocks, uint8 [m][k/256][210].
+
+    Byte map of a block: ql[128] at 0, qh[64] at 128, int8 scales[16] at 192, f16 d at 208."""
+    if k % QK:
+        raise ValueError("k must be a multiple of 256")
+    nsb = k // QK
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ql = rng.integers(0, 256, size=(m, nsb, 128), dtype=np.uint8)
+    qh = rng.integers(0, 256, size=(m, nsb, 64), dtype=np.uint8)
+    sc = rng.integers(sc_lo, sc_hi + 1, size=(m, nsb, 16), dtype=np.int16).astype(np.int8)
+    d = (np.abs(rng.standard_normal(size=(m, nsb))) * 1e-2).astype(np.float16)
+    raw = np.empty((m, nsb, BLOCK_BYTES), np.uint8)
+    raw[:, :, 0:128] = ql
+    raw[:, :, 128:192] = qh
+    raw[:, :, 192:208] = sc.view(np.uint8)
+    raw[:, :, 208:210] = d.astype("<f2").view(np.uint8).reshape(m, nsb, 2)
+    return raw
+
+
+def activations(n, k, seed, kind="normal"):
+    """f32 [n][k] activations.
+
+    normal  : N(0,1)
+    outlier : N(0,1) with round(0.01*k) seeded channels scaled by 20
+    swiglu  : a * silu(b), a, b ~ N(0,1), silu evaluated in f64
+    """
+    rng = np.random.Generator(np.random.PCG64(seed + 10**6))
+    if kind == "normal":
+        return rng.standard_normal(size=(n, k), dtype=np.float32)
+    if kind == "outlier":
+        x = rng.standard_normal(size=(n, k), dtype=np.float32)
+        ch = rng.choice(k, size=int(round(0.01 * k)), replace=False)
+        x[:, ch] *= np.float32(20.0)
+        return x
+    if kind == "swiglu":
+        a = rng.standard_normal(size=(n, k))
+        b = rng.standard_normal(size=(n, k))
+        return (a * (b / (1.0 + np.exp(-b)))).astype(np.float32)
+    raise ValueError(kind)
+
+
+def workload(name):
+    """-> (raw weights, activations, n, m, k) for a named workload."""
+    w = WORKLOADS[name]
+    raw = weights(w["m"], w["k"], w["seed"])
+    x = activations(w["n"], w["k"], w["seed"], w["x"])
+    return raw, x, w["n"], w["m"], w["k"]
