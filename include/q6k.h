@@ -1,0 +1,130 @@
+/*
+ * q6k.h -- C ABI of libq6k.so: the q6_K x int8 prefill GEMM on MI355X (gfx950)
+ *
+ *     Y[N x M] = X[N x K] . dequant(W_q6K[M x K])^T
+ *
+ * Method (page titles of the optimisation log it follows):
+ *   "r38 q6_K BT-style raw-byte mma kernel (LANDED)"
+ *       sec. 2.1  q6_K super-block: 256 weights in 210 B -- ql[128] low nibbles at 0, qh[64] 2-bit
+ *                 high fields at 128, int8 scales[16] at 192 (one per 16 weights), f16 d at 208;
+ *                 w = d * sc[sub-block] * (q - 32)
+ *       sec. 2.2  rescale without a dmin term: acc += da * dsc, dsc = d * sc
+ *       sec. 2.3  expanded B: weights staged as centered int8 (-32..31)
+ *       sec. 2.4  KSPLIT=2: every 32-k chunk is two 16-k halves with their own integer dot and
+ *                 their own d*sc rescale, applied as two independent f32 additions
+ *   "r41 q6_K B-expand widened to uint4 group loads (LANDED)": B expanded from wide loads
+ *   "r53 W_exp pre-expansion plane + cp.async B staging (LANDED)": optional load-time plane of
+ *       centered int8 weights (extra memory, no expand work in the GEMM)
+ *   "r42 stage-wide dsc scale reads (REVERTED)", sec. 3.2 (W_dsc arm): d*sc precomputed as f32
+ *
+ * Conventions for every entry point
+ *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library never allocates,
+ *     frees or retains memory.  `stream` is a hipStream_t (NULL = the null stream).
+ *   - Calls are asynchronous on `stream` and never synchronize.  Arguments are checked on the
+ *     host before anything is launched; on any error nothing is launched and the output buffers
+ *     are untouched.  A fault inside a kernel surfaces at the caller's next synchronization.
+ *   - There is no fallback path: an unsupported request returns an error code.
+ *   - n == 0 or m == 0 is an empty problem: the call returns Q6K_OK and launches nothing.
+ *   - k must be a positive multiple of 256 (whole super-blocks).
+ *   - Buffers read with 16-byte accesses (x, xq, da, w) must be 16-byte aligned; y and dots
+ *     need 4-byte alignment.
+ *
+ * Tiled layouts (produced and consumed only by this library; the byte order is documented so
+ * callers and tests can rebuild the plain [row][k] views):
+ *   token tiles  : NP = n rounded up to 128; tile T holds tokens 32T .. 32T+31
+ *   row tiles    : MP = m rounded up to 128; tile R holds weight rows 32R .. 32R+31
+ *   chunk c      : k range 32c .. 32c+31, nchunk = k/32; half h = 0 (k 0..15) / 1 (k 16..31)
+ *   lane l       : 0..63, position p = l % 32, group g = l / 32
+ *   xq  (int8)   : byte ((T*nchunk + c)*64 + l)*16 + b  holds  Xq[32T + p][32c + 16*(b/8) + 8g + b%8]
+ *   da  (f32)    : float (T*nchunk + c)*32 + 16g + 4q + r  holds  da[32T + 8q + 4g + r][c]
+ *   layout 1 (Q6K_LAYOUT_EXPANDED):
+ *     codes int8 : byte ((R*nchunk + c)*64 + l)*16 + b  holds  q - 32 of row 32R + p at
+ *                  k = 32c + 16*(b/8) + 8g + b%8
+ *     scales f32 : at byte offset MP*k, float ((R*nchunk + c)*32 + p)*2 + h = d*sc[2c + h] of row
+ *                  32R + p (sub-block index counted along the whole row)
+ *   layout 0 (Q6K_LAYOUT_PACKED), 6 bits per weight plus 4 scale bytes per 32 weights:
+ *     codes      : 12 bytes at ((R*nchunk + c)*64 + l)*12 for row 32R + p; with a_e (e = 0..7) the
+ *                  6-bit codes at k = 32c + 8g + e and b_e those at k = 32c + 16 + 8g + e:
+ *                  byte t (t = 0..3)   = (a_t & 15) | (a_{t+4} & 15) << 4
+ *                  byte 4+t            = (b_t & 15) | (b_{t+4} & 15) << 4
+ *                  byte 8+t            = a_t>>4 | (a_{t+4}>>4) << 2 | (b_t>>4) << 4 | (b_{t+4}>>4) << 6
+ *     scales     : at byte offset MP*k*3/4, 4 bytes at ((R*nchunk + c)*32 + p)*4:
+ *                  int8 sc[2c], int8 sc[2c+1], f16 d (little-endian) of row 32R + p
+ *   Padding tokens / rows hold zeros.
+ */
+#ifndef Q6K_H
+#define Q6K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  Q6K_OK = 0,
+  Q6K_EINVAL = -1, /* null pointer, negative size, unknown layout, ld too small */
+  Q6K_ESHAPE = -2, /* k not a positive multiple of 256 */
+  Q6K_EALIGN = -3, /* a pointer or leading dimension breaks the 16-byte alignment rule */
+  Q6K_ESIZE = -4,  /* an output buffer is smaller than the size query returns, or sizes overflow */
+  Q6K_EHIP = -5    /* the HIP runtime rejected a launch */
+} q6k_status;
+
+enum { Q6K_LAYOUT_PACKED = 0, Q6K_LAYOUT_EXPANDED = 1 };
+
+/* Sizes in bytes of the tiled activation buffers for n tokens of k values: returns the size
+ * of xq and stores the size of da in *da_bytes (may be NULL).  Returns 0 for invalid n/k. */
+size_t q6k_act_bytes(int64_t n, int64_t k, size_t* da_bytes);
+
+/* Activation quantize-transpose prepass ("r38 q6_K BT-style raw-byte mma kernel", sec. 2.2 and
+ * 3.2: int8 activations with one scale per token and 32-k chunk, laid out ahead of the GEMM).
+ * For every token t < n and chunk c: amax = max |x|, da = amax / 127 (IEEE f32 division),
+ * q = roundf(x / da) (IEEE f32 division, half away from zero) clamped to [-127, 127]; an
+ * all-zero chunk gives da = 0 and q = 0.
+ *   x       : f32 [n][ldx] row-major, ldx >= k, ldx % 4 == 0, 16-byte aligned
+ *   xq, da  : tiled outputs (see above) of at least the sizes q6k_act_bytes returns
+ * Padding tokens are written as zeros.  Inf/NaN inputs are outside the contract. */
+q6k_status q6k_quantize_act(const float* x, int64_t n, int64_t k, int64_t ldx, void* xq,
+                            size_t xq_bytes, float* da, size_t da_bytes, void* stream);
+
+/* Size in bytes of the weight buffer of an m x k q6_K matrix in `layout`; 0 if invalid. */
+size_t q6k_weight_bytes(int64_t m, int64_t k, int layout);
+
+/* Load-time weight preparation.  Input: raw q6_K blocks, row j's super-block b at byte
+ * (j*(k/256) + b)*210 (byte map of "r38 ..." sec. 2.1; any alignment).  Output: layout 0 (6-bit
+ * codes regrouped for wide loads plus the raw scale bytes; expanded to centered int8 inside the
+ * GEMM, "r41 ..." sec. 2) or layout 1 (centered int8 plane plus f32 d*sc plane, "r53 ..." sec.
+ * 2.3 and the W_dsc plane of "r42 ..." sec. 3.2).  Padding rows are written as zeros. */
+q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layout, void* w_out,
+                              size_t w_out_bytes, void* stream);
+
+/* The GEMM: y[t][j] = sum over 16-k sub-blocks s of da[t][s/2] * (d*sc)[j][s] * D[t][j][s],
+ * D the exact int32 dot of the int8 activations with the centered weights over sub-block s,
+ * accumulated per 32-k chunk as two independent f32 additions ("r38 ..." sec. 2.2, 2.4).
+ *   xq, da  : outputs of q6k_quantize_act for the same n, k
+ *   w       : output of q6k_expand_weights for the same m, k and `layout`
+ *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned; only y[0..n)[0..m) is
+ *             written
+ *   xq, da and w must hold at least the sizes q6k_act_bytes / q6k_weight_bytes return (the
+ *   kernels read whole padded tiles). */
+q6k_status q6k_gemm(const void* xq, const float* da, int64_t n, const void* w, int layout,
+                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
+
+/* Test-only export of the same kernel source: instead of y, stores the int32 sub-block dots
+ * D[t][j][s] (the two KSPLIT halves of every chunk) to dots [n][m][k/16]. */
+q6k_status q6k_gemm_subdots(const void* xq, const float* da, int64_t n, const void* w, int layout,
+                            int64_t m, int64_t k, int32_t* dots, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* q6k_strerror(int status);
+
+/* Liveness counters: number of GEMM launches (q6k_gemm and q6k_gemm_subdots) per layout since
+ * load; out[0] = layout 0, out[1] = layout 1.  Fast-path liveness check in the spirit of
+ * "r53 ..." sec. 3.3 (a path that silently never runs is invisible to parity tests). */
+void q6k_stats(uint64_t out[2]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q6K_H */

@@ -1,0 +1,21 @@
+"""q6_K x int8 prefill GEMM for MI355X (gfx950).
+
+A thin ctypes binding of ``libq6k.so`` (C ABI in ``include/q6k.h``): every function here only
+checks Python-side types, passes device pointers, sizes and the current HIP stream, and raises on
+a non-zero status.  All arithmetic runs in the HIP kernels.  PyTorch is used for device memory
+and streams only.  If the built library is missing, importing the binding raises.
+"""
+from ._lib import (  # noqa: F401
+    LAYOUT_EXPANDED,
+    LAYOUT_PACKED,
+    Q6KError,
+    lib_path,
+    q6k_act_bytes,
+    q6k_expand_weights,
+    q6k_gemm,
+    q6k_gemm_subdots,
+    q6k_quantize_act,
+    q6k_stats,
+    q6k_strerror,
+    q6k_weight_bytes,
+)

@@ -1,0 +1,152 @@
+"""ctypes marshalling for libq6k.so; names match the C entry points of include/q6k.h."""
+import ctypes
+import os
+
+import torch
+
+LAYOUT_PACKED = 0
+LAYOUT_EXPANDED = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "_build", "libq6k.so")
+
+if not os.path.exists(lib_path):
+    raise ImportError(f"libq6k.so is not built ({lib_path}); run __graft_entry__.build()")
+
+_lib = ctypes.CDLL(lib_path)
+_p, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+_lib.q6k_act_bytes.restype = _sz
+_lib.q6k_act_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+_lib.q6k_quantize_act.restype = _int
+_lib.q6k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
+_lib.q6k_weight_bytes.restype = _sz
+_lib.q6k_weight_bytes.argtypes = [_i64, _i64, _int]
+_lib.q6k_expand_weights.restype = _int
+_lib.q6k_expand_weights.argtypes = [_p, _i64, _i64, _int, _p, _sz, _p]
+_lib.q6k_gemm.restype = _int
+_lib.q6k_gemm.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _i64, _p]
+_lib.q6k_gemm_subdots.restype = _int
+_lib.q6k_gemm_subdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
+_lib.q6k_strerror.restype = ctypes.c_char_p
+_lib.q6k_strerror.argtypes = [_int]
+_lib.q6k_stats.restype = None
+_lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+
+EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_weight_bytes", "q6k_expand_weights",
+           "q6k_gemm", "q6k_gemm_subdots", "q6k_strerror", "q6k_stats")
+
+
+class Q6KError(RuntimeError):
+    def __init__(self, status, func):
+        self.status = status
+        super().__init__(f"{func}: {q6k_strerror(status)} (status {status})")
+
+
+def _check(status, func):
+    if status != 0:
+        raise Q6KError(status, func)
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.numel() and not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    return t.data_ptr() if t.numel() else None
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def q6k_strerror(status):
+    return _lib.q6k_strerror(int(status)).decode()
+
+
+def q6k_act_bytes(n, k):
+    """-> (xq bytes, da bytes); (0, 0) for an invalid shape."""
+    da = _sz(0)
+    xb = _lib.q6k_act_bytes(int(n), int(k), ctypes.byref(da))
+    return int(xb), int(da.value)
+
+
+def q6k_weight_bytes(m, k, layout):
+    return int(_lib.q6k_weight_bytes(int(m), int(k), int(layout)))
+
+
+def q6k_quantize_act(x, xq, da, n=None, k=None, ldx=None, stream=None):
+    """x f32 [n][ldx] (device) -> tiled xq (uint8 buffer) and da (f32 buffer)."""
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [n][ldx]")
+    n = x.shape[0] if n is None else n
+    k = x.shape[1] if k is None else k
+    ldx = x.stride(0) if ldx is None else ldx
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x must be row-major")
+    if x.numel() and (n > x.shape[0] or k > x.shape[1]):
+        raise ValueError("n, k exceed the shape of x")
+    _check(_lib.q6k_quantize_act(_ptr(x), n, k, ldx, _ptr(xq), _nbytes(xq), _ptr(da),
+                                 _nbytes(da), _stream(stream)), "q6k_quantize_act")
+
+
+def q6k_expand_weights(w_raw, m, k, layout, w_out, stream=None):
+    """raw q6_K bytes (device uint8, m*(k/256)*210 B) -> prepared weights in `layout`."""
+    if w_raw is not None and w_raw.numel() and _nbytes(w_raw) < m * (k // 256) * 210:
+        raise ValueError("raw weight buffer too small")
+    _check(_lib.q6k_expand_weights(_ptr(w_raw), m, k, layout, _ptr(w_out), _nbytes(w_out),
+                                   _stream(stream)), "q6k_expand_weights")
+
+
+def _check_operands(xq, da, n, w, layout, m, k):
+    """The C GEMM entry points take no buffer sizes: check them here before passing pointers."""
+    if n <= 0 or m <= 0:
+        return
+    xb, db = q6k_act_bytes(n, k)
+    wb = q6k_weight_bytes(m, k, layout)
+    if xb == 0 or wb == 0:
+        return  # the library reports the shape / layout error itself
+    if _nbytes(xq) < xb or _nbytes(da) < db:
+        raise ValueError(f"activation buffers too small: need {xb} + {db} bytes")
+    if _nbytes(w) < wb:
+        raise ValueError(f"weight buffer too small: need {wb} bytes for layout {layout}")
+
+
+def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None):
+    """y f32 [n][ldy] = GEMM of prepared activations and weights."""
+    if y is not None and y.dtype != torch.float32:
+        raise TypeError("y must be float32")
+    if ldy is None:
+        ldy = y.stride(0) if y is not None and y.dim() == 2 else m
+    _check_operands(xq, da, n, w, layout, m, k)
+    if y is not None and n > 0 and m > 0 and y.numel() < (n - 1) * ldy + m:
+        raise ValueError("y too small for n x ldy")
+    _check(_lib.q6k_gemm(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(y), ldy,
+                         _stream(stream)), "q6k_gemm")
+
+
+def q6k_gemm_subdots(xq, da, n, w, layout, m, k, dots, stream=None):
+    """Test-only: int32 sub-block dots [n][m][k/16] from the GEMM kernel source."""
+    if dots is not None and dots.dtype != torch.int32:
+        raise TypeError("dots must be int32")
+    _check_operands(xq, da, n, w, layout, m, k)
+    if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 16):
+        raise ValueError("dots too small for n x m x k/16")
+    _check(_lib.q6k_gemm_subdots(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(dots),
+                                 _stream(stream)), "q6k_gemm_subdots")
+
+
+def q6k_stats():
+    out = (ctypes.c_uint64 * 2)()
+    _lib.q6k_stats(out)
+    return int(out[0]), int(out[1])

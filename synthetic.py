@@ -60,7 +60,12 @@ def activations(n, k, seed, kind="normal"):
     if kind == "swiglu":
         a = rng.standard_normal(size=(n, k))
         b = rng.standard_normal(size=(n, k))
-        return (a * (b / (1.0 + np.exp(-b)))).astype(np.float32)
+        t = np.negative(b)
+        np.exp(t, out=t)
+        t += 1.0
+        np.divide(b, t, out=b)  # silu(b) = b / (1 + exp(-b)), in f64
+        b *= a
+        return b.astype(np.float32)
     raise ValueError(kind)
 
 

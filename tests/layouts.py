@@ -1,0 +1,62 @@
+"""Test-side views of the library's tiled buffers (byte order as documented in include/q6k.h).
+
+These only reorder bytes; they hold none of the method's arithmetic.
+"""
+import numpy as np
+
+
+def round_up(v, q):
+    return (v + q - 1) // q * q
+
+
+def untile_xq(buf, n, k):
+    """tiled xq bytes -> int8 [NP][k] (NP = n rounded up to 128)."""
+    np_ = round_up(n, 128)
+    nchunk = k // 32
+    t = np.asarray(buf, np.uint8)[: np_ * k].view(np.int8).reshape(np_ // 32, nchunk, 2, 32, 2, 8)
+    # axes: T, c, g, p, h, e  ->  token 32T + p, k = 32c + 16h + 8g + e
+    return t.transpose(0, 3, 1, 4, 2, 5).reshape(np_, k)
+
+
+def untile_da(buf, n, k):
+    """tiled da floats -> f32 [NP][k/32]."""
+    np_ = round_up(n, 128)
+    nchunk = k // 32
+    t = np.asarray(buf, np.float32)[: np_ * nchunk].reshape(np_ // 32, nchunk, 2, 4, 4)
+    # axes: T, c, g, q, r -> token 32T + 8q + 4g + r
+    return t.transpose(0, 3, 2, 4, 1).reshape(np_, nchunk)
+
+
+def untile_expanded(buf, m, k):
+    """layout 1 bytes -> (codes int8 [MP][k], dsc f32 [MP][k/16])."""
+    mp = round_up(m, 128)
+    nchunk = k // 32
+    b = np.asarray(buf, np.uint8)
+    codes = b[: mp * k].view(np.int8).reshape(mp // 32, nchunk, 2, 32, 2, 8)
+    codes = codes.transpose(0, 3, 1, 4, 2, 5).reshape(mp, k)
+    sc = b[mp * k: mp * k + mp * (k // 16) * 4].view(np.float32).reshape(mp // 32, nchunk, 32, 2)
+    dsc = sc.transpose(0, 2, 1, 3).reshape(mp, k // 16)
+    return codes, dsc
+
+
+def untile_packed(buf, m, k):
+    """layout 0 bytes -> (6-bit codes uint8 [MP][k], sc int8 [MP][k/16], d-bits uint16 [MP][k/32])."""
+    mp = round_up(m, 128)
+    nchunk = k // 32
+    b = np.asarray(buf, np.uint8)
+    nb = mp * k * 3 // 4
+    w = b[:nb].reshape(mp // 32, nchunk, 2, 32, 3, 4).astype(np.int32)  # T,c,g,p,word,byte
+    n0, n1, h = w[..., 0, :], w[..., 1, :], w[..., 2, :]
+    a = np.zeros(n0.shape[:-1] + (8,), np.int32)
+    bb = np.zeros_like(a)
+    a[..., 0:4] = (n0 & 15) | (((h >> 0) & 3) << 4)
+    a[..., 4:8] = ((n0 >> 4) & 15) | (((h >> 2) & 3) << 4)
+    bb[..., 0:4] = (n1 & 15) | (((h >> 4) & 3) << 4)
+    bb[..., 4:8] = ((n1 >> 4) & 15) | (((h >> 6) & 3) << 4)
+    full = np.stack([a, bb], axis=4)  # T,c,g,p,h,e
+    codes = full.transpose(0, 3, 1, 4, 2, 5).reshape(mp, k).astype(np.uint8)
+    s = b[nb: nb + mp * nchunk * 4].reshape(mp // 32, nchunk, 32, 4).transpose(0, 2, 1, 3)
+    s = s.reshape(mp, nchunk, 4)
+    sc = s[:, :, 0:2].reshape(mp, k // 16).view(np.int8)
+    dbits = s[:, :, 2:4].copy().view("<u2").reshape(mp, nchunk)
+    return codes, sc, dbits

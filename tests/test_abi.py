@@ -1,0 +1,104 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point declared in
+include/q6k.h, reports sizes, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def lib():
+    from q6_int8_prefill_amd import _lib
+    return _lib._lib
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "q6k.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q6k_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 8, names
+    L = lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_size_queries():
+    import q6_int8_prefill_amd as q6k
+    assert q6k.q6k_act_bytes(1, 256) == (128 * 256, 128 * 8 * 4)
+    assert q6k.q6k_act_bytes(3314, 11008) == (3328 * 11008, 3328 * 344 * 4)
+    assert q6k.q6k_act_bytes(0, 256) == (0, 0)
+    assert q6k.q6k_act_bytes(5, 300) == (0, 0)
+    assert q6k.q6k_weight_bytes(40, 512, 1) == 128 * 512 * 5 // 4
+    assert q6k.q6k_weight_bytes(40, 512, 0) == 128 * 512 * 7 // 8
+    assert q6k.q6k_weight_bytes(4096, 11008, 0) == 4096 * 11008 * 7 // 8
+    assert q6k.q6k_weight_bytes(40, 512, 2) == 0
+    assert q6k.q6k_weight_bytes(40, 0, 1) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 4, 300, 300, FAKE, 1 << 30, FAKE, 1 << 30, None), -2),   # k % 256
+    ((FAKE, -1, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, None), -1),  # n < 0
+    ((None, 4, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, None), -1),   # null x
+    ((FAKE, 4, 256, 255, FAKE, 1 << 30, FAKE, 1 << 30, None), -1),   # ldx < k
+    ((FAKE + 4, 4, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, None), -3),  # misaligned x
+    ((FAKE, 4, 256, 258, FAKE, 1 << 30, FAKE, 1 << 30, None), -3),   # ldx % 4
+    ((FAKE, 4, 256, 256, FAKE, 100, FAKE, 1 << 30, None), -4),       # xq too small
+    ((FAKE, 4, 256, 256, FAKE, 1 << 30, FAKE, 100, None), -4),       # da too small
+    ((None, 0, 256, 256, None, 0, None, 0, None), 0),                # empty: no-op
+])
+def test_quantize_act_errors(args, status):
+    assert lib().q6k_quantize_act(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 4, 256, 2, FAKE, 1 << 30, None), -1),    # unknown layout
+    ((FAKE, 4, 512 + 32, 1, FAKE, 1 << 30, None), -2),
+    ((FAKE + 1, 4, 256, 1, FAKE, 1 << 30, None), -3),  # raw must be 2-byte aligned
+    ((FAKE, 4, 256, 1, FAKE + 8, 1 << 30, None), -3),
+    ((FAKE, 4, 256, 1, FAKE, 10, None), -4),
+    ((None, 4, 256, 0, FAKE, 1 << 30, None), -1),
+    ((None, 0, 256, 0, None, 0, None), 0),
+])
+def test_expand_errors(args, status):
+    assert lib().q6k_expand_weights(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 4, FAKE, 3, 8, 256, FAKE, 8, None), -1),      # layout
+    ((FAKE, FAKE, 4, FAKE, 1, 8, 0, FAKE, 8, None), -2),        # k = 0
+    ((FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE, 7, None), -1),      # ldy < m
+    ((FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE + 2, 8, None), -3),  # y not 4-byte aligned
+    ((FAKE, FAKE + 4, 4, FAKE, 1, 8, 256, FAKE, 10, None), -3),  # misaligned da
+    ((FAKE + 8, FAKE, 4, FAKE, 1, 8, 256, FAKE, 8, None), -3),
+    ((None, FAKE, 4, FAKE, 1, 8, 256, FAKE, 8, None), -1),
+    ((FAKE, FAKE, 4, FAKE, 1, 8, 256, None, 8, None), -1),
+    ((FAKE, FAKE, 0, FAKE, 1, 8, 256, FAKE, 8, None), 0),       # n = 0: no-op
+    ((FAKE, FAKE, 4, FAKE, 1, 0, 256, FAKE, 8, None), 0),       # m = 0: no-op
+    ((FAKE, FAKE, -4, FAKE, 1, 8, 256, FAKE, 8, None), -1),
+])
+def test_gemm_errors(args, status):
+    assert lib().q6k_gemm(*args) == status
+
+
+def test_subdots_errors():
+    L = lib()
+    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, None, None) == -1
+    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE + 2, None) == -3
+    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 100, FAKE, None) == -2
+
+
+def test_strerror_and_stats():
+    import q6_int8_prefill_amd as q6k
+    for s in (0, -1, -2, -3, -4, -5, 42):
+        assert isinstance(q6k.q6k_strerror(s), str) and q6k.q6k_strerror(s)
+    a, b = q6k.q6k_stats()
+    assert a >= 0 and b >= 0

@@ -1,0 +1,147 @@
+"""GPU parity of q6k_gemm / q6k_gemm_subdots against the oracle.
+
+  * per-sub-block int32 dots: bit-exact (the KSPLIT=2 halves of "r38 q6_K BT-style raw-byte mma
+    kernel", sec. 2.4), exported by the same kernel source;
+  * outputs: |y - y_ref| <= 1e-3 * sum|terms| per element, for every element at sizes the
+    oracle runs in seconds and on sampled tokens (all rows) at the full workload sizes, in the
+    launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+LAYOUTS = [0, 1]
+
+
+def prepare(x, raw, m, layout):
+    import gpu_util
+    n, k = x.shape
+    xq, da = gpu_util.quantize(x)
+    w = gpu_util.expand(raw, m, k, layout)
+    return xq, da, w
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("n,m,k", [(64, 256, 512), (65, 40, 512), (1, 1, 256), (129, 130, 768),
+                                   (33, 200, 1024)])
+def test_subdots_bit_exact(layout, n, m, k):
+    import gpu_util
+    print(f"subdots layout={layout} n={n} m={m} k={k}", flush=True)
+    raw = synthetic.weights(m, k, seed=n + m + k, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=n * m, kind="outlier")
+    xq, da, w = prepare(x, raw, m, layout)
+    got = gpu_util.subdots(xq, da, n, w, layout, m, k)
+    xq_ref, _ = oracle.quantize(x)
+    np.testing.assert_array_equal(got, oracle.subdots(xq_ref, raw, m))
+
+
+def test_subdots_extreme_magnitude():
+    # D = 16 * 127 * (-32) = -65024, the largest |D|: all codes 0 against xq = 127
+    import gpu_util
+    n, m, k = 32, 32, 256
+    raw = np.zeros((m, 1, 210), np.uint8)
+    raw[:, 0, 208:210] = (0x00, 0x3C)
+    x = np.full((n, k), 5.0, np.float32)
+    for layout in LAYOUTS:
+        xq, da, w = prepare(x, raw, m, layout)
+        got = gpu_util.subdots(xq, da, n, w, layout, m, k)
+        assert (got == -65024).all()
+        y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+        xq_ref, da_ref = oracle.quantize(x)
+        y_ref, _ = oracle.gemm(xq_ref, da_ref, raw, m)
+        np.testing.assert_array_equal(y, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("n,m,k,kind,wide", [(64, 256, 512, "normal", False),
+                                             (65, 40, 512, "outlier", True),
+                                             (1, 1, 256, "normal", True),
+                                             (129, 130, 768, "swiglu", True),
+                                             (200, 384, 2048, "outlier", False)])
+def test_gemm_small_every_output(layout, n, m, k, kind, wide):
+    import gpu_util
+    print(f"gemm layout={layout} n={n} m={m} k={k}", flush=True)
+    raw = synthetic.weights(m, k, seed=k + 3 * m, sc_lo=-128 if wide else -32,
+                            sc_hi=127 if wide else 31)
+    x = synthetic.activations(n, k, seed=n + 11, kind=kind)
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+    xq_ref, da_ref = oracle.quantize(x)
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y, y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_sparse_and_zero_inputs(layout):
+    # degenerate inputs: a single nonzero activation per token, an all-zero token, zero d
+    import gpu_util
+    n, m, k = 40, 72, 512
+    raw = synthetic.weights(m, k, seed=77, sc_lo=-128, sc_hi=127)
+    raw.reshape(m, 2, 210)[5, 1, 208:210] = 0  # d = 0 for one super-block
+    x = np.zeros((n, k), np.float32)
+    for t in range(n - 1):
+        x[t, (37 * t) % k] = (t - 20) * 0.37 + 0.01
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+    xq_ref, da_ref = oracle.quantize(x)
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y, y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+    assert (y[n - 1] == 0).all()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_leading_dimension_untouched_tail(layout):
+    import gpu_util
+    n, m, k, ldy = 70, 50, 512, 64
+    raw = synthetic.weights(m, k, seed=5)
+    x = synthetic.activations(n, k, seed=5)
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k, ldy=ldy)
+    assert np.isnan(y[:, m:]).all()
+    xq_ref, da_ref = oracle.quantize(x)
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y[:, :m], y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+
+
+def test_liveness_counters_tick_per_layout():
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 32, 32, 256
+    raw = synthetic.weights(m, k, seed=1)
+    x = synthetic.activations(n, k, seed=1)
+    for layout in LAYOUTS:
+        xq, da, w = prepare(x, raw, m, layout)
+        before = q6k.q6k_stats()
+        gpu_util.gemm(xq, da, n, w, layout, m, k)
+        after = q6k.q6k_stats()
+        assert after[layout] == before[layout] + 1 and after[1 - layout] == before[1 - layout]
+
+
+def sampled_tokens(n, count, seed):
+    rng = np.random.default_rng(seed)
+    idx = set(rng.choice(n, size=count - 3, replace=False).tolist()) | {0, n - 1, n // 2}
+    return np.array(sorted(idx))
+
+
+@pytest.mark.parametrize("name", ["attn_v_n512", "attn_v_n3314", "ffn_down_n3314"])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_full_size_sampled(name, layout):
+    """Full workload shape, the benchmark's launch configuration; every row of W checked for a
+    sample of tokens (first, middle, last and random ones)."""
+    import gpu_util
+    raw, x, n, m, k = gpu_util.cached_workload(name)
+    print(f"full-size gemm {name} layout={layout}", flush=True)
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+    rows = sampled_tokens(n, 24, seed=n + layout)
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y[rows], y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+    assert np.isfinite(y).all()
