@@ -23,8 +23,8 @@
 namespace {
 
 constexpr int kTile = 32;        // MFMA tile edge: 32 tokens x 32 weight rows
-constexpr int kWgTok = 128;      // tokens per GEMM workgroup (4 token tiles)
-constexpr int kWgRow = 128;      // weight rows per GEMM workgroup (4 row tiles)
+constexpr int kWgTok = 128;      // token padding of the tiled activation buffers
+constexpr int kWgRow = 128;      // row padding of the prepared weight buffers (4 row tiles)
 constexpr int kFragBytes = 16;   // per lane per chunk: 8 bytes for half 0, 8 for half 1
 constexpr int kPackBytes = 12;   // layout 0: per lane per chunk, 16 codes of 6 bits
 constexpr int kBiasI = 0x4B400000;      // bit pattern of 1.5 * 2^23
@@ -33,6 +33,9 @@ constexpr float kBiasF = 12582912.0f;   // 1.5 * 2^23
 std::atomic<uint64_t> g_launches[2];
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
@@ -204,10 +207,20 @@ __device__ __forceinline__ uint32_t center4(uint32_t nib, uint32_t fld) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// GEMM.  Workgroup = 4 waves = 128 tokens x 128 weight rows; wave (wt, wr) owns token tiles
-// 4*bx + 2*wt + {0,1} and row tiles 4*by + 2*wr + {0,1}: four 32x32 output tiles, 64 f32
-// accumulators per lane.  Operands come straight from the tiled global buffers (one 16-byte
-// load per lane per tile and chunk for int8 operands).
+// GEMM.  Workgroup = 4 waves = 64 tokens (token tiles 2*bx, 2*bx+1) x 128 weight rows (row tiles
+// 4*by .. 4*by+3).  Wave w computes token tile w%2 against row tiles 2*(w/2) and 2*(w/2)+1: two
+// 32x32 output tiles, 32 f32 accumulators per lane.
+//
+// Staging: a ring of kRing LDS slots, one 32-k chunk of the workgroup's operands per slot.  Each
+// wave fills its share of a slot with gfx950 direct global->LDS loads (global_load_lds_dwordx4,
+// 16 bytes per lane, no registers): row tile w's weight codes and d*sc, and, for waves 0 and 1,
+// token tile w's activations and da.  Loads run kRing-1 chunks ahead of the compute.  Per chunk c
+// a wave waits for its own loads of chunk c+1 (s_waitcnt vmcnt), layout 0 expands its row tile's
+// 6-bit codes of chunk c+1 into centered int8 and forms d*sc in the slot, one workgroup barrier
+// makes the slot visible and frees the slot of chunk c-1, the loads of chunk c+kRing-1 are issued,
+// and chunk c is computed.  LDS reads and writes are inline assembly with explicit waits: the
+// compiler would otherwise wait for every outstanding direct-to-LDS load before each LDS access,
+// which would serialize the ring.
 //
 // Per chunk and output tile: two v_mfma_i32_32x32x16_i8 (halves 0 and 1), each started from the
 // bit pattern of 1.5*2^23 so that the int32 result D is read as the float 1.5*2^23 + D exactly
@@ -219,121 +232,254 @@ __device__ __forceinline__ uint32_t center4(uint32_t nib, uint32_t fld) {
 // Output layout of the MFMA: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4 (a token)
 // and column l%32 (a weight row).
 // ---------------------------------------------------------------------------------------------
+#ifndef Q6K_WG_PER_CU
+#define Q6K_WG_PER_CU 4
+#endif
+constexpr int kWgTokTiles = 2;   // token tiles per workgroup
+constexpr int kSlotA = 0;        // 2 token tiles x 1 KiB of A fragments
+constexpr int kSlotD = 2048;     // 2 token tiles x 32 da f32
+constexpr int kSlotB = 2304;     // 4 row tiles x 1 KiB of centered int8 B fragments
+constexpr int kSlotS = 6400;     // 4 row tiles x 32 rows x (dsc0, dsc1) f32
+constexpr int kSlotRawB = 7424;  // layout 0: 4 row tiles x 768 B of packed 6-bit codes
+constexpr int kSlotRawS = 10496; // layout 0: 4 row tiles x 32 raw scale words
+
+template <int LAYOUT>
+struct SlotSize {
+  static constexpr int value = LAYOUT == Q6K_LAYOUT_EXPANDED ? 7424 : 11008;
+};
+// LDS slots per workgroup (loads run kRing-1 chunks ahead), sized so that Q6K_WG_PER_CU
+// workgroups fit in the 160 KiB of LDS of a CU.
+template <int LAYOUT>
+struct RingSize {
+  static constexpr int fit = 160 * 1024 / (Q6K_WG_PER_CU * SlotSize<LAYOUT>::value);
+  static constexpr int value = fit > 6 ? 6 : fit;
+  static_assert(value >= 3, "the ring needs at least 3 slots");
+};
+// direct-to-LDS load instructions per chunk: waves 0, 1 load A, da, B, d*sc; waves 2, 3 B, d*sc
+__device__ __forceinline__ constexpr int loads_per_chunk(bool loads_a) { return loads_a ? 4 : 2; }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)(p);
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* gsrc, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc), (lds_void_t*)(lds_wave_base), 16, 0, 0);
+}
+
+// Issue this wave's loads of chunk c (already clamped to a valid chunk) into `slot`.
+template <int LAYOUT>
+__device__ __forceinline__ void issue_chunk(uint8_t* slot, const uint8_t* a_src,
+                                            const uint8_t* b_src, const uint8_t* s_src,
+                                            const uint8_t* d_src, int64_t c, int wave, int lane) {
+  if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
+    dma16(b_src + c * 1024 + lane * 16, slot + kSlotB + wave * 1024);
+    if (lane < 16) dma16(s_src + c * 256 + lane * 16, slot + kSlotS + wave * 256);
+  } else {
+    if (lane < 48) dma16(b_src + c * 768 + lane * 16, slot + kSlotRawB + wave * 768);
+    if (lane < 8) dma16(s_src + c * 128 + lane * 16, slot + kSlotRawS + wave * 128);
+  }
+  if (wave < kWgTokTiles) {
+    dma16(a_src + c * 1024 + lane * 16, slot + kSlotA + wave * 1024);
+    if (lane < 8) dma16(d_src + c * 128 + lane * 16, slot + kSlotD + wave * 128);
+  }
+}
+
+// s_waitcnt vmcnt(chunks * loads of this wave per chunk)
+template <int CHUNKS>
+__device__ __forceinline__ void wait_chunks(bool loads_a) {
+  if (loads_a)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 4) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 2) : "memory");
+}
+
+// Layout 0: expand row tile `wave` of a slot from packed 6-bit codes and raw scale bytes.
+__device__ __forceinline__ void expand_slot(uint8_t* slot, int wave, int lane) {
+  const uint32_t raw = lds_addr(slot + kSlotRawB + wave * 768 + lane * 12);
+  const uint32_t rsc = lds_addr(slot + kSlotRawS + wave * 128 + (lane & 31) * 4);
+  uint32_t n0, n1, h, s;
+  asm volatile(
+      "ds_read_b32 %0, %4\n\t"
+      "ds_read_b32 %1, %4 offset:4\n\t"
+      "ds_read_b32 %2, %4 offset:8\n\t"
+      "ds_read_b32 %3, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(n0), "=&v"(n1), "=&v"(h), "=&v"(s)
+      : "v"(raw), "v"(rsc)
+      : "memory");
+  v4u b;
+  b.x = center4(n0, h);
+  b.y = center4(n0 >> 4, h >> 2);
+  b.z = center4(n1, h >> 4);
+  b.w = center4(n1 >> 4, h >> 6);
+  const float d = __half2float(__ushort_as_half((unsigned short)(s >> 16)));
+  v2f v;
+  v.x = d * (float)(int8_t)(s & 255);  // exact: an 11-bit significand times an int8
+  v.y = d * (float)(int8_t)((s >> 8) & 255);
+  const uint32_t bdst = lds_addr(slot + kSlotB + wave * 1024 + lane * 16);
+  asm volatile("ds_write_b128 %0, %1" ::"v"(bdst), "v"(b) : "memory");
+  if (lane < 32) {
+    const uint32_t sdst = lds_addr(slot + kSlotS + wave * 256 + lane * 8);
+    asm volatile("ds_write_b64 %0, %1" ::"v"(sdst), "v"(v) : "memory");
+  }
+}
+
+// MFMAs and rescale of one 32x32 output tile for one chunk.
+template <bool SUBDOTS>
+__device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, long alo, long ahi,
+                                           v4u b, v2f s, const float (&dav)[16], int lane,
+                                           int64_t c, int64_t T, int64_t R, int64_t n, int64_t m,
+                                           int64_t nchunk, int32_t* __restrict__ dots) {
+  const long blo = (long)(((uint64_t)b.y << 32) | b.x);
+  const long bhi = (long)(((uint64_t)b.w << 32) | b.z);
+  const v16i lo_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo, blo, bias, 0, 0, 0);
+  const v16i hi_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(ahi, bhi, bias, 0, 0, 0);
+  if (SUBDOTS) {
+    const int p = lane & 31, g = lane >> 5;
+    const int64_t mcol = R * kTile + p;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (tok < n && mcol < m) {
+        int32_t* o = dots + (tok * m + mcol) * (2 * nchunk) + 2 * c;
+        o[0] = lo_d[r] - kBiasI;
+        o[1] = hi_d[r] - kBiasI;
+      }
+    }
+  } else {
+    const float nb0 = -kBiasF * s.x;
+    const float nb1 = -kBiasF * s.y;
+    // four phases of 16 independent fma: no VALU instruction depends on the one before it
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(lo_d[r]), s.x, nb0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(t[r], dav[r], acc[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(hi_d[r]), s.y, nb1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(t[r], dav[r], acc[r]);
+  }
+}
+
 template <int LAYOUT, bool SUBDOTS>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict__ xq,
+__global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t* __restrict__ xq,
                                                       const float* __restrict__ da,
                                                       const uint8_t* __restrict__ wcodes,
                                                       const uint8_t* __restrict__ wscales,
                                                       int64_t n, int64_t m, int64_t nchunk,
                                                       float* __restrict__ y, int64_t ldy,
                                                       int32_t* __restrict__ dots) {
+  constexpr int kSlot = SlotSize<LAYOUT>::value;
+  constexpr int kRing = RingSize<LAYOUT>::value;
+  static_assert(Q6K_WG_PER_CU * kRing * kSlot <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kSlot];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int p = lane & 31;
-  const int g = lane >> 5;
-  const int64_t T0 = (int64_t)blockIdx.x * 4 + 2 * (wave & 1);
-  const int64_t R0 = (int64_t)blockIdx.y * 4 + 2 * (wave >> 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool loads_a = wave < kWgTokTiles;
+  const int tt = wave & 1;                              // token tile of this wave in the workgroup
+  const int rp = wave >> 1;                             // row-tile pair of this wave
+  const int64_t T = (int64_t)blockIdx.x * kWgTokTiles + tt;
+  const int64_t R0 = (int64_t)blockIdx.y * 4;           // the workgroup's first row tile
+  const int64_t Ta = (int64_t)blockIdx.x * kWgTokTiles + (loads_a ? wave : 0);
+
+  const uint8_t* a_src = xq + Ta * nchunk * 1024;
+  const uint8_t* d_src = reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128;
+  const uint8_t* b_src;
+  const uint8_t* s_src;
+  if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
+    b_src = wcodes + (R0 + wave) * nchunk * 1024;
+    s_src = wscales + (R0 + wave) * nchunk * 256;
+  } else {
+    b_src = wcodes + (R0 + wave) * nchunk * 768;
+    s_src = wscales + (R0 + wave) * nchunk * 128;
+  }
 
   v16i bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
+  float acc[2][16];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-  float acc[2][2][16];
+  // Prologue: chunks 0 .. kRing-2 in flight; chunk 0 ready in its slot.
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][u][r] = 0.0f;
+  for (int j = 0; j < kRing - 1; ++j)
+    issue_chunk<LAYOUT>(smem + j * kSlot, a_src, b_src, s_src, d_src,
+                        j < nchunk ? j : nchunk - 1, wave, lane);
+  wait_chunks<kRing - 2>(loads_a);
+  if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot(smem, wave, lane);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
+  const int p = lane & 31, g = lane >> 5;
+  int slot_c = 0;                 // slot of chunk c
+  int slot_next = 1;              // slot of chunk c+1
+  int slot_issue = kRing - 1;     // slot of chunk c+kRing-1
   for (int64_t c = 0; c < nchunk; ++c) {
-    uint4 a[2];
-    float dav[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t tc = (T0 + t) * nchunk + c;
-      a[t] = reinterpret_cast<const uint4*>(xq + tc * 64 * kFragBytes)[lane];
-      const float4* dp = reinterpret_cast<const float4*>(da + tc * 32 + 16 * g);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = dp[q];
-        dav[t][4 * q + 0] = f.x;
-        dav[t][4 * q + 1] = f.y;
-        dav[t][4 * q + 2] = f.z;
-        dav[t][4 * q + 3] = f.w;
-      }
-    }
-    uint4 b[2];
-    float dsc0[2], dsc1[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t rc = (R0 + u) * nchunk + c;
-      if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
-        b[u] = reinterpret_cast<const uint4*>(wcodes + rc * 64 * kFragBytes)[lane];
-        const float2 s = reinterpret_cast<const float2*>(wscales)[rc * 32 + p];
-        dsc0[u] = s.x;
-        dsc1[u] = s.y;
-      } else {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(wcodes + (rc * 64 + lane) * kPackBytes);
-        const uint32_t n0 = src[0], n1 = src[1], h = src[2];
-        b[u].x = center4(n0, h);
-        b[u].y = center4(n0 >> 4, h >> 2);
-        b[u].z = center4(n1, h >> 4);
-        b[u].w = center4(n1 >> 4, h >> 6);
-        const uint32_t s = reinterpret_cast<const uint32_t*>(wscales)[rc * 32 + p];
-        const float d = __half2float(__ushort_as_half((unsigned short)(s >> 16)));
-        dsc0[u] = d * (float)(int8_t)(s & 255);
-        dsc1[u] = d * (float)(int8_t)((s >> 8) & 255);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float nb0 = -kBiasF * dsc0[u];
-      const float nb1 = -kBiasF * dsc1[u];
-      const long blo = (long)(((uint64_t)b[u].y << 32) | b[u].x);
-      const long bhi = (long)(((uint64_t)b[u].w << 32) | b[u].z);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const long alo = (long)(((uint64_t)a[t].y << 32) | a[t].x);
-        const long ahi = (long)(((uint64_t)a[t].w << 32) | a[t].z);
-        const v16i dlo = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo, blo, bias, 0, 0, 0);
-        const v16i dhi = __builtin_amdgcn_mfma_i32_32x32x16_i8(ahi, bhi, bias, 0, 0, 0);
-        if (SUBDOTS) {
-          const int64_t mcol = (R0 + u) * kTile + p;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t tok = (T0 + t) * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (tok < n && mcol < m) {
-              int32_t* o = dots + (tok * m + mcol) * (2 * nchunk) + 2 * c;
-              o[0] = dlo[r] - kBiasI;
-              o[1] = dhi[r] - kBiasI;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float lo = __builtin_fmaf(__int_as_float(dlo[r]), dsc0[u], nb0);
-            acc[t][u][r] = __builtin_fmaf(lo, dav[t][r], acc[t][u][r]);
-            const float hi = __builtin_fmaf(__int_as_float(dhi[r]), dsc1[u], nb1);
-            acc[t][u][r] = __builtin_fmaf(hi, dav[t][r], acc[t][u][r]);
-          }
-        }
-      }
-    }
+    // this wave's loads of chunk c+1 have landed (kRing-3 newer chunks may still be in flight)
+    wait_chunks<kRing - 3>(loads_a);
+    if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot(smem + slot_next * kSlot, wave, lane);
+    // chunk c+1 complete in LDS for every wave; every wave is done with chunk c-1's slot
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int64_t ci = c + kRing - 1;
+    issue_chunk<LAYOUT>(smem + slot_issue * kSlot, a_src, b_src, s_src, d_src,
+                        ci < nchunk ? ci : nchunk - 1, wave, lane);
+    // LDS reads of this chunk: row tile 2rp's B and d*sc, A and da, then row tile 2rp+1's
+    const uint8_t* slot = smem + slot_c * kSlot;
+    const uint32_t aa = lds_addr(slot + kSlotA + tt * 1024 + lane * 16);
+    const uint32_t dd = lds_addr(slot + kSlotD + tt * 128 + g * 64);
+    const uint32_t bb = lds_addr(slot + kSlotB + rp * 2048 + lane * 16);
+    const uint32_t ss = lds_addr(slot + kSlotS + rp * 512 + p * 8);
+    v4u a, b0, b1;
+    v4f d0, d1, d2, d3;
+    v2f s0, s1;
+    asm volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b64 %1, %10\n\t"
+        "ds_read_b128 %2, %11\n\t"
+        "ds_read_b128 %3, %12\n\t"
+        "ds_read_b128 %4, %12 offset:16\n\t"
+        "ds_read_b128 %5, %12 offset:32\n\t"
+        "ds_read_b128 %6, %12 offset:48\n\t"
+        "ds_read_b128 %7, %9 offset:1024\n\t"
+        "ds_read_b64 %8, %10 offset:256"
+        : "=&v"(b0), "=&v"(s0), "=&v"(a), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(b1),
+          "=&v"(s1)
+        : "v"(bb), "v"(ss), "v"(aa), "v"(dd)
+        : "memory");
+    asm volatile("s_waitcnt lgkmcnt(2)"
+                 : "+v"(b0), "+v"(s0), "+v"(a), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)::"memory");
+    const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
+                           d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
+    const long alo = (long)(((uint64_t)a.y << 32) | a.x);
+    const long ahi = (long)(((uint64_t)a.w << 32) | a.z);
+    tile_chunk<SUBDOTS>(acc[0], bias, alo, ahi, b0, s0, dav, lane, c, T, R0 + 2 * rp, n, m,
+                        nchunk, dots);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b1), "+v"(s1)::"memory");
+    tile_chunk<SUBDOTS>(acc[1], bias, alo, ahi, b1, s1, dav, lane, c, T, R0 + 2 * rp + 1, n, m,
+                        nchunk, dots);
+    slot_c = slot_next;
+    slot_next = slot_next + 1 == kRing ? 0 : slot_next + 1;
+    slot_issue = slot_issue + 1 == kRing ? 0 : slot_issue + 1;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
+
   if (SUBDOTS) return;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int u = 0; u < 2; ++u) {
+    const int64_t mcol = (R0 + 2 * rp + u) * kTile + p;
+    if (mcol >= m) continue;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t mcol = (R0 + u) * kTile + p;
-      if (mcol >= m) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t tok = (T0 + t) * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (tok < n) y[tok * ldy + mcol] = acc[t][u][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (tok < n) y[tok * ldy + mcol] = acc[u][r];
     }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -390,7 +536,7 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
     if (((uintptr_t)y & 3) != 0) return Q6K_EALIGN;
   }
   const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
-  const int64_t gx = np / kWgTok, gy = mp / kWgRow;
+  const int64_t gx = np / (kTile * 2), gy = mp / kWgRow;
   if (gy > 65535 || gx > INT32_MAX) return Q6K_ESIZE;
   const int64_t nchunk = k / 32;
   size_t codes_bytes, scales_bytes;
