@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--workload", default="ffn_down_n3314")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=160)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -46,6 +48,24 @@ def cpu_baseline(raw, x, m, k, tokens):
     return {"value": 2.0 * tokens * m * k / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"first {tokens} tokens x all {m} rows x k={k} (quantize + reference GEMM), "
                       f"{dt:.1f} s single-threaded"}
+
+
+def counter_traffic(workload, layout):
+    """HBM-side bytes of one GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None if there is none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    src = os.path.join(ROOT, "q6_int8_prefill_amd", "csrc", "q6k.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != digest:
+        return None
+    entry = rec.get("layouts", {}).get(str(layout))
+    return None if entry is None else int(entry["traffic_bytes"])
 
 
 def main():
@@ -79,6 +99,17 @@ def main():
     q6k.q6k_expand_weights(raw_d, m, k, layout, w)
     torch.cuda.synchronize()
     expand_ms = (time.perf_counter() - t0) * 1e3
+
+    if args.copy_probe_mib:
+        # plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE readings calibrate the
+        # GEMM's counter-based HBM traffic
+        nel = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev is not None:
@@ -152,7 +183,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "kernel": f"gemm_kernel<layout {layout}>",
+                     "traffic": counter_traffic(args.workload, layout),
+                     "kernel": f"gemm_kernel<layout {layout}>",
                      "algorithmic_per_launch": {"int8_ops": ops, "bytes": gemm_bytes}},
     }
     if not args.no_cpu_baseline:
