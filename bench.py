@@ -6,7 +6,13 @@ One step = one pass of the hot path over one batch: the activation quantize-tran
 before timing starts.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--cold] [--no-cpu-baseline] [--copy-probe-mib MIB]
+
+Workloads: tiny, attn_v_n512, attn_v_n3314, ffn_down_n3314 (the default and headline case), and
+sweep32: 32 layers of (attn_v 4096x4096 + ffn_down 4096x11008) at 3314 tokens, 64 GEMMs back to
+back on one stream over 1.6 GB of raw weights, inputs drawn on the device.  --cold writes a
+512 MiB scrub buffer before every timed step, so weights and activations come from HBM rather
+than the 256 MB Infinity Cache.
 """
 import argparse
 import json
@@ -29,8 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layout", type=int, default=1, choices=[0, 1])
     ap.add_argument("--workload", default="ffn_down_n3314")
+    ap.add_argument("--cold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=160)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -40,6 +47,7 @@ def cpu_baseline(raw, x, m, k, tokens):
     """The oracle as it stands (single-threaded C), on the first `tokens` tokens of the same
     workload, all rows: quantize + reference GEMM."""
     import oracle
+    tokens = min(tokens, x.shape[0])
     xs = x[:tokens]
     t0 = time.perf_counter()
     xq, da = oracle.quantize(xs)
@@ -68,6 +76,33 @@ def counter_traffic(workload, layout):
     return None if entry is None else int(entry["traffic_bytes"])
 
 
+class Problem:
+    """Device buffers of one GEMM: activations, prepared weights, quantized activations, output."""
+
+    def __init__(self, q6k, torch, x_d, raw_d, n, m, k, layout, dev):
+        self.q6k, self.n, self.m, self.k, self.layout = q6k, n, m, k, layout
+        self.x = x_d
+        xb, db = q6k.q6k_act_bytes(n, k)
+        self.xq = torch.empty(xb, dtype=torch.uint8, device=dev)
+        self.da = torch.empty(db // 4, dtype=torch.float32, device=dev)
+        self.w = torch.empty(q6k.q6k_weight_bytes(m, k, layout), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((n, m), dtype=torch.float32, device=dev)
+        q6k.q6k_expand_weights(raw_d, m, k, layout, self.w)
+
+    def quantize(self):
+        self.q6k.q6k_quantize_act(self.x, self.xq, self.da)
+
+    def gemm(self):
+        self.q6k.q6k_gemm(self.xq, self.da, self.n, self.w, self.layout, self.m, self.k, self.y)
+
+    def alg_bytes(self):
+        """Algorithmic bytes: GEMM = weights as stored + int8 activations + f32 scales + f32 Y;
+        prepass = f32 X + int8 activations + f32 scales."""
+        a_bytes = self.n * self.k + self.n * (self.k // 32) * 4
+        return {"gemm": self.w.numel() + a_bytes + self.n * self.m * 4,
+                "prepass": self.n * self.k * 4 + a_bytes}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -82,23 +117,41 @@ def main():
     import q6_int8_prefill_amd as q6k
 
     dev = torch.device("cuda:0")
-    raw, x, n, m, k = synthetic.workload(args.workload)
     layout = args.layout
-
-    # inputs resident in HBM
-    x_d = torch.from_numpy(x).to(dev)
-    raw_d = torch.from_numpy(raw.reshape(-1)).to(dev)
-    xb, db = q6k.q6k_act_bytes(n, k)
-    xq = torch.empty(xb, dtype=torch.uint8, device=dev)
-    da = torch.empty(db // 4, dtype=torch.float32, device=dev)
-    w = torch.empty(q6k.q6k_weight_bytes(m, k, layout), dtype=torch.uint8, device=dev)
-    y = torch.empty((n, m), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    sweep = args.workload == "sweep32"
 
+    # ------------------------------------------------------------ inputs resident in HBM
     t0 = time.perf_counter()
-    q6k.q6k_expand_weights(raw_d, m, k, layout, w)
+    raw = x = None
+    problems = []
+    if sweep:
+        for layer in range(synthetic.SWEEP_LAYERS):
+            for kind in ("attn_v", "ffn_down"):
+                s = synthetic.sweep_layer(layer, kind)
+                raw_d = synthetic.weights_torch(s["m"], s["k"], s["seed"], dev)
+                x_d = synthetic.activations_torch(s["n"], s["k"], s["seed"], dev, s["x"])
+                problems.append(Problem(q6k, torch, x_d, raw_d, s["n"], s["m"], s["k"], layout, dev))
+                del raw_d
+    else:
+        raw, x, n, m, k = synthetic.workload(args.workload)
+        x_d = torch.from_numpy(x).to(dev)
+        raw_d = torch.from_numpy(raw.reshape(-1)).to(dev)
+        problems.append(Problem(q6k, torch, x_d, raw_d, n, m, k, layout, dev))
     torch.cuda.synchronize()
-    expand_ms = (time.perf_counter() - t0) * 1e3
+    setup_s = time.perf_counter() - t0
+
+    # load-time weight preparation of the first matrix, timed once on its own
+    p0 = problems[0]
+    raw0 = (synthetic.weights_torch(p0.m, p0.k, 7, dev) if sweep
+            else torch.from_numpy(raw.reshape(-1)).to(dev))
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_a.record(stream)
+    q6k.q6k_expand_weights(raw0, p0.m, p0.k, layout, p0.w)
+    e_b.record(stream)
+    torch.cuda.synchronize()
+    expand_us = e_a.elapsed_time(e_b) * 1e3
+    del raw0
 
     if args.copy_probe_mib:
         # plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE readings calibrate the
@@ -111,49 +164,76 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        q6k.q6k_quantize_act(x_d, xq, da)
-        if ev is not None:
-            ev[1].record(stream)
-        q6k.q6k_gemm(xq, da, n, w, layout, m, k, y)
-        if ev is not None:
-            ev[2].record(stream)
+    # 512 MiB written between steps evicts the 256 MB Infinity Cache
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    def step(evs=None):
+        # evs[j] = events before the prepass, between prepass and GEMM, after the GEMM
+        for j, p in enumerate(problems):
+            if evs is not None:
+                evs[j][0].record(stream)
+            p.quantize()
+            if evs is not None:
+                evs[j][1].record(stream)
+            p.gemm()
+            if evs is not None:
+                evs[j][2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in problems]
+           for _ in range(args.steps)]
+    if scrub is None:
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_per_step = start.elapsed_time(end) / args.steps
+    else:
+        # cold: the scrub runs between steps, outside the timed span of each step
+        step_ms, wall = [], 0.0
+        for i in range(args.steps):
+            scrub.fill_(i & 255)
+            torch.cuda.synchronize()
+            s_ev = torch.cuda.Event(enable_timing=True)
+            e_ev = torch.cuda.Event(enable_timing=True)
+            wall0 = time.perf_counter()
+            s_ev.record(stream)
+            step(evs[i])
+            e_ev.record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - wall0
+            step_ms.append(s_ev.elapsed_time(e_ev))
+        ms_per_step = float(np.mean(step_ms))
 
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    prep_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    gemm_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    gemm_avg_us = float(gemm_ms.mean() * 1e3)
-    prep_avg_us = float(prep_ms.mean() * 1e3)
+    gemm_us = np.array([[e[1].elapsed_time(e[2]) * 1e3 for e in st] for st in evs])
+    prep_us = np.array([[e[0].elapsed_time(e[1]) * 1e3 for e in st] for st in evs])
+    gemm_total_us = float(gemm_us.sum(axis=1).mean())
+    prep_total_us = float(prep_us.sum(axis=1).mean())
 
-    ops = 2.0 * n * m * k
-    gmac = n * m * k / 1e9
+    ops = sum(2.0 * p.n * p.m * p.k for p in problems)
+    gmac = ops / 2e9
     value = ops / (ms_per_step * 1e-3) / 1e12
-    gemm_tops = ops / (gemm_avg_us * 1e-6) / 1e12
-    # algorithmic bytes of one GEMM launch: weights as stored, int8 activations, f32 scales, f32 Y
-    w_bytes = w.numel()
-    a_bytes = n * k + n * (k // 32) * 4
-    y_bytes = n * m * 4
-    gemm_bytes = w_bytes + a_bytes + y_bytes
-    prep_bytes = n * k * 4 + a_bytes
+    gemm_tops = ops / (gemm_total_us * 1e-6) / 1e12
+    gemm_bytes = sum(p.alg_bytes()["gemm"] for p in problems)
+    prep_bytes = sum(p.alg_bytes()["prepass"] for p in problems)
+
+    if sweep:
+        config = {"workload": "sweep32", "layers": synthetic.SWEEP_LAYERS,
+                  "gemms": "per layer: attn_v n=3314 m=4096 k=4096, ffn_down n=3314 m=4096 k=11008",
+                  "layout": layout, "cold": args.cold,
+                  "step": "64 x (q6k_quantize_act + q6k_gemm)"}
+    else:
+        config = {"workload": args.workload, "n": p0.n, "m": p0.m, "k": p0.k, "layout": layout,
+                  "cold": args.cold, "step": "q6k_quantize_act + q6k_gemm"}
 
     out = {
         "metric": METRIC,
@@ -168,27 +248,34 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": args.workload, "n": n, "m": m, "k": k, "layout": layout,
-                   "step": "q6k_quantize_act + q6k_gemm"},
+        "config": config,
         "us_per_gmac": round(ms_per_step * 1e3 / gmac, 4),
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
-        "gemm": {"avg_us": round(gemm_avg_us, 2), "min_us": round(float(gemm_ms.min() * 1e3), 2),
-                 "tops": round(gemm_tops, 2), "us_per_gmac": round(gemm_avg_us / gmac, 4),
-                 "pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2)},
-        "prepass": {"avg_us": round(prep_avg_us, 2),
-                    "gbs": round(prep_bytes / (prep_avg_us * 1e-6) / 1e9, 1),
-                    "pct_hbm_peak": round(100.0 * prep_bytes / (prep_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)},
-        "expand_ms_once": round(expand_ms, 3),
-        "weight_bytes": {"raw": int(raw.size), "prepared": int(w_bytes)},
+        "gemm": {"avg_us": round(float(gemm_us.mean()), 2),
+                 "min_us": round(float(gemm_us.min()), 2),
+                 "total_us_per_step": round(gemm_total_us, 2),
+                 "tops": round(gemm_tops, 2), "us_per_gmac": round(gemm_total_us / gmac, 4),
+                 "pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
+                 "alg_gbs": round(gemm_bytes / (gemm_total_us * 1e-6) / 1e9, 1)},
+        "prepass": {"total_us_per_step": round(prep_total_us, 2),
+                    "gbs": round(prep_bytes / (prep_total_us * 1e-6) / 1e9, 1),
+                    "pct_hbm_peak": round(100.0 * prep_bytes / (prep_total_us * 1e-6) / 1e9
+                                          / HBM_PEAK_GBS, 2)},
+        "expand_us_once": {"m": p0.m, "k": p0.k, "us": round(expand_us, 1)},
+        "weight_bytes": {"prepared_total": int(sum(p.w.numel() for p in problems))},
         "wall_s_timed": round(wall, 4),
+        "setup_s": round(setup_s, 1),
+        # the dominant kernel is the GEMM: algorithmic int8 ops over its event-timed duration
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": counter_traffic(args.workload, layout),
+                     "traffic": (counter_traffic(args.workload, layout)
+                                 if not (sweep or args.cold) else None),
                      "kernel": f"gemm_kernel<layout {layout}>",
-                     "algorithmic_per_launch": {"int8_ops": ops, "bytes": gemm_bytes}},
+                     "algorithmic_per_launch": {"int8_ops": 2.0 * p0.n * p0.m * p0.k,
+                                                "bytes": p0.alg_bytes()["gemm"]}},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(raw, x, m, k, args.cpu_sample_tokens)
+    if not args.no_cpu_baseline and raw is not None:
+        out["cpu_baseline"] = cpu_baseline(raw, x, p0.m, p0.k, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -75,3 +75,54 @@ def workload(name):
     raw = weights(w["m"], w["k"], w["seed"])
     x = activations(w["n"], w["k"], w["seed"], w["x"])
     return raw, x, w["n"], w["m"], w["k"]
+
+
+# ------------------------------------------------------------------------------------------------
+# Device-side generators with the same distributions, for workloads too large to draw on the host
+# (the 32-layer sweep).  They draw from torch's seeded CUDA generator, so their values differ from
+# the numpy generators above; tests that compare against the oracle use the numpy ones.
+# ------------------------------------------------------------------------------------------------
+def weights_torch(m, k, seed, device, sc_lo=-32, sc_hi=31):
+    """Raw q6_K blocks as a flat uint8 device tensor of m*(k/256)*210 bytes."""
+    import torch
+    nsb = k // QK
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    raw = torch.empty((m, nsb, BLOCK_BYTES), dtype=torch.uint8, device=device)
+    raw[:, :, 0:192] = torch.randint(0, 256, (m, nsb, 192), generator=g, device=device,
+                                     dtype=torch.int32).to(torch.uint8)
+    sc = torch.randint(sc_lo, sc_hi + 1, (m, nsb, 16), generator=g, device=device, dtype=torch.int32)
+    raw[:, :, 192:208] = sc.to(torch.int8).view(torch.uint8)
+    d = (torch.randn((m, nsb), generator=g, device=device).abs() * 1e-2).to(torch.float16)
+    raw[:, :, 208:210] = d.view(torch.uint8).reshape(m, nsb, 2)
+    return raw.reshape(-1)
+
+
+def activations_torch(n, k, seed, device, kind="normal"):
+    """f32 [n][k] device activations with the distributions of activations()."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 10**6)
+    if kind == "normal":
+        return torch.randn((n, k), generator=g, device=device)
+    if kind == "outlier":
+        x = torch.randn((n, k), generator=g, device=device)
+        ch = torch.randperm(k, generator=g, device=device)[: int(round(0.01 * k))]
+        x[:, ch] *= 20.0
+        return x
+    if kind == "swiglu":
+        a = torch.randn((n, k), generator=g, device=device, dtype=torch.float64)
+        b = torch.randn((n, k), generator=g, device=device, dtype=torch.float64)
+        return (a * (b * torch.sigmoid(b))).to(torch.float32)
+    raise ValueError(kind)
+
+
+SWEEP_LAYERS = 32
+
+
+def sweep_layer(layer, kind):
+    """Shape and seed of one GEMM of the 32-layer sweep: kind 'attn_v' (4096x4096, outlier
+    activations, seed 1000+layer) or 'ffn_down' (4096x11008, post-SwiGLU-like, seed 2000+layer)."""
+    if kind == "attn_v":
+        return dict(n=3314, m=4096, k=4096, seed=1000 + layer, x="outlier")
+    return dict(n=3314, m=4096, k=11008, seed=2000 + layer, x="swiglu")
