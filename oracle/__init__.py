@@ -47,6 +47,7 @@ def _load():
         lib.q6o_dequant.argtypes = [p, i64, i64, p]
         lib.q6o_quantize.argtypes = [p, i64, i64, p, p]
         lib.q6o_subdots.argtypes = [p, p, i64, i64, i64, p]
+        lib.q6o_chunkdots.argtypes = [p, p, i64, i64, i64, p]
         lib.q6o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p]
         _lib = lib
     return _lib
@@ -112,6 +113,16 @@ def subdots(xq, raw, m):
     raw = _raw(raw, m, k)
     out = np.empty((n, m, k // 16), np.int32)
     _load().q6o_subdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
+    return out
+
+
+def chunkdots(xq, raw, m):
+    """-> int32 [n][m][k/32] per-chunk integer numerators with the sub-block scales applied."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    n, k = xq.shape
+    raw = _raw(raw, m, k)
+    out = np.empty((n, m, k // 32), np.int32)
+    _load().q6o_chunkdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
     return out
 
 

@@ -150,6 +150,35 @@ void q6o_subdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int
   free(wc);
 }
 
+/* Per-chunk integer numerators with the sub-block scales applied:
+ *   E[n][m][c] = sum over the 32 elements i of chunk c of xq[n][i] * sc[m][i/16] * (q[m][i] - 32)
+ * (int64 accumulation, stored as int32: |E| <= 32 * 127 * 4096 < 2^24).  [r38 sec. 2.1] gives
+ * one f16 d per 256-element super-block and one int8 sc per 16 elements, so the chunk's share of
+ * y is da[n][c] * d[m][c/8] * E[n][m][c], which equals the two per-half terms of sec. 2.2 summed
+ * in exact arithmetic.  Written from the definition: decode each element, multiply by its own
+ * scale, sum over the chunk. */
+void q6o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
+                   int32_t* dots) {
+  int64_t nc = k / 32;
+  int64_t row_bytes = (k / QK) * BLOCK_BYTES;
+  int32_t* ws = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  for (int64_t j = 0; j < m; ++j) {
+    const uint8_t* row = raw + j * row_bytes;
+    for (int64_t i = 0; i < k; ++i) {
+      const uint8_t* blk = row + (i / QK) * BLOCK_BYTES;
+      int sc = (int8_t)blk[OFF_SC + (i % QK) / 16];
+      ws[i] = sc * (q6o_code(blk, (int)(i % QK)) - 32);
+    }
+    for (int64_t t = 0; t < n; ++t)
+      for (int64_t c = 0; c < nc; ++c) {
+        int64_t acc = 0;
+        for (int i = 0; i < 32; ++i) acc += (int64_t)xq[t * k + c * 32 + i] * (int64_t)ws[c * 32 + i];
+        dots[(t * m + j) * nc + c] = (int32_t)acc;
+      }
+  }
+  free(ws);
+}
+
 /* Reference output: y[n][m] = sum_s da[n][s/2] * (d[m][s/16] * sc[m][s]) * D[n][m][s] in f64,
  * and t[n][m] = sum_s |that term|, the tolerance scale ([r38 sec. 2.2]: one rescale per
  * 16-element half, no dmin term).  t may be NULL. */

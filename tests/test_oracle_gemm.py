@@ -101,3 +101,58 @@ def test_row_and_token_subsets_commute(oracle_mod):
     ys, ts = oracle_mod.gemm(xq[rows], da[rows], np.ascontiguousarray(raw[cols]), len(cols))
     np.testing.assert_array_equal(ys, y[rows][:, cols])
     np.testing.assert_array_equal(ts, t[rows][:, cols])
+
+
+# ------------------------------------------------------------------------------------------------
+# Per-chunk numerators with the sub-block scales applied (the integer part of a 32-k chunk's
+# contribution: y = sum_c da[c] * d[c/8] * E[c]).
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n,m,k", [(1, 1, 256), (5, 7, 512), (6, 9, 1024)])
+def test_chunkdots_from_subdots_and_scales(oracle_mod, n, m, k):
+    # E[c] = sc[2c] * D[2c] + sc[2c+1] * D[2c+1], from the pinned sub-block dots and the decoded
+    # int8 scales (a different route: the scale is applied after the 16-element dot)
+    raw = synthetic.weights(m, k, seed=31 + k, sc_lo=-128, sc_hi=127)
+    xq, _ = oracle_mod.quantize(synthetic.activations(n, k, seed=5 + n, kind="outlier"))
+    _, sc, _ = oracle_mod.decode(raw, m, k)
+    dots = oracle_mod.subdots(xq, raw, m).astype(np.int64)          # [n][m][k/16]
+    want = (dots * sc.astype(np.int64)[None, :, :]).reshape(n, m, k // 32, 2).sum(axis=3)
+    np.testing.assert_array_equal(oracle_mod.chunkdots(xq, raw, m), want)
+
+
+def test_chunkdots_brute_force_from_dequant(oracle_mod):
+    # sc * (q - 32) = w / d exactly (d * sc * (q - 32) needs at most 24 significant bits), so the
+    # numerators are the int64 dot of xq with w / d over each 32-element chunk
+    n, m, k = 4, 6, 512
+    raw = synthetic.weights(m, k, seed=77, sc_lo=-128, sc_hi=127)
+    xq, _ = oracle_mod.quantize(synthetic.activations(n, k, seed=8))
+    _, _, d = oracle_mod.decode(raw, m, k)
+    assert (d != 0).all()
+    w = oracle_mod.dequant(raw, m, k)
+    ws = w / np.repeat(d.astype(np.float64), 256, axis=1)
+    assert (ws == np.round(ws)).all()
+    want = np.einsum("nci,mci->nmc", xq.reshape(n, k // 32, 32).astype(np.int64),
+                     ws.astype(np.int64).reshape(m, k // 32, 32))
+    np.testing.assert_array_equal(oracle_mod.chunkdots(xq, raw, m), want)
+
+
+def test_chunkdots_reassemble_output(oracle_mod):
+    # sum_c da[c] * d[c/8] * E[c] reproduces the reference output
+    n, m, k = 5, 8, 768
+    raw = synthetic.weights(m, k, seed=12, sc_lo=-128, sc_hi=127)
+    xq, da = oracle_mod.quantize(synthetic.activations(n, k, seed=13, kind="swiglu"))
+    _, _, d = oracle_mod.decode(raw, m, k)
+    e = oracle_mod.chunkdots(xq, raw, m).astype(np.float64)
+    got = np.einsum("nc,mc,nmc->nm", da.astype(np.float64),
+                    np.repeat(d.astype(np.float64), 8, axis=1), e)
+    y, t = oracle_mod.gemm(xq, da, raw, m)
+    assert (np.abs(got - y) <= 1e-12 * t).all()
+
+
+def test_chunkdots_extreme_magnitude(oracle_mod):
+    # the largest |E|: sc = -128 on every sub-block, all codes 0 (value -32), xq = 127
+    raw = np.zeros((1, 1, 210), np.uint8)
+    raw[0, 0, 192:208] = np.uint8(0x80)
+    xq = np.full((1, 256), 127, np.int8)
+    np.testing.assert_array_equal(oracle_mod.chunkdots(xq, raw, 1),
+                                  np.full((1, 1, 8), 32 * 127 * 4096))
+    assert 32 * 127 * 4096 < 2 ** 24
