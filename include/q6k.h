@@ -16,6 +16,8 @@
  *   "r53 W_exp pre-expansion plane + cp.async B staging (LANDED)": optional load-time plane of
  *       centered int8 weights (extra memory, no expand work in the GEMM)
  *   "r42 stage-wide dsc scale reads (REVERTED)", sec. 3.2 (W_dsc arm): d*sc precomputed as f32
+ * Layout 2 applies the same weights (w = d * sc * (q - 32), "r38 ..." sec. 2.1) with the int8 sc
+ * folded into the integer dot, so each 32-k chunk carries one f32 rescale da * d instead of two.
  *
  * Conventions for every entry point
  *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library never allocates,
@@ -50,6 +52,12 @@
  *                  byte 8+t            = a_t>>4 | (a_{t+4}>>4) << 2 | (b_t>>4) << 4 | (b_{t+4}>>4) << 6
  *     scales     : at byte offset MP*k*3/4, 4 bytes at ((R*nchunk + c)*32 + p)*4:
  *                  int8 sc[2c], int8 sc[2c+1], f16 d (little-endian) of row 32R + p
+ *   layout 2 (Q6K_LAYOUT_FOLDED), the int8 sub-block scale applied to the codes ahead of time:
+ *     v = sc[k/16] * (q - 32) (in [-4064, 4096]) of row 32R + p at k = 32c + 16*(b/8) + 8g + b%8
+ *     is stored as two int8 digits, lo = ((v + 32) mod 64) - 32 and hi = (v - lo) / 64:
+ *     codes      : byte ((R*nchunk + c)*2 + h)*1024 + l*16 + b  holds lo (h = 0) or hi (h = 1)
+ *     scales     : at byte offset MP*k*2, float (R*(k/256) + s)*32 + p = d of row 32R + p,
+ *                  super-block s (the f16 d converted exactly)
  *   Padding tokens / rows hold zeros.
  */
 #ifndef Q6K_H
@@ -71,7 +79,7 @@ typedef enum {
   Q6K_EHIP = -5    /* the HIP runtime rejected a launch */
 } q6k_status;
 
-enum { Q6K_LAYOUT_PACKED = 0, Q6K_LAYOUT_EXPANDED = 1 };
+enum { Q6K_LAYOUT_PACKED = 0, Q6K_LAYOUT_EXPANDED = 1, Q6K_LAYOUT_FOLDED = 2 };
 
 /* Sizes in bytes of the tiled activation buffers for n tokens of k values: returns the size
  * of xq and stores the size of da in *da_bytes (may be NULL).  Returns 0 for invalid n/k. */
@@ -94,35 +102,47 @@ size_t q6k_weight_bytes(int64_t m, int64_t k, int layout);
 /* Load-time weight preparation.  Input: raw q6_K blocks, row j's super-block b at byte
  * (j*(k/256) + b)*210 (byte map of "r38 ..." sec. 2.1; any alignment).  Output: layout 0 (6-bit
  * codes regrouped for wide loads plus the raw scale bytes; expanded to centered int8 inside the
- * GEMM, "r41 ..." sec. 2) or layout 1 (centered int8 plane plus f32 d*sc plane, "r53 ..." sec.
- * 2.3 and the W_dsc plane of "r42 ..." sec. 3.2).  Padding rows are written as zeros. */
+ * GEMM, "r41 ..." sec. 2), layout 1 (centered int8 plane plus f32 d*sc plane, "r53 ..." sec.
+ * 2.3 and the W_dsc plane of "r42 ..." sec. 3.2) or layout 2 (two int8 digit planes of
+ * sc * (q - 32) plus one f32 d per super-block).  Padding rows are written as zeros. */
 q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layout, void* w_out,
                               size_t w_out_bytes, void* stream);
 
 /* The GEMM: y[t][j] = sum over 16-k sub-blocks s of da[t][s/2] * (d*sc)[j][s] * D[t][j][s],
- * D the exact int32 dot of the int8 activations with the centered weights over sub-block s,
- * accumulated per 32-k chunk as two independent f32 additions ("r38 ..." sec. 2.2, 2.4).
+ * D the exact int32 dot of the int8 activations with the centered weights over sub-block s
+ * ("r38 ..." sec. 2.2, 2.4).  Layouts 0 and 1 accumulate each 32-k chunk as two independent f32
+ * additions, one per 16-k half.  Layout 2 forms the chunk's exact integer
+ * E = sc[2c]*D[2c] + sc[2c+1]*D[2c+1] and adds da * E once per chunk, then applies d once per
+ * super-block; the result differs from layouts 0/1 only in f32 rounding.
  *   xq, da  : outputs of q6k_quantize_act for the same n, k
  *   w       : output of q6k_expand_weights for the same m, k and `layout`
  *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned; only y[0..n)[0..m) is
  *             written
  *   xq, da and w must hold at least the sizes q6k_act_bytes / q6k_weight_bytes return (the
- *   kernels read whole padded tiles). */
+ *   kernels read whole padded tiles).  Layout 2 also needs k <= 2^25 (Q6K_ESIZE otherwise). */
 q6k_status q6k_gemm(const void* xq, const float* da, int64_t n, const void* w, int layout,
                     int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
 
 /* Test-only export of the same kernel source: instead of y, stores the int32 sub-block dots
- * D[t][j][s] (the two KSPLIT halves of every chunk) to dots [n][m][k/16]. */
+ * D[t][j][s] (the two KSPLIT halves of every chunk) to dots [n][m][k/16].  Layouts 0 and 1 only
+ * (layout 2 never forms them: Q6K_EINVAL). */
 q6k_status q6k_gemm_subdots(const void* xq, const float* da, int64_t n, const void* w, int layout,
                             int64_t m, int64_t k, int32_t* dots, void* stream);
+
+/* Test-only export of the layout-2 kernel: instead of y, stores the per-chunk integer numerators
+ * E[t][j][c] = sc[j][2c]*D[t][j][2c] + sc[j][2c+1]*D[t][j][2c+1] (|E| < 2^24), as the kernel
+ * reconstructs them from its two digit products, to dots [n][m][k/32].  Layout 2 only
+ * (Q6K_EINVAL otherwise). */
+q6k_status q6k_gemm_chunkdots(const void* xq, const float* da, int64_t n, const void* w,
+                              int layout, int64_t m, int64_t k, int32_t* dots, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* q6k_strerror(int status);
 
-/* Liveness counters: number of GEMM launches (q6k_gemm and q6k_gemm_subdots) per layout since
- * load; out[0] = layout 0, out[1] = layout 1.  Fast-path liveness check in the spirit of
+/* Liveness counters: number of GEMM launches (q6k_gemm and the test exports) per layout since
+ * load; out[L] = layout L for L = 0, 1, 2.  Fast-path liveness check in the spirit of
  * "r53 ..." sec. 3.3 (a path that silently never runs is invisible to parity tests). */
-void q6k_stats(uint64_t out[2]);
+void q6k_stats(uint64_t out[3]);
 
 #ifdef __cplusplus
 }

@@ -7,12 +7,14 @@ and streams only.  If the built library is missing, importing the binding raises
 """
 from ._lib import (  # noqa: F401
     LAYOUT_EXPANDED,
+    LAYOUT_FOLDED,
     LAYOUT_PACKED,
     Q6KError,
     lib_path,
     q6k_act_bytes,
     q6k_expand_weights,
     q6k_gemm,
+    q6k_gemm_chunkdots,
     q6k_gemm_subdots,
     q6k_quantize_act,
     q6k_stats,

@@ -6,6 +6,7 @@ import torch
 
 LAYOUT_PACKED = 0
 LAYOUT_EXPANDED = 1
+LAYOUT_FOLDED = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "_build", "libq6k.so")
@@ -27,13 +28,15 @@ _lib.q6k_gemm.restype = _int
 _lib.q6k_gemm.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _i64, _p]
 _lib.q6k_gemm_subdots.restype = _int
 _lib.q6k_gemm_subdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
+_lib.q6k_gemm_chunkdots.restype = _int
+_lib.q6k_gemm_chunkdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
 _lib.q6k_strerror.restype = ctypes.c_char_p
 _lib.q6k_strerror.argtypes = [_int]
 _lib.q6k_stats.restype = None
 _lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
 
 EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_weight_bytes", "q6k_expand_weights",
-           "q6k_gemm", "q6k_gemm_subdots", "q6k_strerror", "q6k_stats")
+           "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots", "q6k_strerror", "q6k_stats")
 
 
 class Q6KError(RuntimeError):
@@ -146,7 +149,19 @@ def q6k_gemm_subdots(xq, da, n, w, layout, m, k, dots, stream=None):
                                  _stream(stream)), "q6k_gemm_subdots")
 
 
+def q6k_gemm_chunkdots(xq, da, n, w, layout, m, k, dots, stream=None):
+    """Test-only: int32 per-chunk numerators [n][m][k/32] from the layout-2 kernel source."""
+    if dots is not None and dots.dtype != torch.int32:
+        raise TypeError("dots must be int32")
+    _check_operands(xq, da, n, w, layout, m, k)
+    if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 32):
+        raise ValueError("dots too small for n x m x k/32")
+    _check(_lib.q6k_gemm_chunkdots(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(dots),
+                                   _stream(stream)), "q6k_gemm_chunkdots")
+
+
 def q6k_stats():
-    out = (ctypes.c_uint64 * 2)()
+    """-> launch counts per layout (layout 0, 1, 2)."""
+    out = (ctypes.c_uint64 * 3)()
     _lib.q6k_stats(out)
-    return int(out[0]), int(out[1])
+    return tuple(int(v) for v in out)

@@ -6,6 +6,10 @@
 //   gemm_kernel<L, D>   : q6_K x int8 GEMM on v_mfma_i32_32x32x16_i8 (the int8 MFMA whose
 //                         K is 16, so the two 16-k halves of a chunk stay separate integers);
 //                         D = true is the test-only sub-block dot export of the same source
+//   folded_kernel<D>    : the same GEMM on layout 2, where the int8 sub-block scale is applied
+//                         inside the integer dot (two int8 digit planes of sc * (q - 32)) and
+//                         each chunk needs one f32 rescale instead of two; D = true exports the
+//                         per-chunk integer numerators
 //
 // The method follows "r38 q6_K BT-style raw-byte mma kernel (LANDED)" (sec. 2.1 layout,
 // sec. 2.2 rescale without dmin, sec. 2.4 KSPLIT=2), "r41 q6_K B-expand widened to uint4 group
@@ -30,9 +34,10 @@ constexpr int kPackBytes = 12;   // layout 0: per lane per chunk, 16 codes of 6 
 constexpr int kBiasI = 0x4B400000;      // bit pattern of 1.5 * 2^23
 constexpr float kBiasF = 12582912.0f;   // 1.5 * 2^23
 
-std::atomic<uint64_t> g_launches[2];
+std::atomic<uint64_t> g_launches[3];
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -149,7 +154,36 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint8_t* __restrict__
   const int8_t sc1 = (int8_t)blk[192 + 2 * (cc & 7) + 1];
   const uint16_t dbits = (uint16_t)(blk[208] | (blk[209] << 8));
   const int64_t tc = R * nchunk + c;  // (row tile, chunk) index
-  if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
+  if (LAYOUT == Q6K_LAYOUT_FOLDED) {
+    // v = sc * (q - 32) in [-4064, 4096] = 64 * hi + lo with lo in [-32, 31], hi in [-63, 64]
+    const bool live = R * kTile + p < m;
+    int lo[32], hi[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int v = live ? (i < 16 ? sc0 : sc1) * (code[i] - 32) : 0;
+      lo[i] = ((v + 32) & 63) - 32;
+      hi[i] = (v - lo[i]) / 64;  // exact: v - lo is a multiple of 64
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int* cv = h ? hi : lo;
+      uint4 s0, s1;
+      s0.x = pack4(cv[0], cv[1], cv[2], cv[3]);
+      s0.y = pack4(cv[4], cv[5], cv[6], cv[7]);
+      s0.z = pack4(cv[16], cv[17], cv[18], cv[19]);
+      s0.w = pack4(cv[20], cv[21], cv[22], cv[23]);
+      s1.x = pack4(cv[8], cv[9], cv[10], cv[11]);
+      s1.y = pack4(cv[12], cv[13], cv[14], cv[15]);
+      s1.z = pack4(cv[24], cv[25], cv[26], cv[27]);
+      s1.w = pack4(cv[28], cv[29], cv[30], cv[31]);
+      uint4* dst = reinterpret_cast<uint4*>(codes + (tc * 2 + h) * 64 * kFragBytes);
+      dst[p] = s0;
+      dst[p + 32] = s1;
+    }
+    if (cc == 0)
+      reinterpret_cast<float*>(scales)[(R * nsb + sb) * 32 + p] =
+          live ? __half2float(__ushort_as_half(dbits)) : 0.0f;
+  } else if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
     const bool live = R * kTile + p < m;  // padding rows are stored as zeros
     int cv[32];
 #pragma unroll
@@ -483,6 +517,325 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 }
 
 // ---------------------------------------------------------------------------------------------
+// GEMM on layout 2 (folded scales).  q6_K has one f16 d per 256-element super-block and one int8
+// sc per 16 elements, so a 32-k chunk contributes da * d * E to y with the exact integer
+//     E = sum_k xq[k] * v[k],   v = sc[k/16] * (q[k] - 32)  in [-4064, 4096].
+// v does not fit an int8 MFMA operand; it is stored as two int8 digit planes v = 64*hi + lo.  Per
+// chunk and 32x32 tile: two v_mfma_i32_32x32x32_i8 (low and high digits, full 32-k chunk each),
+// both started from the bit pattern of 1.5*2^23 (|E_lo| <= 32*127*32, |E_hi| <= 32*127*64, both
+// < 2^22, so each result reads exactly as the float 1.5*2^23 + E_part).  Then
+//     u  = fma(F_hi, 64, -65 * 1.5*2^23)  = 64*E_hi - 1.5*2^23   (a multiple of 64 below 2^30:
+//                                                               exact)
+//     e  = u + F_lo                       = E                    (|E| < 2^24: exact)
+//     sb = fma(e, da, sb)
+// three VALU operations per output per chunk, all exact up to the single rounding of the last.
+// After the 8th chunk of a super-block, acc = fma(sb, d, acc) and sb restarts at 0.
+//
+// Orientation: the weights are the MFMA's A operand and the activations its B operand, so lane l,
+// register r of a tile holds weight row 8*(r/4) + 4*(l/32) + r%4 and token l%32: each lane needs a
+// single da per token tile and chunk.  Workgroup = 4 waves = 64 tokens (token tiles 2*bx, 2*bx+1)
+// x 128 weight rows (row tiles 4*by .. 4*by+3); wave w computes row tile 4*by + w against both
+// token tiles.  The staging ring is the one of gemm_kernel: each wave loads its row tile's two
+// digit planes (and, for the last chunk of a super-block, its 32 d values); waves 0 and 1 load the
+// activations and da of token tile w.
+// ---------------------------------------------------------------------------------------------
+#ifndef Q6K_FOLDED_WG_PER_CU
+#define Q6K_FOLDED_WG_PER_CU 3
+#endif
+constexpr int kFSlotA = 0;      // 2 token tiles x 1 KiB of int8 activations
+constexpr int kFSlotB = 2048;   // 4 row tiles x (1 KiB low digits + 1 KiB high digits)
+constexpr int kFSlotW = 10240;  // 4 row tiles x 32 d f32 (filled for a super-block's last chunk)
+constexpr int kFSlot = 10752;
+// da of a whole super-block (8 chunks x 32 floats = 1 KiB per token tile) is loaded with one
+// full-wave load, into one of two buffers (super-block parity) outside the ring
+constexpr int kFDaBytes = 2 * 2 * 1024;
+// 4 slots: loads run 3 chunks ahead, and 4 divides the 8 chunks of a super-block, so that with
+// the loop unrolled over a super-block every slot index is a compile-time constant
+constexpr int kFRing = 4;
+static_assert(Q6K_FOLDED_WG_PER_CU * (kFRing * kFSlot + kFDaBytes) <= 160 * 1024, "LDS budget");
+constexpr float kFoldK = -65.0f * kBiasF;  // exact: 195 * 2^22
+
+// Direct-to-LDS load of 16 bytes per lane through a buffer resource: the wave's LDS base goes in
+// M0, the lane offset is a constant register and the chunk offset a scalar, so no per-load
+// address arithmetic runs on the vector ALU.  Lanes past the resource's size read zeros.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                       uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_wave_base), 16, voff, soff, 0, 0);
+}
+
+// Buffer resource over `bytes` bytes at p (raw, no stride; 32-bit range, checked on the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+struct FoldSrc {
+  __amdgpu_buffer_rsrc_t a, d, b, w;  // activations, da, digit planes, d of this wave's tiles
+};
+
+// Issue this wave's loads of chunk ci (ci % 8 == CI8) into `slot`.  A chunk past the end is
+// replaced by the last chunk, so that every wave issues at least 2 loads per chunk (3 for waves 0
+// and 1), which the count-based waits rely on; the d load of a super-block's last chunk and the
+// da load of its first are extra and are only issued for real chunks.  The da of super-block s
+// goes to buffer s % 2, last read for super-block s - 2, whose reads ended before the barrier of
+// iteration 8s - 8; it is issued at iteration 8s - 3.
+template <int CI8>
+__device__ __forceinline__ void issue_folded(uint8_t* slot, uint8_t* da_buf, const FoldSrc& src,
+                                             int64_t ci, int64_t nchunk, int wave, int lane) {
+  const bool live = ci < nchunk;
+  const uint32_t cl = (uint32_t)(live ? ci : nchunk - 1);
+  const uint32_t l16 = lane * 16;
+  bdma16(src.b, l16, cl * 2048, slot + kFSlotB + wave * 2048);
+  bdma16(src.b, l16 + 1024, cl * 2048, slot + kFSlotB + wave * 2048 + 1024);
+  if (CI8 == 7 && live && lane < 8)
+    bdma16(src.w, l16, (uint32_t)(ci >> 3) * 128, slot + kFSlotW + wave * 128);
+  if (wave < kWgTokTiles) {
+    bdma16(src.a, l16, cl * 1024, slot + kFSlotA + wave * 1024);
+    if (CI8 == 0 && live)
+      bdma16(src.d, l16, (uint32_t)ci * 128, da_buf + ((ci >> 3) & 1) * 2048 + wave * 1024);
+  }
+}
+
+// s_waitcnt vmcnt(chunks * the fewest loads this wave issues per chunk)
+template <int CHUNKS>
+__device__ __forceinline__ void wait_folded(bool loads_a) {
+  if (loads_a)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 3) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 2) : "memory");
+}
+
+// One chunk's operands in registers: the wave's row tile (both digit planes), the two token
+// tiles and their da for this lane's token.
+struct FoldOps {
+  v4i lo, hi, x0, x1;
+  v2f dav;
+};
+
+// Start the LDS reads of one chunk's operands; the data is waited for (lgkmcnt) before use.
+// bb, xa, dd are per-lane LDS addresses of slot 0 / of the current da buffer; the slot and chunk
+// offsets are immediates, so that no per-slot address is kept in a register.
+template <int OFF_SLOT, int OFF_DA>
+__device__ __forceinline__ void read_ops(FoldOps& o, uint32_t bb, uint32_t xa, uint32_t dd) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:%9\n\t"
+      "ds_read_b128 %1, %6 offset:%10\n\t"
+      "ds_read_b128 %2, %7 offset:%11\n\t"
+      "ds_read_b32 %3, %8 offset:%12\n\t"
+      "ds_read_b32 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %7 offset:%14"
+      : "=&v"(o.lo), "=&v"(o.hi), "=&v"(o.x0), "=&v"(o.dav.x), "=&v"(o.dav.y), "=&v"(o.x1)
+      : "v"(bb), "v"(xa), "v"(dd), "n"(OFF_SLOT), "n"(OFF_SLOT + 1024), "n"(OFF_SLOT),
+        "n"(OFF_DA), "n"(OFF_DA + 1024), "n"(OFF_SLOT + 1024)
+      : "memory");
+}
+
+// e = 64*E_hi + E_lo from the two biased digit products (exact, see above), in two phases of 16
+// independent operations (no VALU instruction depends on the one before it).
+__device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, const v16i& fl) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = __builtin_fmaf(__int_as_float(fh[r]), 64.0f, kFoldK);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] += __int_as_float(fl[r]);
+}
+
+// sb (+)= e * da -- the first chunk of a super-block starts sb afresh -- or, for the test export,
+// the store of e.
+template <bool DOTS, bool FIRST>
+__device__ __forceinline__ void rescale(float (&sb)[16], const float (&e)[16], float dav, int lane,
+                                        int64_t c, int64_t tok, int64_t row0, int64_t n,
+                                        int64_t m, int64_t nchunk, int32_t* __restrict__ dots) {
+  if (DOTS) {
+    const int g = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = row0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (tok < n && row < m) dots[(tok * m + row) * nchunk + c] = (int32_t)e[r];
+    }
+  } else if (FIRST) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[r] = e[r] * dav;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[r] = __builtin_fmaf(e[r], dav, sb[r]);
+  }
+}
+
+// An empty statement that the compiler must keep in program order with the other volatile
+// statements (barriers, LDS reads) and that "modifies" the operands and the accumulators: code
+// that reads them after it cannot move above it, code that writes them before cannot move below.
+__device__ __forceinline__ void order_after(FoldOps& o, float (&v)[16]) {
+  asm volatile(""
+               : "+v"(o.lo), "+v"(o.hi), "+v"(o.x1), "+v"(v[0]), "+v"(v[1]), "+v"(v[2]),
+                 "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]),
+                 "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
+                 "+v"(v[15]));
+}
+
+struct FoldCtx {
+  uint8_t* smem;
+  uint8_t* da_buf;
+  FoldSrc src;
+  int64_t nchunk, n, m, tok0, row0;
+  int32_t* dots;
+  uint32_t bb, xa, wa;  // per-lane LDS addresses in slot 0: digits, activations, d
+  int wave, lane;
+  bool loads_a;
+};
+
+// Chunk c = 8s + CC of the main loop.
+// Chunk c = 8s + CC of the main loop.  `o` holds this chunk's operands (read during the previous
+// step); once the last MFMA has taken them, the reads of chunk c+1 are started into the same
+// registers and complete while the second tile is rescaled.  dcur / dnext: this lane's da
+// address in the da buffer of super-block s / s + 1.
+template <bool DOTS, int CC>
+__device__ __forceinline__ void folded_step(const FoldCtx& k, int64_t s, uint32_t dcur,
+                                            uint32_t dnext, FoldOps& o, const v16i& bias,
+                                            float (&acc)[2][16], float (&sb)[2][16]) {
+  const int64_t c = 8 * s + CC;
+  // this wave's loads of chunk c+1 have landed (one newer chunk may still be in flight); after
+  // the barrier every wave's have, and every wave is done with chunk c-1's slot
+  wait_folded<kFRing - 3>(k.loads_a);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"
+               : "+v"(o.lo), "+v"(o.hi), "+v"(o.x0), "+v"(o.x1), "+v"(o.dav)::"memory");
+  constexpr int kIssue = (CC + kFRing - 1) % kFRing;
+  issue_folded<(CC + kFRing - 1) % 8>(k.smem + kIssue * kFSlot, k.da_buf, k.src,
+                                      c + kFRing - 1, k.nchunk, k.wave, k.lane);
+  const v16i fh0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.hi, o.x0, bias, 0, 0, 0);
+  const v16i fl0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.lo, o.x0, bias, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  float e0[16];
+  fold_digits(e0, fh0, fl0);
+  rescale<DOTS, CC == 0>(sb[0], e0, o.dav.x, k.lane, c, k.tok0, k.row0, k.n, k.m, k.nchunk,
+                         k.dots);
+  // order point: the second tile's MFMAs read operands that pass through this statement after
+  // the first tile's rescale, so the instruction selector cannot hoist them (four live MFMA
+  // results would not fit the register budget)
+  order_after(o, sb[0]);
+  const v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.hi, o.x1, bias, 0, 0, 0);
+  const v16i fl1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.lo, o.x1, bias, 0, 0, 0);
+  const float da1 = o.dav.y;
+  __builtin_amdgcn_sched_barrier(0);
+  // (after the last chunk this reads a stale slot whose values are never used: all addresses
+  // stay inside the LDS arrays, and it keeps the step a single basic block)
+  read_ops<((CC + 1) % kFRing) * kFSlot, ((CC + 1) % 8) * 128>(o, k.bb, k.xa,
+                                                                CC == 7 ? dnext : dcur);
+  __builtin_amdgcn_sched_barrier(0);
+  float e1[16];
+  fold_digits(e1, fh1, fl1);
+  rescale<DOTS, CC == 0>(sb[1], e1, da1, k.lane, c, k.tok0 + kTile, k.row0, k.n, k.m,
+                         k.nchunk, k.dots);
+  order_after(o, sb[1]);  // the next step starts after this one's rescale
+  if (!DOTS && CC == 7) {
+    // end of a super-block: apply the d of each of this lane's 16 rows (in this chunk's slot)
+    constexpr int kW = (CC % kFRing) * kFSlot;
+    v4f d0, d1, d2, d3;
+    asm volatile(
+        "ds_read_b128 %0, %9 offset:%10\n\t"
+        "ds_read_b128 %1, %9 offset:%11\n\t"
+        "ds_read_b128 %2, %9 offset:%12\n\t"
+        "ds_read_b128 %3, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "+v"(o.lo), "+v"(o.hi), "+v"(o.x0),
+          "+v"(o.x1), "+v"(o.dav)
+        : "v"(k.wa), "n"(kW), "n"(kW + 32), "n"(kW + 64), "n"(kW + 96)
+        : "memory");
+    const float dv[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
+                          d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(sb[u][r], dv[r], acc[u][r]);
+  }
+}
+
+template <bool DOTS>
+__global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ da,
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
+    int32_t* __restrict__ dots) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot + kFDaBytes];
+  FoldCtx k;
+  k.smem = smem;
+  k.da_buf = smem + kFRing * kFSlot;
+  k.lane = threadIdx.x & 63;
+  k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  k.loads_a = k.wave < kWgTokTiles;
+  const int64_t T0 = (int64_t)blockIdx.x * kWgTokTiles;  // the workgroup's first token tile
+  const int64_t R = (int64_t)blockIdx.y * 4 + k.wave;    // this wave's row tile
+  const int64_t Ta = T0 + (k.loads_a ? k.wave : 0);
+  const int64_t nsb = nchunk / 8;
+  k.src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
+  k.src.d = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
+  k.src.b = make_rsrc(wcodes + R * nchunk * 2048, nchunk * 2048);
+  k.src.w = make_rsrc(wd + R * nsb * 128, nsb * 128);
+  k.nchunk = nchunk;
+  k.n = n;
+  k.m = m;
+  k.dots = dots;
+  const int p = k.lane & 31, g = k.lane >> 5;
+  k.tok0 = T0 * kTile + p;
+  k.row0 = R * kTile;
+  k.bb = lds_addr(smem) + kFSlotB + k.wave * 2048 + k.lane * 16;
+  k.xa = lds_addr(smem) + kFSlotA + k.lane * 16;
+  k.wa = lds_addr(smem) + kFSlotW + k.wave * 128 + g * 16;
+  // da of token p sits at position 16*((p/4)%2) + 4*(p/8) + p%4 of a tile's 32 floats
+  const uint32_t d0 = lds_addr(k.da_buf) + 4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
+
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
+  float acc[2][16], sb[2][16];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = sb[u][r] = 0.0f;
+
+  // Prologue: chunks 0 .. 2 in flight; chunk 0 ready in its slot and read into registers.
+  issue_folded<0>(smem + 0 * kFSlot, k.da_buf, k.src, 0, nchunk, k.wave, k.lane);
+  issue_folded<1>(smem + 1 * kFSlot, k.da_buf, k.src, 1, nchunk, k.wave, k.lane);
+  issue_folded<2>(smem + 2 * kFSlot, k.da_buf, k.src, 2, nchunk, k.wave, k.lane);
+  wait_folded<kFRing - 2>(k.loads_a);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  FoldOps ops;
+  read_ops<0, 0>(ops, k.bb, k.xa, d0);
+
+  for (int64_t s = 0; s < nsb; ++s) {
+    const uint32_t dcur = d0 + (s & 1) * 2048, dnext = d0 + ((s + 1) & 1) * 2048;
+    folded_step<DOTS, 0>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 1>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 2>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 3>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 4>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 5>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 6>(k, s, dcur, dnext, ops, bias, acc, sb);
+    folded_step<DOTS, 7>(k, s, dcur, dnext, ops, bias, acc, sb);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
+
+  if (DOTS) return;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t tok = (T0 + u) * kTile + p;
+    if (tok >= n) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row0 = R * kTile + 8 * q + 4 * g;
+      float* dst = y + tok * ldy + row0;
+      if (vec_store && row0 + 3 < m) {
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (row0 + rr < m) dst[rr] = acc[u][4 * q + rr];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Host-side helpers
 // ---------------------------------------------------------------------------------------------
 inline int64_t round_up(int64_t v, int64_t q) { return (v + q - 1) / q * q; }
@@ -498,12 +851,19 @@ bool act_sizes(int64_t n, int64_t k, size_t* xq_bytes, size_t* da_bytes) {
   return true;
 }
 
+bool valid_layout(int layout) {
+  return layout == Q6K_LAYOUT_PACKED || layout == Q6K_LAYOUT_EXPANDED || layout == Q6K_LAYOUT_FOLDED;
+}
+
 bool weight_sizes(int64_t m, int64_t k, int layout, size_t* codes, size_t* scales) {
   if (m < 0 || k <= 0 || k % 256 || m > kMaxDim || k > kMaxDim) return false;
-  if (layout != Q6K_LAYOUT_PACKED && layout != Q6K_LAYOUT_EXPANDED) return false;
+  if (!valid_layout(layout)) return false;
   const int64_t mp = round_up(m, kWgRow);
   if (mp != 0 && k > (int64_t)(SIZE_MAX / 8) / mp) return false;
-  if (layout == Q6K_LAYOUT_EXPANDED) {
+  if (layout == Q6K_LAYOUT_FOLDED) {
+    *codes = (size_t)mp * (size_t)k * 2;
+    *scales = (size_t)mp * (size_t)(k / 256) * sizeof(float);
+  } else if (layout == Q6K_LAYOUT_EXPANDED) {
     *codes = (size_t)mp * (size_t)k;
     *scales = (size_t)mp * (size_t)(k / 16) * sizeof(float);
   } else {
@@ -517,17 +877,24 @@ q6k_status launch_status() {
   return hipGetLastError() == hipSuccess ? Q6K_OK : Q6K_EHIP;
 }
 
-template <bool SUBDOTS>
+enum { kOutY = 0, kOutSubdots = 1, kOutChunkdots = 2 };
+
+template <int OUT>
 q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w, int layout,
                        int64_t m, int64_t k, float* y, int64_t ldy, int32_t* dots, void* stream) {
   if (n < 0 || m < 0) return Q6K_EINVAL;
-  if (layout != Q6K_LAYOUT_PACKED && layout != Q6K_LAYOUT_EXPANDED) return Q6K_EINVAL;
+  if (!valid_layout(layout)) return Q6K_EINVAL;
+  if (OUT == kOutSubdots && layout == Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
+  if (OUT == kOutChunkdots && layout != Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
   if (k <= 0 || k % 256) return Q6K_ESHAPE;
   if (n > kMaxDim || m > kMaxDim || k > kMaxDim) return Q6K_ESIZE;
+  // layout 2 addresses a row tile's digit planes (k/32 * 2048 bytes) through one 32-bit buffer
+  // range
+  if (layout == Q6K_LAYOUT_FOLDED && k / 32 * 2048 > INT32_MAX) return Q6K_ESIZE;
   if (n == 0 || m == 0) return Q6K_OK;
   if (!xq || !da || !w) return Q6K_EINVAL;
   if (!aligned16(xq) || !aligned16(da) || !aligned16(w)) return Q6K_EALIGN;
-  if (SUBDOTS) {
+  if (OUT != kOutY) {
     if (!dots) return Q6K_EINVAL;
     if (((uintptr_t)dots & 3) != 0) return Q6K_EALIGN;
   } else {
@@ -543,14 +910,21 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   weight_sizes(m, k, layout, &codes_bytes, &scales_bytes);
   const uint8_t* wc = static_cast<const uint8_t*>(w);
   const uint8_t* ws = wc + codes_bytes;
+  const uint8_t* a = static_cast<const uint8_t*>(xq);
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid((unsigned)gx, (unsigned)gy), block(256);
-  if (layout == Q6K_LAYOUT_EXPANDED)
-    hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_EXPANDED, SUBDOTS>), grid, block, 0, s,
-                       static_cast<const uint8_t*>(xq), da, wc, ws, n, m, nchunk, y, ldy, dots);
-  else
-    hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_PACKED, SUBDOTS>), grid, block, 0, s,
-                       static_cast<const uint8_t*>(xq), da, wc, ws, n, m, nchunk, y, ldy, dots);
+  constexpr bool kDots = OUT != kOutY;
+  if (layout == Q6K_LAYOUT_FOLDED) {
+    const int vec_store = OUT == kOutY && aligned16(y) && ldy % 4 == 0;
+    hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, ws, n, m, nchunk, y,
+                       ldy, vec_store, dots);
+  } else if (layout == Q6K_LAYOUT_EXPANDED) {
+    hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_EXPANDED, kDots>), grid, block, 0, s, a, da, wc,
+                       ws, n, m, nchunk, y, ldy, dots);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_PACKED, kDots>), grid, block, 0, s, a, da, wc, ws,
+                       n, m, nchunk, y, ldy, dots);
+  }
   const q6k_status st = launch_status();
   if (st == Q6K_OK) g_launches[layout].fetch_add(1, std::memory_order_relaxed);
   return st;
@@ -600,7 +974,7 @@ size_t q6k_weight_bytes(int64_t m, int64_t k, int layout) {
 q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layout, void* w_out,
                               size_t w_out_bytes, void* stream) {
   if (m < 0) return Q6K_EINVAL;
-  if (layout != Q6K_LAYOUT_PACKED && layout != Q6K_LAYOUT_EXPANDED) return Q6K_EINVAL;
+  if (!valid_layout(layout)) return Q6K_EINVAL;
   if (k <= 0 || k % 256) return Q6K_ESHAPE;
   size_t cb, sb;
   if (!weight_sizes(m, k, layout, &cb, &sb)) return Q6K_ESIZE;
@@ -614,7 +988,10 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
   uint8_t* codes = static_cast<uint8_t*>(w_out);
   dim3 grid((unsigned)(mp / kTile), (unsigned)nsb), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (layout == Q6K_LAYOUT_EXPANDED)
+  if (layout == Q6K_LAYOUT_FOLDED)
+    hipLaunchKernelGGL(expand_kernel<Q6K_LAYOUT_FOLDED>, grid, block, 0, s,
+                       static_cast<const uint8_t*>(w_raw), m, nsb, codes, codes + cb);
+  else if (layout == Q6K_LAYOUT_EXPANDED)
     hipLaunchKernelGGL(expand_kernel<Q6K_LAYOUT_EXPANDED>, grid, block, 0, s,
                        static_cast<const uint8_t*>(w_raw), m, nsb, codes, codes + cb);
   else
@@ -625,12 +1002,17 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
 
 q6k_status q6k_gemm(const void* xq, const float* da, int64_t n, const void* w, int layout,
                     int64_t m, int64_t k, float* y, int64_t ldy, void* stream) {
-  return gemm_common<false>(xq, da, n, w, layout, m, k, y, ldy, nullptr, stream);
+  return gemm_common<kOutY>(xq, da, n, w, layout, m, k, y, ldy, nullptr, stream);
 }
 
 q6k_status q6k_gemm_subdots(const void* xq, const float* da, int64_t n, const void* w, int layout,
                             int64_t m, int64_t k, int32_t* dots, void* stream) {
-  return gemm_common<true>(xq, da, n, w, layout, m, k, nullptr, 0, dots, stream);
+  return gemm_common<kOutSubdots>(xq, da, n, w, layout, m, k, nullptr, 0, dots, stream);
+}
+
+q6k_status q6k_gemm_chunkdots(const void* xq, const float* da, int64_t n, const void* w,
+                              int layout, int64_t m, int64_t k, int32_t* dots, void* stream) {
+  return gemm_common<kOutChunkdots>(xq, da, n, w, layout, m, k, nullptr, 0, dots, stream);
 }
 
 const char* q6k_strerror(int status) {
@@ -645,10 +1027,9 @@ const char* q6k_strerror(int status) {
   }
 }
 
-void q6k_stats(uint64_t out[2]) {
+void q6k_stats(uint64_t out[3]) {
   if (!out) return;
-  out[0] = g_launches[0].load(std::memory_order_relaxed);
-  out[1] = g_launches[1].load(std::memory_order_relaxed);
+  for (int i = 0; i < 3; ++i) out[i] = g_launches[i].load(std::memory_order_relaxed);
 }
 
 }  // extern "C"

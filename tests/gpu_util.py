@@ -47,6 +47,13 @@ def subdots(xq, da, n, w, layout, m, k):
     return dots.cpu().numpy()
 
 
+def chunkdots(xq, da, n, w, layout, m, k):
+    dots = torch.full((n, m, k // 32), -7, dtype=torch.int32, device=DEV)
+    q6k.q6k_gemm_chunkdots(xq, da, n, w, layout, m, k, dots)
+    torch.cuda.synchronize()
+    return dots.cpu().numpy()
+
+
 def within_tolerance(y, y_ref, t_ref, rel=1e-3):
     """|y - y_ref| <= rel * sum|terms| elementwise (t_ref = 0 demands y = 0)."""
     err = np.abs(y.astype(np.float64) - y_ref)

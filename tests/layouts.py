@@ -60,3 +60,16 @@ def untile_packed(buf, m, k):
     sc = s[:, :, 0:2].reshape(mp, k // 16).view(np.int8)
     dbits = s[:, :, 2:4].copy().view("<u2").reshape(mp, nchunk)
     return codes, sc, dbits
+
+
+def untile_folded(buf, m, k):
+    """layout 2 bytes -> (low digits int8 [MP][k], high digits int8 [MP][k], d f32 [MP][k/256])."""
+    mp = round_up(m, 128)
+    nchunk = k // 32
+    b = np.asarray(buf, np.uint8)
+    planes = b[: mp * k * 2].view(np.int8).reshape(mp // 32, nchunk, 2, 2, 32, 2, 8)
+    # axes: R, c, h (digit), g, p, hh, e  ->  row 32R + p, k = 32c + 16hh + 8g + e
+    planes = planes.transpose(2, 0, 4, 1, 5, 3, 6).reshape(2, mp, k)
+    nsb = k // 256
+    d = b[mp * k * 2: mp * k * 2 + mp * nsb * 4].view(np.float32).reshape(mp // 32, nsb, 32)
+    return planes[0], planes[1], d.transpose(0, 2, 1).reshape(mp, nsb)

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     L = lib()
     for name in names:
         assert hasattr(L, name), name
@@ -37,7 +37,9 @@ def test_size_queries():
     assert q6k.q6k_weight_bytes(40, 512, 1) == 128 * 512 * 5 // 4
     assert q6k.q6k_weight_bytes(40, 512, 0) == 128 * 512 * 7 // 8
     assert q6k.q6k_weight_bytes(4096, 11008, 0) == 4096 * 11008 * 7 // 8
-    assert q6k.q6k_weight_bytes(40, 512, 2) == 0
+    assert q6k.q6k_weight_bytes(40, 512, 2) == 128 * 512 * 2 + 128 * 2 * 4
+    assert q6k.q6k_weight_bytes(4096, 11008, 2) == 4096 * 11008 * 2 + 4096 * 43 * 4
+    assert q6k.q6k_weight_bytes(40, 512, 3) == 0
     assert q6k.q6k_weight_bytes(40, 0, 1) == 0
 
 
@@ -60,7 +62,7 @@ def test_quantize_act_errors(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((FAKE, 4, 256, 2, FAKE, 1 << 30, None), -1),    # unknown layout
+    ((FAKE, 4, 256, 3, FAKE, 1 << 30, None), -1),    # unknown layout
     ((FAKE, 4, 512 + 32, 1, FAKE, 1 << 30, None), -2),
     ((FAKE + 1, 4, 256, 1, FAKE, 1 << 30, None), -3),  # raw must be 2-byte aligned
     ((FAKE, 4, 256, 1, FAKE + 8, 1 << 30, None), -3),
@@ -94,11 +96,21 @@ def test_subdots_errors():
     assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, None, None) == -1
     assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE + 2, None) == -3
     assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 100, FAKE, None) == -2
+    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 2, 8, 256, FAKE, None) == -1  # layout 2
+
+
+def test_chunkdots_errors():
+    L = lib()
+    assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 256, None, None) == -1
+    assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 256, FAKE + 2, None) == -3
+    assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 100, FAKE, None) == -2
+    for layout in (0, 1, 3):  # only layout 2 forms the per-chunk numerators
+        assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, layout, 8, 256, FAKE, None) == -1
 
 
 def test_strerror_and_stats():
     import q6_int8_prefill_amd as q6k
     for s in (0, -1, -2, -3, -4, -5, 42):
         assert isinstance(q6k.q6k_strerror(s), str) and q6k.q6k_strerror(s)
-    a, b = q6k.q6k_stats()
-    assert a >= 0 and b >= 0
+    counts = q6k.q6k_stats()
+    assert len(counts) == 3 and all(c >= 0 for c in counts)

@@ -1,12 +1,12 @@
-"""GPU parity of q6k_expand_weights (both layouts) against the oracle decode: byte-exact codes,
-exact scales.  Shapes include those of the pages' byte-exactness test ("r53 W_exp pre-expansion
+"""GPU parity of q6k_expand_weights (all three layouts) against the oracle decode: byte-exact
+codes, exact scales.  Shapes include those of the pages' byte-exactness test ("r53 W_exp pre-expansion
 plane + cp.async B staging", sec. 4: (64,256), (40,512), (24,768))."""
 import numpy as np
 import pytest
 
 import oracle
 import synthetic
-from layouts import round_up, untile_expanded, untile_packed
+from layouts import round_up, untile_expanded, untile_folded, untile_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -50,12 +50,29 @@ def check_packed(raw, m, k):
     assert w.size == round_up(m, 128) * k * 7 // 8
 
 
+def check_folded(raw, m, k):
+    # the two digits must rebuild sc * (q - 32) exactly, with the low digit in [-32, 31] (which
+    # makes the pair unique); d is the f16 d of each super-block as f32
+    import gpu_util
+    print(f"expand layout 2 m={m} k={k}", flush=True)
+    w = gpu_util.expand(raw, m, k, 2).cpu().numpy()
+    lo, hi, d = untile_folded(w, m, k)
+    wc, sc, d_ref = oracle.decode(raw, m, k)
+    v = np.repeat(sc.astype(np.int32), 16, axis=1) * wc.astype(np.int32)
+    np.testing.assert_array_equal(64 * hi[:m].astype(np.int32) + lo[:m], v)
+    assert lo.min() >= -32 and lo.max() <= 31
+    np.testing.assert_array_equal(d[:m].view(np.uint32), d_ref.astype(np.float32).view(np.uint32))
+    assert (lo[m:] == 0).all() and (hi[m:] == 0).all() and (d[m:] == 0).all()
+    assert w.size == round_up(m, 128) * k * 2 + round_up(m, 128) * (k // 256) * 4
+
+
 @pytest.mark.parametrize("m,k", SHAPES)
 @pytest.mark.parametrize("wide", [False, True])
 def test_expand_layouts_small(m, k, wide):
     raw = raw_for(m, k, seed=m * 7 + k, wide=wide)
     check_expanded(raw, m, k)
     check_packed(raw, m, k)
+    check_folded(raw, m, k)
 
 
 def test_expand_all_byte_values():
@@ -68,6 +85,7 @@ def test_expand_all_byte_values():
         raw[r, 0, 208:210] = (0x00, 0x3C)
     check_expanded(raw, m, k)
     check_packed(raw, m, k)
+    check_folded(raw, m, k)
 
 
 @pytest.mark.parametrize("name", ["attn_v_n512", "ffn_down_n3314"])
@@ -76,3 +94,4 @@ def test_expand_full_size(name):
     raw, _, _, m, k = gpu_util.cached_workload(name)
     check_expanded(raw, m, k)
     check_packed(raw, m, k)
+    check_folded(raw, m, k)

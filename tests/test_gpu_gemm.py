@@ -1,7 +1,9 @@
-"""GPU parity of q6k_gemm / q6k_gemm_subdots against the oracle.
+"""GPU parity of q6k_gemm / q6k_gemm_subdots / q6k_gemm_chunkdots against the oracle.
 
-  * per-sub-block int32 dots: bit-exact (the KSPLIT=2 halves of "r38 q6_K BT-style raw-byte mma
-    kernel", sec. 2.4), exported by the same kernel source;
+  * per-sub-block int32 dots (layouts 0 and 1): bit-exact (the KSPLIT=2 halves of "r38 q6_K
+    BT-style raw-byte mma kernel", sec. 2.4), exported by the same kernel source;
+  * per-chunk numerators sc*D summed over both halves (layout 2): bit-exact, exported by the same
+    kernel source after its float reconstruction of the two digit products;
   * outputs: |y - y_ref| <= 1e-3 * sum|terms| per element, for every element at sizes the
     oracle runs in seconds and on sampled tokens (all rows) at the full workload sizes, in the
     launch configuration the benchmark times.
@@ -13,7 +15,8 @@ import oracle
 import synthetic
 
 pytestmark = pytest.mark.gpu
-LAYOUTS = [0, 1]
+LAYOUTS = [0, 1, 2]
+SPLIT_LAYOUTS = [0, 1]  # layouts whose kernel keeps the two 16-k halves apart
 
 
 def prepare(x, raw, m, layout):
@@ -24,7 +27,7 @@ def prepare(x, raw, m, layout):
     return xq, da, w
 
 
-@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("layout", SPLIT_LAYOUTS)
 @pytest.mark.parametrize("n,m,k", [(64, 256, 512), (65, 40, 512), (1, 1, 256), (129, 130, 768),
                                    (33, 200, 1024)])
 def test_subdots_bit_exact(layout, n, m, k):
@@ -45,7 +48,7 @@ def test_subdots_extreme_magnitude():
     raw = np.zeros((m, 1, 210), np.uint8)
     raw[:, 0, 208:210] = (0x00, 0x3C)
     x = np.full((n, k), 5.0, np.float32)
-    for layout in LAYOUTS:
+    for layout in SPLIT_LAYOUTS:
         xq, da, w = prepare(x, raw, m, layout)
         got = gpu_util.subdots(xq, da, n, w, layout, m, k)
         assert (got == -65024).all()
@@ -53,6 +56,46 @@ def test_subdots_extreme_magnitude():
         xq_ref, da_ref = oracle.quantize(x)
         y_ref, _ = oracle.gemm(xq_ref, da_ref, raw, m)
         np.testing.assert_array_equal(y, y_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("n,m,k", [(64, 256, 512), (65, 40, 512), (1, 1, 256), (129, 130, 768),
+                                   (33, 200, 1024), (160, 384, 2048)])
+def test_chunkdots_bit_exact(n, m, k):
+    import gpu_util
+    print(f"chunkdots layout=2 n={n} m={m} k={k}", flush=True)
+    raw = synthetic.weights(m, k, seed=n + m + k, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=n * m, kind="outlier")
+    xq, da, w = prepare(x, raw, m, 2)
+    got = gpu_util.chunkdots(xq, da, n, w, 2, m, k)
+    xq_ref, _ = oracle.quantize(x)
+    np.testing.assert_array_equal(got, oracle.chunkdots(xq_ref, raw, m))
+
+
+@pytest.mark.parametrize("sc_byte,code_byte,want", [(0x80, 0x00, 32 * 127 * 4096),
+                                                    (0x7F, 0x00, -32 * 127 * 127 * 32),
+                                                    (0x80, 0xFF, None)])
+def test_chunkdots_extreme_magnitude(sc_byte, code_byte, want):
+    # |E| up to 32 * 127 * 4096 (sc = -128, all codes 0, xq = 127): the digit products and their
+    # float reconstruction must stay exact at the ends of the range
+    import gpu_util
+    n, m, k = 32, 32, 256
+    raw = np.zeros((m, 1, 210), np.uint8)
+    raw[:, 0, :192] = code_byte
+    raw[:, 0, 192:208] = sc_byte
+    raw[:, 0, 208:210] = (0x00, 0x3C)
+    x = np.full((n, k), 5.0, np.float32)
+    x[1::2] *= -1
+    xq, da, w = prepare(x, raw, m, 2)
+    got = gpu_util.chunkdots(xq, da, n, w, 2, m, k)
+    xq_ref, da_ref = oracle.quantize(x)
+    ref = oracle.chunkdots(xq_ref, raw, m)
+    np.testing.assert_array_equal(got, ref)
+    if want is not None:
+        assert (np.abs(ref) == abs(want)).all()
+    y = gpu_util.gemm(xq, da, n, w, 2, m, k)
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y, y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -120,7 +163,8 @@ def test_liveness_counters_tick_per_layout():
         before = q6k.q6k_stats()
         gpu_util.gemm(xq, da, n, w, layout, m, k)
         after = q6k.q6k_stats()
-        assert after[layout] == before[layout] + 1 and after[1 - layout] == before[1 - layout]
+        for other in LAYOUTS:
+            assert after[other] == before[other] + (1 if other == layout else 0)
 
 
 def sampled_tokens(n, count, seed):
