@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layout", type=int, default=1, choices=[0, 1, 2])
+    ap.add_argument("--layout", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--workload", default="ffn_down_n3314")
     ap.add_argument("--cold", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

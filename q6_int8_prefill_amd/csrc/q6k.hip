@@ -762,8 +762,20 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   k.lane = threadIdx.x & 63;
   k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   k.loads_a = k.wave < kWgTokTiles;
-  const int64_t T0 = (int64_t)blockIdx.x * kWgTokTiles;  // the workgroup's first token tile
-  const int64_t R = (int64_t)blockIdx.y * 4 + k.wave;    // this wave's row tile
+  // XCD-aware tile order: workgroup pid = x + gx*y runs on XCD pid % 8, and each XCD has its own
+  // L2.  When the grid splits evenly, XCD j takes one (gx/2) x (gy/4) rectangle of the output,
+  // so each activation tile is fetched into 4 of the 8 L2s and each weight tile into 2
+  // (dispatch order would otherwise spread every tile over all 8).
+  int64_t bx = blockIdx.x, by = blockIdx.y;
+  if (gridDim.x % 2 == 0 && gridDim.y % 4 == 0) {
+    const int64_t pid = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+    const int64_t xcd = pid % 8, local = pid / 8;
+    const int64_t rw = gridDim.x / 2, rh = gridDim.y / 4;
+    bx = (xcd % 2) * rw + local % rw;
+    by = (xcd / 2) * rh + local / rw;
+  }
+  const int64_t T0 = bx * kWgTokTiles;     // the workgroup's first token tile
+  const int64_t R = by * 4 + k.wave;       // this wave's row tile
   const int64_t Ta = T0 + (k.loads_a ? k.wave : 0);
   const int64_t nsb = nchunk / 8;
   k.src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
