@@ -189,3 +189,25 @@ def test_gemm_full_size_sampled(name, layout):
     ok, worst = gpu_util.within_tolerance(y[rows], y_ref, t_ref)
     assert ok, f"worst |err|/T = {worst}"
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("name", ["attn_v_n3314", "ffn_down_n3314"])
+def test_folded_rounding_no_worse_than_split(name):
+    """Layout 2 combines the two 16-k halves of a chunk before any float rounding, but only after
+    each half's own int8 scale has been applied exactly in integers.  The pages warn that fusing
+    the halves before their scales breaks the 1e-3 gate ("r38 q6_K BT-style raw-byte mma kernel",
+    sec. 3.3, item 2); this checks that the folded form's error against the f64 reference stays
+    within the two-halves form's on the same inputs (measured: 3-5 times smaller)."""
+    import gpu_util
+    raw, x, n, m, k = gpu_util.cached_workload(name)
+    rows = sampled_tokens(n, 16, seed=7)
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    worst = {}
+    for layout in (1, 2):
+        xq, da, w = prepare(x, raw, m, layout)
+        y = gpu_util.gemm(xq, da, n, w, layout, m, k)[rows].astype(np.float64)
+        worst[layout] = float((np.abs(y - y_ref) / np.maximum(t_ref, 1e-300)).max())
+    print(f"{name}: worst |err|/T layout 1 {worst[1]:.3e}, layout 2 {worst[2]:.3e}", flush=True)
+    assert worst[2] <= 2 * worst[1]
+    assert worst[2] < 1e-6
