@@ -4,7 +4,7 @@
  *     Y[N x M] = X[N x K] . dequant(W_q6K[M x K])^T
  *
  * Method (page titles of the optimisation log it follows):
- *   "r38 q6_K BT-style raw-byte mma kernel (LANDED)"
+ *   "r38 — q6_K BT-style raw-byte mma kernel (LANDED)"
  *       sec. 2.1  q6_K super-block: 256 weights in 210 B -- ql[128] low nibbles at 0, qh[64] 2-bit
  *                 high fields at 128, int8 scales[16] at 192 (one per 16 weights), f16 d at 208;
  *                 w = d * sc[sub-block] * (q - 32)
@@ -12,10 +12,10 @@
  *       sec. 2.3  expanded B: weights staged as centered int8 (-32..31)
  *       sec. 2.4  KSPLIT=2: every 32-k chunk is two 16-k halves with their own integer dot and
  *                 their own d*sc rescale, applied as two independent f32 additions
- *   "r41 q6_K B-expand widened to uint4 group loads (LANDED)": B expanded from wide loads
- *   "r53 W_exp pre-expansion plane + cp.async B staging (LANDED)": optional load-time plane of
+ *   "r41 — q6_K B-expand widened to uint4 group loads (LANDED)": B expanded from wide loads
+ *   "r53 — q6_K bundle: W_exp pre-expansion plane + cp.async B staging (LANDED)": optional load-time plane of
  *       centered int8 weights (extra memory, no expand work in the GEMM)
- *   "r42 stage-wide dsc scale reads (REVERTED)", sec. 3.2 (W_dsc arm): d*sc precomputed as f32
+ *   "r42 — q6_K stage-wide dsc scale reads (REVERTED)", sec. 3.2 (W_dsc arm): d*sc precomputed as f32
  * Layout 2 applies the same weights (w = d * sc * (q - 32), "r38 ..." sec. 2.1) with the int8 sc
  * folded into the integer dot, so each 32-k chunk carries one f32 rescale da * d instead of two.
  *
@@ -85,7 +85,7 @@ enum { Q6K_LAYOUT_PACKED = 0, Q6K_LAYOUT_EXPANDED = 1, Q6K_LAYOUT_FOLDED = 2 };
  * of xq and stores the size of da in *da_bytes (may be NULL).  Returns 0 for invalid n/k. */
 size_t q6k_act_bytes(int64_t n, int64_t k, size_t* da_bytes);
 
-/* Activation quantize-transpose prepass ("r38 q6_K BT-style raw-byte mma kernel", sec. 2.2 and
+/* Activation quantize-transpose prepass ("r38 — q6_K BT-style raw-byte mma kernel", sec. 2.2 and
  * 3.2: int8 activations with one scale per token and 32-k chunk, laid out ahead of the GEMM).
  * For every token t < n and chunk c: amax = max |x|, da = amax / 127 (IEEE f32 division),
  * q = roundf(x / da) (IEEE f32 division, half away from zero) clamped to [-127, 127]; an

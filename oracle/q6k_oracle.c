@@ -7,13 +7,13 @@
  * no code, header, table or constant with the HIP kernels.
  *
  * Sources (titles of the pages of the optimisation log this follows):
- *   [r38]  "r38 q6_K BT-style raw-byte mma kernel (LANDED)"
+ *   [r38]  "r38 — q6_K BT-style raw-byte mma kernel (LANDED)"
  *            sec. 2.1  the real q6_K layout: ql[128] low nibbles, qh[64] 2-bit high fields,
  *                      scales[16] int8 (one per 16 elements), f16 d; w = d * sc[sub] * (q - 32)
  *            sec. 2.2  rescale without a dmin term: sum += da * dsc, dsc = d * sc[16-sub-block]
  *            sec. 2.4  KSPLIT=2: each 32-k chunk is two 16-k halves with their own integer sums
  *            sec. 3.2  the per-element index map (ql/qh index and shift) and the dsc offsets 192/208
- *   [r41]  "r41 q6_K B-expand widened to uint4 group loads (LANDED)", sec. 2: byte map of a block
+ *   [r41]  "r41 — q6_K B-expand widened to uint4 group loads (LANDED)", sec. 2: byte map of a block
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - activation scale: symmetric absmax per (token, 32-k chunk): da = amax / 127 in IEEE f32;

@@ -11,10 +11,10 @@
 //                         each chunk needs one f32 rescale instead of two; D = true exports the
 //                         per-chunk integer numerators
 //
-// The method follows "r38 q6_K BT-style raw-byte mma kernel (LANDED)" (sec. 2.1 layout,
-// sec. 2.2 rescale without dmin, sec. 2.4 KSPLIT=2), "r41 q6_K B-expand widened to uint4 group
-// loads (LANDED)" (expand from wide loads) and "r53 W_exp pre-expansion plane + cp.async B
-// staging (LANDED)" (optional pre-expanded plane).  The tiling is this library's own.
+// The method follows "r38 — q6_K BT-style raw-byte mma kernel (LANDED)" (sec. 2.1 layout,
+// sec. 2.2 rescale without dmin, sec. 2.4 KSPLIT=2), "r41 — q6_K B-expand widened to uint4
+// group loads (LANDED)" (expand from wide loads) and "r53 — q6_K bundle: W_exp pre-expansion
+// plane + cp.async B staging (LANDED)" (optional pre-expanded plane).  The tiling is this library's own.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 

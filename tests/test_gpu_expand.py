@@ -1,6 +1,6 @@
 """GPU parity of q6k_expand_weights (all three layouts) against the oracle decode: byte-exact
-codes, exact scales.  Shapes include those of the pages' byte-exactness test ("r53 W_exp pre-expansion
-plane + cp.async B staging", sec. 4: (64,256), (40,512), (24,768))."""
+codes, exact scales.  Shapes include those of the pages' byte-exactness test ("r53 — q6_K bundle:
+W_exp pre-expansion plane + cp.async B staging (LANDED)", sec. 4: (64,256), (40,512), (24,768))."""
 import numpy as np
 import pytest
 

@@ -1,7 +1,7 @@
 """GPU parity of q6k_gemm / q6k_gemm_subdots / q6k_gemm_chunkdots against the oracle.
 
-  * per-sub-block int32 dots (layouts 0 and 1): bit-exact (the KSPLIT=2 halves of "r38 q6_K
-    BT-style raw-byte mma kernel", sec. 2.4), exported by the same kernel source;
+  * per-sub-block int32 dots (layouts 0 and 1): bit-exact (the KSPLIT=2 halves of "r38 — q6_K
+    BT-style raw-byte mma kernel (LANDED)", sec. 2.4), exported by the same kernel source;
   * per-chunk numerators sc*D summed over both halves (layout 2): bit-exact, exported by the same
     kernel source after its float reconstruction of the two digit products;
   * outputs: |y - y_ref| <= 1e-3 * sum|terms| per element, for every element at sizes the
@@ -195,7 +195,7 @@ def test_gemm_full_size_sampled(name, layout):
 def test_folded_rounding_no_worse_than_split(name):
     """Layout 2 combines the two 16-k halves of a chunk before any float rounding, but only after
     each half's own int8 scale has been applied exactly in integers.  The pages warn that fusing
-    the halves before their scales breaks the 1e-3 gate ("r38 q6_K BT-style raw-byte mma kernel",
+    the halves before their scales breaks the 1e-3 gate ("r38 — q6_K BT-style raw-byte mma kernel",
     sec. 3.3, item 2); this checks that the folded form's error against the f64 reference stays
     within the two-halves form's on the same inputs (measured: 3-5 times smaller)."""
     import gpu_util

@@ -2,12 +2,12 @@
 
 The decode is checked against what the pages fix, not against itself:
   * hand-built blocks whose codes follow from the byte map of a block
-    ("r41 q6_K B-expand widened to uint4 group loads", sec. 2; "r38 q6_K BT-style raw-byte mma
-    kernel", sec. 2.1);
+    ("r41 — q6_K B-expand widened to uint4 group loads (LANDED)", sec. 2; "r38 — q6_K BT-style
+    raw-byte mma kernel (LANDED)", sec. 2.1);
   * the worked example of element 70 (r38 sec. 2.1), stored under tests/golden/;
   * the two other statements of the same index map that the pages print: the dense load-time
-    expander that walks a block in (half, 64-byte run) order ("r53 W_exp pre-expansion plane",
-    sec. 3.2) and the 16-element group closed form of the wide-load expand (r41 sec. 3.2),
+    expander that walks a block in (half, 64-byte run) order ("r53 — q6_K bundle: W_exp
+    pre-expansion plane + cp.async B staging (LANDED)", sec. 3.2) and the 16-element group closed form of the wide-load expand (r41 sec. 3.2),
     re-expressed here in vectorised numpy;
   * the f16 d conversion against numpy's own binary16 decoder, including subnormals.
 """

@@ -2,7 +2,7 @@
 
   * brute force: the per-16-element dots against numpy's integer einsum, and the f64 output
     against a plain f64 matmul of (da * xq) with the dequantized weights -- the q6_K rescale
-    without a dmin term ("r38 q6_K BT-style raw-byte mma kernel", sec. 2.2) is exactly that
+    without a dmin term ("r38 — q6_K BT-style raw-byte mma kernel", sec. 2.2) is exactly that
     product in exact arithmetic;
   * an exact special case: activations already on the int8 grid (da = 1) and power-of-two d
     make the output equal X @ W^T exactly in f64;

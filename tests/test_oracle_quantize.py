@@ -1,7 +1,7 @@
 """Pins for the oracle's activation quantization (CPU only).
 
-The pages give only "a per-token-block quantization scale" for the activations ("r38 q6_K
-BT-style raw-byte mma kernel", sec. 2.2).  The reading adopted (symmetric absmax per 32-k chunk,
+The pages name only a scale per token block for the activations ("r38 — q6_K BT-style raw-byte
+mma kernel (LANDED)", sec. 2.2).  The reading adopted (symmetric absmax per 32-k chunk,
 da = amax/127 in f32, q = round-half-away(x/da) clamped to +-127, zero chunk -> da = 0, q = 0) is
 pinned here by special cases with known answers and by closed-form invariants of that reading.
 """
