@@ -58,19 +58,28 @@ def cpu_baseline(raw, x, m, k, tokens):
                       f"{dt:.1f} s single-threaded"}
 
 
+def kernel_source_digest():
+    """sha256 (16 hex digits) of the kernel source with comments and whitespace removed: it
+    changes when the code changes, not when only its comments do."""
+    import hashlib
+    import re
+    with open(os.path.join(ROOT, "q6_int8_prefill_amd", "csrc", "q6k.hip")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def counter_traffic(workload, layout):
     """HBM-side bytes of one GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
-    or None if there is none for this workload or the kernel source changed since it was taken."""
-    import hashlib
+    or None if there is none for this workload or the kernel code changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
-    src = os.path.join(ROOT, "q6_int8_prefill_amd", "csrc", "q6k.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != digest:
+    if rec.get("kernel_code_sha256_16") != kernel_source_digest():
         return None
     entry = rec.get("layouts", {}).get(str(layout))
     return None if entry is None else int(entry["traffic_bytes"])
