@@ -48,6 +48,7 @@ def _load():
         lib.q6o_quantize.argtypes = [p, i64, i64, p, p]
         lib.q6o_subdots.argtypes = [p, p, i64, i64, i64, p]
         lib.q6o_chunkdots.argtypes = [p, p, i64, i64, i64, p]
+        lib.q6o_swiglu.argtypes = [p, p, i64, p]
         lib.q6o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p]
         _lib = lib
     return _lib
@@ -113,6 +114,16 @@ def subdots(xq, raw, m):
     raw = _raw(raw, m, k)
     out = np.empty((n, m, k // 16), np.int32)
     _load().q6o_subdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
+    return out
+
+
+def swiglu(gate, up):
+    """-> f64 array of up * silu(gate) (same shape), from f32 inputs."""
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    up = np.ascontiguousarray(up, dtype=np.float32)
+    assert gate.shape == up.shape
+    out = np.empty(gate.shape, np.float64)
+    _load().q6o_swiglu(_ptr(gate), _ptr(up), gate.size, _ptr(out))
     return out
 
 

@@ -150,6 +150,17 @@ void q6o_subdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int
   free(wc);
 }
 
+/* SwiGLU product feeding ffn_down, in f64: h = up * silu(gate), silu(g) = g / (1 + exp(-g)), for
+ * `count` elements.  The pages quantize this product right after it is produced (the fused
+ * producers of "r53 — q6_K bundle: W_exp pre-expansion plane + cp.async B staging (LANDED)",
+ * sec. 1); the quantization itself is q6o_quantize. */
+void q6o_swiglu(const float* gate, const float* up, int64_t count, double* h) {
+  for (int64_t i = 0; i < count; ++i) {
+    double g = (double)gate[i];
+    h[i] = (double)up[i] * (g / (1.0 + exp(-g)));
+  }
+}
+
 /* Per-chunk integer numerators with the sub-block scales applied:
  *   E[n][m][c] = sum over the 32 elements i of chunk c of xq[n][i] * sc[m][i/16] * (q[m][i] - 32)
  * (int64 accumulation, stored as int32: |E| <= 32 * 127 * 4096 < 2^24).  [r38 sec. 2.1] gives
