@@ -6,13 +6,15 @@ One step = one pass of the hot path over one batch: the activation quantize-tran
 before timing starts.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1] [--workload NAME]
-                    [--cold] [--no-cpu-baseline] [--copy-probe-mib MIB]
+                    [--cold] [--swiglu] [--no-cpu-baseline] [--copy-probe-mib MIB]
 
 Workloads: tiny, attn_v_n512, attn_v_n3314, ffn_down_n3314 (the default and headline case), and
 sweep32: 32 layers of (attn_v 4096x4096 + ffn_down 4096x11008) at 3314 tokens, 64 GEMMs back to
 back on one stream over 1.6 GB of raw weights, inputs drawn on the device.  --cold writes a
 512 MiB scrub buffer before every timed step, so weights and activations come from HBM rather
-than the 256 MB Infinity Cache.
+than the 256 MB Infinity Cache.  --swiglu (single workloads) replaces the prepass by the fused
+producer q6k_swiglu_quantize_act reading the two SwiGLU factors, and also times the unfused pair
+(q6k_swiglu_f32 writing h, then q6k_quantize_act) once for comparison.
 """
 import argparse
 import json
@@ -36,6 +38,8 @@ def parse():
     ap.add_argument("--layout", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--workload", default="ffn_down_n3314")
     ap.add_argument("--cold", action="store_true")
+    ap.add_argument("--swiglu", action="store_true",
+                    help="feed the GEMM from the fused SwiGLU -> int8 producer (gate, up inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -88,9 +92,10 @@ def counter_traffic(workload, layout):
 class Problem:
     """Device buffers of one GEMM: activations, prepared weights, quantized activations, output."""
 
-    def __init__(self, q6k, torch, x_d, raw_d, n, m, k, layout, dev):
+    def __init__(self, q6k, torch, x_d, raw_d, n, m, k, layout, dev, up_d=None):
         self.q6k, self.n, self.m, self.k, self.layout = q6k, n, m, k, layout
         self.x = x_d
+        self.up = up_d  # with up: x is the gate and the producer is the fused SwiGLU quantize
         xb, db = q6k.q6k_act_bytes(n, k)
         self.xq = torch.empty(xb, dtype=torch.uint8, device=dev)
         self.da = torch.empty(db // 4, dtype=torch.float32, device=dev)
@@ -99,7 +104,10 @@ class Problem:
         q6k.q6k_expand_weights(raw_d, m, k, layout, self.w)
 
     def quantize(self):
-        self.q6k.q6k_quantize_act(self.x, self.xq, self.da)
+        if self.up is None:
+            self.q6k.q6k_quantize_act(self.x, self.xq, self.da)
+        else:
+            self.q6k.q6k_swiglu_quantize_act(self.x, self.up, self.xq, self.da)
 
     def gemm(self):
         self.q6k.q6k_gemm(self.xq, self.da, self.n, self.w, self.layout, self.m, self.k, self.y)
@@ -108,8 +116,9 @@ class Problem:
         """Algorithmic bytes: GEMM = weights as stored + int8 activations + f32 scales + f32 Y;
         prepass = f32 X + int8 activations + f32 scales."""
         a_bytes = self.n * self.k + self.n * (self.k // 32) * 4
+        x_bytes = self.n * self.k * (4 if self.up is None else 8)
         return {"gemm": self.w.numel() + a_bytes + self.n * self.m * 4,
-                "prepass": self.n * self.k * 4 + a_bytes}
+                "prepass": x_bytes + a_bytes}
 
 
 def main():
@@ -142,6 +151,15 @@ def main():
                 x_d = synthetic.activations_torch(s["n"], s["k"], s["seed"], dev, s["x"])
                 problems.append(Problem(q6k, torch, x_d, raw_d, s["n"], s["m"], s["k"], layout, dev))
                 del raw_d
+    elif args.swiglu:
+        spec = synthetic.WORKLOADS[args.workload]
+        n, m, k = spec["n"], spec["m"], spec["k"]
+        raw = synthetic.weights(m, k, spec["seed"])
+        gate, up = synthetic.swiglu_inputs(n, k, spec["seed"])
+        raw_d = torch.from_numpy(raw.reshape(-1)).to(dev)
+        problems.append(Problem(q6k, torch, torch.from_numpy(gate).to(dev), raw_d, n, m, k,
+                                layout, dev, up_d=torch.from_numpy(up).to(dev)))
+        raw = None  # the CPU baseline quantizes x; here the input is the factor pair
     else:
         raw, x, n, m, k = synthetic.workload(args.workload)
         x_d = torch.from_numpy(x).to(dev)
@@ -152,8 +170,8 @@ def main():
 
     # load-time weight preparation of the first matrix, timed once on its own
     p0 = problems[0]
-    raw0 = (synthetic.weights_torch(p0.m, p0.k, 7, dev) if sweep
-            else torch.from_numpy(raw.reshape(-1)).to(dev))
+    raw0 = (torch.from_numpy(raw.reshape(-1)).to(dev) if raw is not None
+            else synthetic.weights_torch(p0.m, p0.k, 7, dev))
     e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_a.record(stream)
     q6k.q6k_expand_weights(raw0, p0.m, p0.k, layout, p0.w)
@@ -243,6 +261,8 @@ def main():
     else:
         config = {"workload": args.workload, "n": p0.n, "m": p0.m, "k": p0.k, "layout": layout,
                   "cold": args.cold, "step": "q6k_quantize_act + q6k_gemm"}
+        if args.swiglu:
+            config["producer"] = "fused SwiGLU (gate, up f32 inputs)"
 
     out = {
         "metric": METRIC,
@@ -283,6 +303,29 @@ def main():
                      "algorithmic_per_launch": {"int8_ops": 2.0 * p0.n * p0.m * p0.k,
                                                 "bytes": p0.alg_bytes()["gemm"]}},
     }
+    if args.swiglu:
+        # the unfused pair for comparison: h written by q6k_swiglu_f32, then q6k_quantize_act
+        h = torch.empty((p0.n, p0.k), dtype=torch.float32, device=dev)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        reps = 20
+        for _ in range(3):
+            q6k.q6k_swiglu_f32(p0.x, p0.up, h)
+            q6k.q6k_quantize_act(h, p0.xq, p0.da)
+        torch.cuda.synchronize()
+        t_sw = t_q = 0.0
+        for _ in range(reps):
+            e[0].record(stream)
+            q6k.q6k_swiglu_f32(p0.x, p0.up, h)
+            e[1].record(stream)
+            q6k.q6k_quantize_act(h, p0.xq, p0.da)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            t_sw += e[0].elapsed_time(e[1]) * 1e3 / reps
+            t_q += e[1].elapsed_time(e[2]) * 1e3 / reps
+        out["producer"] = {"fused_us": out["prepass"]["total_us_per_step"],
+                           "unfused_swiglu_us": round(t_sw, 2), "unfused_quantize_us": round(t_q, 2),
+                           "unfused_total_us": round(t_sw + t_q, 2)}
+        out["config"]["step"] = "q6k_swiglu_quantize_act + q6k_gemm"
     if not args.no_cpu_baseline and raw is not None:
         out["cpu_baseline"] = cpu_baseline(raw, x, p0.m, p0.k, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

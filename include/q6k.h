@@ -96,6 +96,22 @@ size_t q6k_act_bytes(int64_t n, int64_t k, size_t* da_bytes);
 q6k_status q6k_quantize_act(const float* x, int64_t n, int64_t k, int64_t ldx, void* xq,
                             size_t xq_bytes, float* da, size_t da_bytes, void* stream);
 
+/* Fused producer for ffn_down: quantizes h = up * silu(gate), silu(g) = g / (1 + e^-g), exactly as
+ * q6k_quantize_act quantizes x, without writing h ("r53 — q6_K bundle: W_exp pre-expansion
+ * plane + cp.async B staging (LANDED)", sec. 1: the SwiGLU product's producers fused).  h is
+ * formed in f32 with expf (a few ulp); the codes and da are those q6k_quantize_act gives for that
+ * f32 h.
+ *   gate, up: f32 [n][ld] row-major, ld >= k, ld % 4 == 0, both 16-byte aligned
+ *   xq, da  : tiled outputs as for q6k_quantize_act */
+q6k_status q6k_swiglu_quantize_act(const float* gate, const float* up, int64_t n, int64_t k,
+                                   int64_t ld, void* xq, size_t xq_bytes, float* da,
+                                   size_t da_bytes, void* stream);
+
+/* Test-only export of the producer's f32 h = up * silu(gate): h [n][ldh] row-major, ldh >= k;
+ * 4-byte aligned pointers; n * k below 2^38. */
+q6k_status q6k_swiglu_f32(const float* gate, const float* up, int64_t n, int64_t k, int64_t ld,
+                          float* h, int64_t ldh, void* stream);
+
 /* Size in bytes of the weight buffer of an m x k q6_K matrix in `layout`; 0 if invalid. */
 size_t q6k_weight_bytes(int64_t m, int64_t k, int layout);
 

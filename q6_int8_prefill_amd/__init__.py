@@ -19,5 +19,7 @@ from ._lib import (  # noqa: F401
     q6k_quantize_act,
     q6k_stats,
     q6k_strerror,
+    q6k_swiglu_f32,
+    q6k_swiglu_quantize_act,
     q6k_weight_bytes,
 )

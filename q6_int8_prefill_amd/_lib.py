@@ -20,6 +20,10 @@ _lib.q6k_act_bytes.restype = _sz
 _lib.q6k_act_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
 _lib.q6k_quantize_act.restype = _int
 _lib.q6k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
+_lib.q6k_swiglu_quantize_act.restype = _int
+_lib.q6k_swiglu_quantize_act.argtypes = [_p, _p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
+_lib.q6k_swiglu_f32.restype = _int
+_lib.q6k_swiglu_f32.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p]
 _lib.q6k_weight_bytes.restype = _sz
 _lib.q6k_weight_bytes.argtypes = [_i64, _i64, _int]
 _lib.q6k_expand_weights.restype = _int
@@ -35,7 +39,8 @@ _lib.q6k_strerror.argtypes = [_int]
 _lib.q6k_stats.restype = None
 _lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
 
-EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_weight_bytes", "q6k_expand_weights",
+EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_swiglu_quantize_act", "q6k_swiglu_f32",
+           "q6k_weight_bytes", "q6k_expand_weights",
            "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots", "q6k_strerror", "q6k_stats")
 
 
@@ -101,6 +106,42 @@ def q6k_quantize_act(x, xq, da, n=None, k=None, ldx=None, stream=None):
         raise ValueError("n, k exceed the shape of x")
     _check(_lib.q6k_quantize_act(_ptr(x), n, k, ldx, _ptr(xq), _nbytes(xq), _ptr(da),
                                  _nbytes(da), _stream(stream)), "q6k_quantize_act")
+
+
+def _rows_f32(name, t, n, k):
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [n][ld]")
+    if t.numel() and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major")
+    if t.numel() and (n > t.shape[0] or k > t.shape[1]):
+        raise ValueError(f"n, k exceed the shape of {name}")
+
+
+def q6k_swiglu_quantize_act(gate, up, xq, da, n=None, k=None, stream=None):
+    """gate, up f32 [n][ld] (device, same strides) -> tiled xq, da of h = up * silu(gate)."""
+    n = gate.shape[0] if n is None else n
+    k = gate.shape[1] if k is None else k
+    _rows_f32("gate", gate, n, k)
+    _rows_f32("up", up, n, k)
+    if gate.stride(0) != up.stride(0):
+        raise ValueError("gate and up must share their row stride")
+    _check(_lib.q6k_swiglu_quantize_act(_ptr(gate), _ptr(up), n, k, gate.stride(0), _ptr(xq),
+                                        _nbytes(xq), _ptr(da), _nbytes(da), _stream(stream)),
+           "q6k_swiglu_quantize_act")
+
+
+def q6k_swiglu_f32(gate, up, h, stream=None):
+    """Test-only: h = up * silu(gate) as the fused producer forms it (f32 [n][k] tensors)."""
+    n, k = gate.shape
+    _rows_f32("gate", gate, n, k)
+    _rows_f32("up", up, n, k)
+    _rows_f32("h", h, n, k)
+    if gate.stride(0) != up.stride(0):
+        raise ValueError("gate and up must share their row stride")
+    _check(_lib.q6k_swiglu_f32(_ptr(gate), _ptr(up), n, k, gate.stride(0), _ptr(h), h.stride(0),
+                               _stream(stream)), "q6k_swiglu_f32")
 
 
 def q6k_expand_weights(w_raw, m, k, layout, w_out, stream=None):

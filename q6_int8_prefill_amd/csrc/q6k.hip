@@ -48,62 +48,108 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Prepass.  Block = 32 tokens (one token tile) x 8 chunks; thread (p, cc) owns token 32T + p and
-// chunk 8*blockIdx.y + cc.  Each thread reads its 128 contiguous input bytes, computes
-// da = amax / 127 and q = roundf(x / da) with correctly rounded f32 divisions, and writes the two
-// 16-byte lane slots of that token (lane p and lane p + 32) plus its da.
+// Prepass.  Block = 4 waves = one token tile (32 tokens) x 8 chunks (256 k values).  Wave w walks
+// tokens 8w .. 8w+7 of the tile; per token its 64 lanes read the 1 KiB of those 256 values with
+// one coalesced 16-byte load each (lane l holds k 4l .. 4l+3 of the window, chunk l / 8).  The 8
+// lanes of a chunk exchange their maxima (da = amax / 127, IEEE f32), each quantizes its four
+// values (q = roundf(x / da), correctly rounded f32 division, clamped to +-127) and puts them, as
+// one 4-byte word, at their place of the tiled layout in LDS; the block then writes its eight
+// 1 KiB code blocks and 1 KiB of scales with coalesced 16-byte stores.
+// With SWIGLU the input value is produced on the fly from two rows, h = up * silu(gate), so that
+// the f32 product feeding ffn_down is quantized without ever being written ("r53 — q6_K bundle:
+// W_exp pre-expansion plane + cp.async B staging (LANDED)", sec. 1: fused producers).
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x, int64_t n,
-                                                           int64_t ldx, int64_t nchunk,
+
+// up * silu(gate), silu(g) = g / (1 + e^-g), in f32 (expf within a few ulp; e^-g overflows to
+// infinity for very negative g and gives a signed zero).  The test export computes h with this
+// same function.
+__device__ __forceinline__ float swiglu_f32(float g, float u) { return u * (g / (1.0f + expf(-g))); }
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x,
+                                                           const float* __restrict__ up,
+                                                           int64_t n, int64_t ldx, int64_t nchunk,
                                                            uint8_t* __restrict__ xq,
                                                            float* __restrict__ da) {
-  const int p = threadIdx.x & 31;
-  const int64_t c = (int64_t)blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t T = blockIdx.x;
-  if (c >= nchunk) return;
-  const int64_t tok = T * kTile + p;
-  float v[32];
-  if (tok < n) {
-    const float4* src = reinterpret_cast<const float4*>(x + tok * ldx + c * 32);
+  const int64_t c = (int64_t)blockIdx.y * 8 + (lane >> 3);  // this lane's chunk
+  const int kk = 4 * (lane & 7);                             // its first k inside the chunk
+  const bool live_c = c < nchunk;
+  // place of the lane's 4 codes in the chunk's 1 KiB block: slot p + 32*g, byte 8*h + kk % 8
+  const int g = (kk >> 3) & 1, h = kk >> 4;
+  __shared__ __attribute__((aligned(16))) uint8_t codes[8 * 1024];
+  __shared__ __attribute__((aligned(16))) float scales[8 * 32];
+  // all eight loads first (eight rows in flight per wave), then the arithmetic
+  float4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 f = src[i];
-      v[4 * i + 0] = f.x;
-      v[4 * i + 1] = f.y;
-      v[4 * i + 2] = f.z;
-      v[4 * i + 3] = f.w;
+  for (int j = 0; j < 8; ++j) {
+    const int64_t tok = T * kTile + 8 * wave + j;
+    v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tok < n && live_c) v[j] = *reinterpret_cast<const float4*>(x + tok * ldx + c * 32 + kk);
+  }
+  if (SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t tok = T * kTile + 8 * wave + j;
+      if (tok < n && live_c) {
+        const float4 u = *reinterpret_cast<const float4*>(up + tok * ldx + c * 32 + kk);
+        v[j].x = swiglu_f32(v[j].x, u.x);
+        v[j].y = swiglu_f32(v[j].y, u.y);
+        v[j].z = swiglu_f32(v[j].z, u.z);
+        v[j].w = swiglu_f32(v[j].w, u.w);
+      }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
   }
-  float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const float scale = amax / 127.0f;
-  int q[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float r = 0.0f;
-    if (scale != 0.0f) r = fminf(fmaxf(roundf(v[i] / scale), -127.0f), 127.0f);
-    q[i] = (int)r;
+  for (int j = 0; j < 8; ++j) {
+    const int p = 8 * wave + j;
+    float amax = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const float scale = amax / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (scale != 0.0f) {
+      q0 = (int)fminf(fmaxf(roundf(v[j].x / scale), -127.0f), 127.0f);
+      q1 = (int)fminf(fmaxf(roundf(v[j].y / scale), -127.0f), 127.0f);
+      q2 = (int)fminf(fmaxf(roundf(v[j].z / scale), -127.0f), 127.0f);
+      q3 = (int)fminf(fmaxf(roundf(v[j].w / scale), -127.0f), 127.0f);
+    }
+    // stage the tile's codes and scales in LDS in their global order
+    *reinterpret_cast<uint32_t*>(codes + (lane >> 3) * 1024 + (p + 32 * g) * kFragBytes + 8 * h +
+                                 (kk & 7)) = pack4(q0, q1, q2, q3);
+    // token p = 8*qq + 4*gg + r  ->  float slot 16*gg + 4*qq + r
+    if ((lane & 7) == 0) scales[(lane >> 3) * 32 + 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3)] = scale;
   }
-  // lane p   : k 0..7  (half 0) and k 16..23 (half 1)
-  // lane p+32: k 8..15 (half 0) and k 24..31 (half 1)
-  uint4 s0, s1;
-  s0.x = pack4(q[0], q[1], q[2], q[3]);
-  s0.y = pack4(q[4], q[5], q[6], q[7]);
-  s0.z = pack4(q[16], q[17], q[18], q[19]);
-  s0.w = pack4(q[20], q[21], q[22], q[23]);
-  s1.x = pack4(q[8], q[9], q[10], q[11]);
-  s1.y = pack4(q[12], q[13], q[14], q[15]);
-  s1.z = pack4(q[24], q[25], q[26], q[27]);
-  s1.w = pack4(q[28], q[29], q[30], q[31]);
-  uint4* dst = reinterpret_cast<uint4*>(xq + (T * nchunk + c) * 64 * kFragBytes);
-  dst[p] = s0;
-  dst[p + 32] = s1;
-  // token p = 8*qq + 4*g + r  ->  float slot 16*g + 4*qq + r
-  da[(T * nchunk + c) * 32 + 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3)] = scale;
+  __syncthreads();
+  // coalesced stores: thread t writes 32 bytes of chunk t / 32's 1 KiB block; threads 0..63 the
+  // 8 x 32 scales
+  const int t = threadIdx.x;
+  const int64_t ct = (int64_t)blockIdx.y * 8 + (t >> 5);
+  if (ct < nchunk) {
+    const uint4* srcq = reinterpret_cast<const uint4*>(codes + t * 32);
+    uint4* dstq = reinterpret_cast<uint4*>(xq + (T * nchunk + ct) * 64 * kFragBytes + (t & 31) * 32);
+    dstq[0] = srcq[0];
+    dstq[1] = srcq[1];
+  }
+  if (t < 64) {
+    const int64_t cd = (int64_t)blockIdx.y * 8 + (t >> 3);
+    if (cd < nchunk)
+      reinterpret_cast<float4*>(da + (T * nchunk + cd) * 32)[t & 7] =
+          reinterpret_cast<const float4*>(scales)[t];
+  }
+}
+
+// Test export: h = up * silu(gate) with the producer's own function, row-major [n][ldh].
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ gate,
+                                                     const float* __restrict__ up, int64_t n,
+                                                     int64_t k, int64_t ld, float* __restrict__ h,
+                                                     int64_t ldh) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * k) return;
+  const int64_t t = i / k, e = i % k;
+  h[t * ldh + e] = swiglu_f32(gate[t * ld + e], up[t * ld + e]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -942,6 +988,28 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   return st;
 }
 
+template <bool SWIGLU>
+q6k_status quantize_common(const float* x, const float* up, int64_t n, int64_t k, int64_t ldx,
+                           void* xq, size_t xq_bytes, float* da, size_t da_bytes, void* stream) {
+  if (n < 0) return Q6K_EINVAL;
+  if (k <= 0 || k % 256) return Q6K_ESHAPE;
+  size_t need_x, need_d;
+  if (!act_sizes(n, k, &need_x, &need_d)) return Q6K_ESIZE;
+  if (n == 0) return Q6K_OK;
+  if (!x || !xq || !da) return Q6K_EINVAL;
+  if (ldx < k) return Q6K_EINVAL;
+  if (!aligned16(x) || ldx % 4 || !aligned16(xq) || !aligned16(da)) return Q6K_EALIGN;
+  if (xq_bytes < need_x || da_bytes < need_d) return Q6K_ESIZE;
+  const int64_t np = round_up(n, kWgTok);
+  const int64_t nchunk = k / 32;
+  const int64_t gx = np / kTile, gy = (nchunk + 7) / 8;
+  if (gx > INT32_MAX || gy > 65535) return Q6K_ESIZE;
+  hipLaunchKernelGGL(quantize_act_kernel<SWIGLU>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), x, up, n, ldx, nchunk,
+                     static_cast<uint8_t*>(xq), da);
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -958,22 +1026,27 @@ size_t q6k_act_bytes(int64_t n, int64_t k, size_t* da_bytes) {
 
 q6k_status q6k_quantize_act(const float* x, int64_t n, int64_t k, int64_t ldx, void* xq,
                             size_t xq_bytes, float* da, size_t da_bytes, void* stream) {
-  if (n < 0) return Q6K_EINVAL;
-  if (k <= 0 || k % 256) return Q6K_ESHAPE;
-  size_t need_x, need_d;
-  if (!act_sizes(n, k, &need_x, &need_d)) return Q6K_ESIZE;
-  if (n == 0) return Q6K_OK;
-  if (!x || !xq || !da) return Q6K_EINVAL;
-  if (ldx < k) return Q6K_EINVAL;
-  if (!aligned16(x) || ldx % 4 || !aligned16(xq) || !aligned16(da)) return Q6K_EALIGN;
-  if (xq_bytes < need_x || da_bytes < need_d) return Q6K_ESIZE;
-  const int64_t np = round_up(n, kWgTok);
-  const int64_t nchunk = k / 32;
-  const int64_t gx = np / kTile, gy = (nchunk + 7) / 8;
-  if (gx > INT32_MAX || gy > 65535) return Q6K_ESIZE;
-  hipLaunchKernelGGL(quantize_act_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), x, n, ldx, nchunk,
-                     static_cast<uint8_t*>(xq), da);
+  return quantize_common<false>(x, nullptr, n, k, ldx, xq, xq_bytes, da, da_bytes, stream);
+}
+
+q6k_status q6k_swiglu_quantize_act(const float* gate, const float* up, int64_t n, int64_t k,
+                                   int64_t ld, void* xq, size_t xq_bytes, float* da,
+                                   size_t da_bytes, void* stream) {
+  if (n > 0 && !up) return Q6K_EINVAL;
+  if (n > 0 && up && !aligned16(up)) return Q6K_EALIGN;
+  return quantize_common<true>(gate, up, n, k, ld, xq, xq_bytes, da, da_bytes, stream);
+}
+
+q6k_status q6k_swiglu_f32(const float* gate, const float* up, int64_t n, int64_t k, int64_t ld,
+                          float* h, int64_t ldh, void* stream) {
+  if (n < 0 || k < 0) return Q6K_EINVAL;
+  if (n == 0 || k == 0) return Q6K_OK;
+  if (!gate || !up || !h) return Q6K_EINVAL;
+  if (ld < k || ldh < k) return Q6K_EINVAL;
+  if (((uintptr_t)gate | (uintptr_t)up | (uintptr_t)h) & 3) return Q6K_EALIGN;
+  if (n > kMaxDim || k > kMaxDim || k > ((int64_t)1 << 38) / n) return Q6K_ESIZE;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)((n * k + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), gate, up, n, k, ld, h, ldh);
   return launch_status();
 }
 

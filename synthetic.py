@@ -69,6 +69,15 @@ def activations(n, k, seed, kind="normal"):
     raise ValueError(kind)
 
 
+def swiglu_inputs(n, k, seed):
+    """(gate, up) f32 [n][k]: the two factors of the post-SwiGLU activations that
+    activations(n, k, seed, "swiglu") forms in f64 (up = a, gate = b, same draws)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 10**6))
+    a = rng.standard_normal(size=(n, k))
+    b = rng.standard_normal(size=(n, k))
+    return b.astype(np.float32), a.astype(np.float32)
+
+
 def workload(name):
     """-> (raw weights, activations, n, m, k) for a named workload."""
     w = WORKLOADS[name]

@@ -17,12 +17,12 @@ def lib():
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "q6k.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q6k_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(q6k_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     L = lib()
     for name in names:
         assert hasattr(L, name), name
@@ -114,3 +114,18 @@ def test_strerror_and_stats():
         assert isinstance(q6k.q6k_strerror(s), str) and q6k.q6k_strerror(s)
     counts = q6k.q6k_stats()
     assert len(counts) == 3 and all(c >= 0 for c in counts)
+
+
+def test_swiglu_errors():
+    L = lib()
+    good = (FAKE, FAKE, 4, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, None)
+    assert L.q6k_swiglu_quantize_act(*good[:2], 4, 300, 300, *good[5:]) == -2       # k % 256
+    assert L.q6k_swiglu_quantize_act(FAKE, None, *good[2:]) == -1                   # null up
+    assert L.q6k_swiglu_quantize_act(FAKE, FAKE + 4, *good[2:]) == -3               # misaligned up
+    assert L.q6k_swiglu_quantize_act(FAKE + 4, FAKE, *good[2:]) == -3               # misaligned gate
+    assert L.q6k_swiglu_quantize_act(FAKE, FAKE, 4, 256, 255, *good[5:]) == -1      # ld < k
+    assert L.q6k_swiglu_quantize_act(FAKE, FAKE, 4, 256, 256, FAKE, 100, FAKE, 1 << 30, None) == -4
+    assert L.q6k_swiglu_quantize_act(None, None, 0, 256, 256, None, 0, None, 0, None) == 0
+    assert L.q6k_swiglu_f32(FAKE, FAKE, 4, 256, 255, FAKE, 256, None) == -1
+    assert L.q6k_swiglu_f32(FAKE, FAKE, 4, 256, 256, FAKE + 2, 256, None) == -3
+    assert L.q6k_swiglu_f32(FAKE, FAKE, 0, 256, 256, None, 256, None) == 0
