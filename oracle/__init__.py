@@ -14,7 +14,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "q6k_oracle.c")
+_SRC = [os.path.join(_HERE, "q6k_oracle.c"), os.path.join(_HERE, "q4k_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "_build", "libq6k_oracle.so")
 _lib = None
 
@@ -27,7 +27,7 @@ def build():
     os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
     tmp = _LIB_PATH + ".tmp"
     subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
-                           _SRC, "-o", tmp, "-lm"])
+                           *_SRC, "-o", tmp, "-lm"])
     os.replace(tmp, _LIB_PATH)
 
 
@@ -49,6 +49,14 @@ def _load():
         lib.q6o_subdots.argtypes = [p, p, i64, i64, i64, p]
         lib.q6o_chunkdots.argtypes = [p, p, i64, i64, i64, p]
         lib.q6o_swiglu.argtypes = [p, p, i64, p]
+        lib.q4o_scale_min.argtypes = [p, ctypes.c_int, p, p]
+        lib.q4o_code.restype = ctypes.c_int
+        lib.q4o_code.argtypes = [p, ctypes.c_int]
+        lib.q4o_decode.argtypes = [p, i64, i64, p, p, p, p, p]
+        lib.q4o_dequant.argtypes = [p, i64, i64, p]
+        lib.q4o_chunkdots.argtypes = [p, p, i64, i64, i64, p]
+        lib.q4o_chunksums.argtypes = [p, i64, i64, p]
+        lib.q4o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p]
         lib.q6o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p]
         _lib = lib
     return _lib
@@ -147,4 +155,83 @@ def gemm(xq, da, raw, m):
     y = np.empty((n, m), np.float64)
     t = np.empty((n, m), np.float64)
     _load().q6o_gemm(_ptr(xq), _ptr(da), n, _ptr(raw), m, k, _ptr(y), _ptr(t))
+    return y, t
+
+
+# ------------------------------------------------------------------------------------------------
+# q4_K (q4k_oracle.c)
+# ------------------------------------------------------------------------------------------------
+Q4_BLOCK_BYTES = 144
+
+
+def _raw4(raw, m, k):
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    assert raw.size == m * (k // QK) * Q4_BLOCK_BYTES, (raw.size, m, k)
+    return raw
+
+
+def q4_scale_min(scales12, j):
+    """-> (sc, m) 6-bit pair of sub-block j from the 12 scale bytes."""
+    s = np.ascontiguousarray(scales12, dtype=np.uint8)
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    _load().q4o_scale_min(_ptr(s), int(j), ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def q4_code(block, e):
+    """-> 4-bit code of element e of one 144-byte block."""
+    b = np.ascontiguousarray(block, dtype=np.uint8)
+    return int(_load().q4o_code(_ptr(b), int(e)))
+
+
+def q4_decode(raw, m, k):
+    """-> (codes uint8 [m][k], sc uint8 [m][k/32], mn uint8 [m][k/32], d f64 [m][k/256],
+    dmin f64 [m][k/256])."""
+    raw = _raw4(raw, m, k)
+    codes = np.empty((m, k), np.uint8)
+    sc = np.empty((m, k // 32), np.uint8)
+    mn = np.empty((m, k // 32), np.uint8)
+    d = np.empty((m, k // QK), np.float64)
+    dmin = np.empty((m, k // QK), np.float64)
+    _load().q4o_decode(_ptr(raw), m, k, _ptr(codes), _ptr(sc), _ptr(mn), _ptr(d), _ptr(dmin))
+    return codes, sc, mn, d, dmin
+
+
+def q4_dequant(raw, m, k):
+    """-> f64 [m][k] dequantized q4_K weights."""
+    raw = _raw4(raw, m, k)
+    w = np.empty((m, k), np.float64)
+    _load().q4o_dequant(_ptr(raw), m, k, _ptr(w))
+    return w
+
+
+def q4_chunkdots(xq, raw, m):
+    """-> int32 [n][m][k/32] integer dots of the activation codes with the 4-bit weight codes."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    n, k = xq.shape
+    raw = _raw4(raw, m, k)
+    out = np.empty((n, m, k // 32), np.int32)
+    _load().q4o_chunkdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
+    return out
+
+
+def q4_chunksums(xq):
+    """-> int32 [n][k/32] sums of each chunk's activation codes."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    n, k = xq.shape
+    out = np.empty((n, k // 32), np.int32)
+    _load().q4o_chunksums(_ptr(xq), n, k, _ptr(out))
+    return out
+
+
+def q4_gemm(xq, da, raw, m):
+    """-> (y f64 [n][m], t f64 [n][m]) for q4_K weights."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    da = np.ascontiguousarray(da, dtype=np.float32)
+    n, k = xq.shape
+    assert da.shape == (n, k // 32)
+    raw = _raw4(raw, m, k)
+    y = np.empty((n, m), np.float64)
+    t = np.empty((n, m), np.float64)
+    _load().q4o_gemm(_ptr(xq), _ptr(da), n, _ptr(raw), m, k, _ptr(y), _ptr(t))
     return y, t

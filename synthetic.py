@@ -69,6 +69,26 @@ def activations(n, k, seed, kind="normal"):
     raise ValueError(kind)
 
 
+Q4K_BLOCK_BYTES = 144
+
+
+def weights_q4k(m, k, seed):
+    """Raw q4_K blocks uint8 [m][k/256][144]: qs uniform bytes, the 12 scale bytes uniform (every
+    6-bit scale and min uniform in 0..63), then d and dmin = f16(|N(0,1)| * 1e-2), little-endian
+    at bytes 0 and 2."""
+    assert k % QK == 0
+    nsb = k // QK
+    rng = np.random.Generator(np.random.PCG64(seed + 5 * 10**6))
+    raw = np.zeros((m, nsb, Q4K_BLOCK_BYTES), np.uint8)
+    raw[:, :, 16:144] = rng.integers(0, 256, size=(m, nsb, 128), dtype=np.uint8)
+    raw[:, :, 4:16] = rng.integers(0, 256, size=(m, nsb, 12), dtype=np.uint8)
+    d = (np.abs(rng.standard_normal(size=(m, nsb))) * 1e-2).astype(np.float16)
+    dmin = (np.abs(rng.standard_normal(size=(m, nsb))) * 1e-2).astype(np.float16)
+    raw[:, :, 0:2] = d.view(np.uint8).reshape(m, nsb, 2)
+    raw[:, :, 2:4] = dmin.view(np.uint8).reshape(m, nsb, 2)
+    return raw
+
+
 def swiglu_inputs(n, k, seed):
     """(gate, up) f32 [n][k]: the two factors of the post-SwiGLU activations that
     activations(n, k, seed, "swiglu") forms in f64 (up = a, gate = b, same draws)."""
