@@ -6,7 +6,8 @@ One step = one pass of the hot path over one batch: the activation quantize-tran
 before timing starts.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1] [--workload NAME]
-                    [--cold] [--swiglu] [--no-cpu-baseline] [--copy-probe-mib MIB]
+                    [--weights q6k|q4k] [--cold] [--swiglu] [--no-cpu-baseline]
+                    [--copy-probe-mib MIB]
 
 Workloads: tiny, attn_v_n512, attn_v_n3314, ffn_down_n3314 (the default and headline case), and
 sweep32: 32 layers of (attn_v 4096x4096 + ffn_down 4096x11008) at 3314 tokens, 64 GEMMs back to
@@ -14,7 +15,9 @@ back on one stream over 1.6 GB of raw weights, inputs drawn on the device.  --co
 512 MiB scrub buffer before every timed step, so weights and activations come from HBM rather
 than the 256 MB Infinity Cache.  --swiglu (single workloads) replaces the prepass by the fused
 producer q6k_swiglu_quantize_act reading the two SwiGLU factors, and also times the unfused pair
-(q6k_swiglu_f32 writing h, then q6k_quantize_act) once for comparison.
+(q6k_swiglu_f32 writing h, then q6k_quantize_act) once for comparison.  --weights q4k runs the
+q4_K variant on the same shapes (synthetic q4_K weights): step = q6k_quantize_act +
+q4k_act_sums + q4k_gemm.
 """
 import argparse
 import json
@@ -37,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layout", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--workload", default="ffn_down_n3314")
+    ap.add_argument("--weights", default="q6k", choices=["q6k", "q4k"],
+                    help="weight format: q6_K (the headline) or the q4_K variant")
     ap.add_argument("--cold", action="store_true")
     ap.add_argument("--swiglu", action="store_true",
                     help="feed the GEMM from the fused SwiGLU -> int8 producer (gate, up inputs)")
@@ -47,7 +52,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(raw, x, m, k, tokens):
+def cpu_baseline(raw, x, m, k, tokens, weights="q6k"):
     """The oracle as it stands (single-threaded C), on the first `tokens` tokens of the same
     workload, all rows: quantize + reference GEMM."""
     import oracle
@@ -55,7 +60,7 @@ def cpu_baseline(raw, x, m, k, tokens):
     xs = x[:tokens]
     t0 = time.perf_counter()
     xq, da = oracle.quantize(xs)
-    oracle.gemm(xq, da, raw, m)
+    (oracle.q4_gemm if weights == "q4k" else oracle.gemm)(xq, da, raw, m)
     dt = time.perf_counter() - t0
     return {"value": 2.0 * tokens * m * k / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"first {tokens} tokens x all {m} rows x k={k} (quantize + reference GEMM), "
@@ -87,6 +92,33 @@ def counter_traffic(workload, layout):
         return None
     entry = rec.get("layouts", {}).get(str(layout))
     return None if entry is None else int(entry["traffic_bytes"])
+
+
+class Q4Problem:
+    """Device buffers of one q4_K GEMM (same activations path plus the per-chunk sums)."""
+
+    def __init__(self, q6k, torch, x_d, raw_d, n, m, k, dev):
+        self.q6k, self.n, self.m, self.k, self.layout = q6k, n, m, k, "q4k"
+        self.x, self.up = x_d, None
+        xb, db = q6k.q6k_act_bytes(n, k)
+        self.xq = torch.empty(xb, dtype=torch.uint8, device=dev)
+        self.da = torch.empty(db // 4, dtype=torch.float32, device=dev)
+        self.das = torch.empty(db // 4, dtype=torch.float32, device=dev)
+        self.w = torch.empty(q6k.q4k_weight_bytes(m, k), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((n, m), dtype=torch.float32, device=dev)
+        q6k.q4k_expand_weights(raw_d, m, k, self.w)
+
+    def quantize(self):
+        self.q6k.q6k_quantize_act(self.x, self.xq, self.da)
+        self.q6k.q4k_act_sums(self.xq, self.da, self.n, self.k, self.das)
+
+    def gemm(self):
+        self.q6k.q4k_gemm(self.xq, self.da, self.das, self.n, self.w, self.m, self.k, self.y)
+
+    def alg_bytes(self):
+        a_bytes = self.n * self.k + self.n * (self.k // 32) * 8
+        return {"gemm": self.w.numel() + a_bytes + self.n * self.m * 4,
+                "prepass": self.n * self.k * 4 + a_bytes}
 
 
 class Problem:
@@ -160,6 +192,13 @@ def main():
         problems.append(Problem(q6k, torch, torch.from_numpy(gate).to(dev), raw_d, n, m, k,
                                 layout, dev, up_d=torch.from_numpy(up).to(dev)))
         raw = None  # the CPU baseline quantizes x; here the input is the factor pair
+    elif args.weights == "q4k":
+        spec = synthetic.WORKLOADS[args.workload]
+        n, m, k = spec["n"], spec["m"], spec["k"]
+        raw = synthetic.weights_q4k(m, k, spec["seed"])
+        x = synthetic.activations(n, k, spec["seed"], spec["x"])
+        problems.append(Q4Problem(q6k, torch, torch.from_numpy(x).to(dev),
+                                  torch.from_numpy(raw.reshape(-1)).to(dev), n, m, k, dev))
     else:
         raw, x, n, m, k = synthetic.workload(args.workload)
         x_d = torch.from_numpy(x).to(dev)
@@ -174,7 +213,10 @@ def main():
             else synthetic.weights_torch(p0.m, p0.k, 7, dev))
     e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_a.record(stream)
-    q6k.q6k_expand_weights(raw0, p0.m, p0.k, layout, p0.w)
+    if args.weights == "q4k" and not sweep:
+        q6k.q4k_expand_weights(raw0, p0.m, p0.k, p0.w)
+    else:
+        q6k.q6k_expand_weights(raw0, p0.m, p0.k, layout, p0.w)
     e_b.record(stream)
     torch.cuda.synchronize()
     expand_us = e_a.elapsed_time(e_b) * 1e3
@@ -263,6 +305,9 @@ def main():
                   "cold": args.cold, "step": "q6k_quantize_act + q6k_gemm"}
         if args.swiglu:
             config["producer"] = "fused SwiGLU (gate, up f32 inputs)"
+        if args.weights == "q4k":
+            config.update(weights="q4_K", layout="q4k planes",
+                          step="q6k_quantize_act + q4k_act_sums + q4k_gemm")
 
     out = {
         "metric": METRIC,
@@ -298,8 +343,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "traffic": (counter_traffic(args.workload, layout)
-                                 if not (sweep or args.cold) else None),
-                     "kernel": f"gemm_kernel<layout {layout}>",
+                                 if not (sweep or args.cold or args.weights == "q4k") else None),
+                     "kernel": ("q4k_gemm_kernel" if args.weights == "q4k" else
+                                "folded_kernel (layout 2)" if layout == 2 else
+                                f"gemm_kernel<layout {layout}>"),
                      "algorithmic_per_launch": {"int8_ops": 2.0 * p0.n * p0.m * p0.k,
                                                 "bytes": p0.alg_bytes()["gemm"]}},
     }
@@ -327,7 +374,8 @@ def main():
                            "unfused_total_us": round(t_sw + t_q, 2)}
         out["config"]["step"] = "q6k_swiglu_quantize_act + q6k_gemm"
     if not args.no_cpu_baseline and raw is not None:
-        out["cpu_baseline"] = cpu_baseline(raw, x, p0.m, p0.k, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(raw, x, p0.m, p0.k, args.cpu_sample_tokens,
+                                           args.weights)
     print(json.dumps(out), flush=True)
 
 

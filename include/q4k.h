@@ -1,0 +1,74 @@
+/*
+ * q4k.h -- C ABI of the q4_K variant in libq6k.so: the q4_K x int8 prefill GEMM on MI355X
+ *
+ *     Y[N x M] = X[N x K] . dequant(W_q4K[M x K])^T
+ *
+ * Pages (titles of the optimisation log this follows):
+ *   "r18: Load-time B pre-expansion — staging becomes a bulk copy (W_exp's debut, REVERTED)"
+ *       sec. 1    a q4_K super-block: 256 weights in 144 bytes, a 16-byte header (f16 d at 0,
+ *                 f16 dmin at 2, twelve bytes of 6-bit scale/min pairs at 4) and 128 bytes of
+ *                 4-bit codes; eight sub-blocks of 32
+ *       sec. 2    the load-time EB plane (codes as one byte each, 0..15) and SB plane (the pair
+ *                 d*sc, -dmin*m per 32-element chunk and row)
+ *   "r38 — q6_K BT-style raw-byte mma kernel (LANDED)", sec. 2.2: q4_K's rescale has two terms
+ *       and needs the activations' per-chunk sum next to their scale
+ * The bit packing the pages do not print is the GGUF K-quant one: for sub-block j < 4,
+ * sc = s[j] & 63, m = s[j+4] & 63; for j >= 4, sc = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+ * m = (s[j+4] >> 4) | (s[j] >> 6) << 4 (s = the 12 scale bytes); code byte 16 + 32g + l holds
+ * element 64g + l in its low nibble and 64g + 32 + l in its high nibble; w = d*sc*q - dmin*m.
+ *
+ * Conventions, status codes and the tiled activation layout (xq, da) are those of q6k.h: the
+ * activations are quantized by q6k_quantize_act (or q6k_swiglu_quantize_act), then
+ * q4k_act_sums adds das = da * S per (token, chunk), S the sum of the chunk's 32 codes, in the
+ * tiled order of da.  Every pointer is a device pointer owned by the caller; calls are
+ * asynchronous on `stream`; arguments are checked on the host and nothing is launched on error.
+ *
+ * Prepared weights (q4k_expand_weights), rows padded to MP = m rounded up to 128:
+ *   codes : byte ((R*nchunk + c)*64 + l)*16 + b holds the code (0..15) of row 32R + p at
+ *           k = 32c + 16*(b/8) + 8g + b%8 (l = p + 32g: the lane order of xq)
+ *   pairs : at byte offset MP*k, float2 ((R*(k/256) + s)*8 + cc)*32 + p = (d*sc, -dmin*m) of row
+ *           32R + p, chunk 8s + cc
+ * 1.25 bytes per weight; padding rows hold zeros.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "q6k.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Size in bytes of the prepared weights of an m x k q4_K matrix; 0 if invalid. */
+size_t q4k_weight_bytes(int64_t m, int64_t k);
+
+/* Load-time preparation.  Input: raw q4_K blocks, row j's super-block b at byte (j*(k/256)+b)*144,
+ * 16-byte aligned.  Output: the codes and pairs above, w_out_bytes >= q4k_weight_bytes(m, k). */
+q6k_status q4k_expand_weights(const void* w_raw, int64_t m, int64_t k, void* w_out,
+                              size_t w_out_bytes, void* stream);
+
+/* das = da * S for the tiled activations of q6k_quantize_act (same n, k); das has the size and
+ * order of da (q6k_act_bytes). */
+q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, float* das,
+                        size_t das_bytes, void* stream);
+
+/* The GEMM: y[t][j] = sum over chunks c of da*(d*sc)*D - (dmin*m)*das, D the exact int32 dot of
+ * the int8 activations with the 4-bit codes over the chunk.  y f32 [n][ldy], ldy >= m, 4-byte
+ * aligned; xq, da, das, w 16-byte aligned and of the sizes above; k <= 2^25. */
+q6k_status q4k_gemm(const void* xq, const float* da, const float* das, int64_t n, const void* w,
+                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
+
+/* Test-only export of the same kernel source: the int32 chunk dots D to dots [n][m][k/32]. */
+q6k_status q4k_gemm_dots(const void* xq, int64_t n, const void* w, int64_t m, int64_t k,
+                         int32_t* dots, void* stream);
+
+/* Liveness counter: q4k_gemm and q4k_gemm_dots launches since load. */
+uint64_t q4k_launches(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4K_H */

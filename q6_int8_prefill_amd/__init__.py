@@ -1,11 +1,17 @@
 """q6_K x int8 prefill GEMM for MI355X (gfx950).
 
-A thin ctypes binding of ``libq6k.so`` (C ABI in ``include/q6k.h``): every function here only
+A thin ctypes binding of ``libq6k.so`` (C ABI in ``include/q6k.h`` and ``include/q4k.h``): every function here only
 checks Python-side types, passes device pointers, sizes and the current HIP stream, and raises on
 a non-zero status.  All arithmetic runs in the HIP kernels.  PyTorch is used for device memory
 and streams only.  If the built library is missing, importing the binding raises.
 """
 from ._lib import (  # noqa: F401
+    q4k_act_sums,
+    q4k_expand_weights,
+    q4k_gemm,
+    q4k_gemm_dots,
+    q4k_launches,
+    q4k_weight_bytes,
     LAYOUT_EXPANDED,
     LAYOUT_FOLDED,
     LAYOUT_PACKED,

@@ -34,6 +34,18 @@ _lib.q6k_gemm_subdots.restype = _int
 _lib.q6k_gemm_subdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
 _lib.q6k_gemm_chunkdots.restype = _int
 _lib.q6k_gemm_chunkdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
+_lib.q4k_weight_bytes.restype = _sz
+_lib.q4k_weight_bytes.argtypes = [_i64, _i64]
+_lib.q4k_expand_weights.restype = _int
+_lib.q4k_expand_weights.argtypes = [_p, _i64, _i64, _p, _sz, _p]
+_lib.q4k_act_sums.restype = _int
+_lib.q4k_act_sums.argtypes = [_p, _p, _i64, _i64, _p, _sz, _p]
+_lib.q4k_gemm.restype = _int
+_lib.q4k_gemm.argtypes = [_p, _p, _p, _i64, _p, _i64, _i64, _p, _i64, _p]
+_lib.q4k_gemm_dots.restype = _int
+_lib.q4k_gemm_dots.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p]
+_lib.q4k_launches.restype = ctypes.c_uint64
+_lib.q4k_launches.argtypes = []
 _lib.q6k_strerror.restype = ctypes.c_char_p
 _lib.q6k_strerror.argtypes = [_int]
 _lib.q6k_stats.restype = None
@@ -41,7 +53,9 @@ _lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
 
 EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_swiglu_quantize_act", "q6k_swiglu_f32",
            "q6k_weight_bytes", "q6k_expand_weights",
-           "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots", "q6k_strerror", "q6k_stats")
+           "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots", "q6k_strerror", "q6k_stats",
+           "q4k_weight_bytes", "q4k_expand_weights", "q4k_act_sums", "q4k_gemm", "q4k_gemm_dots",
+           "q4k_launches")
 
 
 class Q6KError(RuntimeError):
@@ -206,3 +220,68 @@ def q6k_stats():
     out = (ctypes.c_uint64 * 3)()
     _lib.q6k_stats(out)
     return tuple(int(v) for v in out)
+
+
+# ------------------------------------------------------------------------------------------------
+# q4_K variant (include/q4k.h)
+# ------------------------------------------------------------------------------------------------
+def q4k_weight_bytes(m, k):
+    return int(_lib.q4k_weight_bytes(int(m), int(k)))
+
+
+def q4k_expand_weights(w_raw, m, k, w_out, stream=None):
+    """raw q4_K bytes (device uint8, m*(k/256)*144 B) -> prepared codes + (d*sc, -dmin*m) pairs."""
+    if w_raw is not None and w_raw.numel() and _nbytes(w_raw) < m * (k // 256) * 144:
+        raise ValueError("raw weight buffer too small")
+    _check(_lib.q4k_expand_weights(_ptr(w_raw), m, k, _ptr(w_out), _nbytes(w_out),
+                                   _stream(stream)), "q4k_expand_weights")
+
+
+def q4k_act_sums(xq, da, n, k, das, stream=None):
+    """das = da * (sum of each chunk's codes), tiled like da."""
+    xb, db = q6k_act_bytes(n, k)
+    if n > 0 and xb and (_nbytes(xq) < xb or _nbytes(da) < db):
+        raise ValueError("activation buffers too small")
+    _check(_lib.q4k_act_sums(_ptr(xq), _ptr(da), n, k, _ptr(das), _nbytes(das), _stream(stream)),
+           "q4k_act_sums")
+
+
+def _check_q4_operands(xq, da, das, n, w, m, k):
+    if n <= 0 or m <= 0:
+        return
+    xb, db = q6k_act_bytes(n, k)
+    wb = q4k_weight_bytes(m, k)
+    if xb == 0 or wb == 0:
+        return
+    if _nbytes(xq) < xb or (da is not None and _nbytes(da) < db) or (das is not None and _nbytes(das) < db):
+        raise ValueError("activation buffers too small")
+    if _nbytes(w) < wb:
+        raise ValueError(f"weight buffer too small: need {wb} bytes")
+
+
+def q4k_gemm(xq, da, das, n, w, m, k, y, ldy=None, stream=None):
+    """y f32 [n][ldy] = q4_K GEMM of prepared activations (xq, da, das) and weights."""
+    if y is not None and y.dtype != torch.float32:
+        raise TypeError("y must be float32")
+    if ldy is None:
+        ldy = y.stride(0) if y is not None and y.dim() == 2 else m
+    _check_q4_operands(xq, da, das, n, w, m, k)
+    if y is not None and n > 0 and m > 0 and y.numel() < (n - 1) * ldy + m:
+        raise ValueError("y too small for n x ldy")
+    _check(_lib.q4k_gemm(_ptr(xq), _ptr(da), _ptr(das), n, _ptr(w), m, k, _ptr(y), ldy,
+                         _stream(stream)), "q4k_gemm")
+
+
+def q4k_gemm_dots(xq, n, w, m, k, dots, stream=None):
+    """Test-only: int32 chunk dots [n][m][k/32] from the q4_K GEMM kernel source."""
+    if dots is not None and dots.dtype != torch.int32:
+        raise TypeError("dots must be int32")
+    _check_q4_operands(xq, None, None, n, w, m, k)
+    if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 32):
+        raise ValueError("dots too small for n x m x k/32")
+    _check(_lib.q4k_gemm_dots(_ptr(xq), n, _ptr(w), m, k, _ptr(dots), _stream(stream)),
+           "q4k_gemm_dots")
+
+
+def q4k_launches():
+    return int(_lib.q4k_launches())

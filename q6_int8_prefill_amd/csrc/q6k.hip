@@ -22,6 +22,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "q4k.h"
 #include "q6k.h"
 
 namespace {
@@ -35,6 +36,7 @@ constexpr int kBiasI = 0x4B400000;      // bit pattern of 1.5 * 2^23
 constexpr float kBiasF = 12582912.0f;   // 1.5 * 2^23
 
 std::atomic<uint64_t> g_launches[3];
+std::atomic<uint64_t> g_q4k_launches;
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -893,6 +895,331 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   }
 }
 
+// =============================================================================================
+// q4_K variant ("r18: Load-time B pre-expansion — staging becomes a bulk copy (W_exp's debut,
+// REVERTED)"): 144-byte super-blocks of 256 weights, f16 d and dmin, eight 6-bit (sc, m) pairs,
+// 4-bit codes; w = d*sc*q - dmin*m per 32-element chunk.  A chunk contributes
+//     da * (d*sc) * D - da * (dmin*m) * S,   D = sum xq*q (exact int),   S = sum xq
+// so the activations carry da and da*S (the pages' per-token d|ssum pair, "r38 — q6_K BT-style
+// raw-byte mma kernel (LANDED)", sec. 2.2), and the weights are prepared at load time as the
+// pages' EB plane (codes as int8 0..15, here in MFMA lane order) and SB plane ((d*sc, -dmin*m)
+// f32 pairs per row and chunk).
+// =============================================================================================
+constexpr int kQ4Block = 144;
+
+// Prepass with sums: the q6_K prepass plus das = da * S per (token, chunk), S the sum of the
+// chunk's 32 codes (exact in int), rounded once to f32; stored in the tiled order of da.
+__global__ __launch_bounds__(256) void q4k_act_sums_kernel(const uint8_t* __restrict__ xq,
+                                                           const float* __restrict__ da,
+                                                           int64_t ntile, int64_t nchunk,
+                                                           float* __restrict__ das) {
+  // one thread per (token tile, chunk, token): sums the token's two 16-byte lane slots
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= ntile * nchunk * 32) return;
+  const int64_t tc = i / 32;
+  const int p = (int)(i % 32);
+  const uint8_t* blk = xq + tc * 64 * kFragBytes;
+  int sum = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 v = reinterpret_cast<const uint4*>(blk)[p + 32 * h];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum += (int8_t)((w[b] >> (8 * e)) & 255);
+  }
+  const int slot = 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3);
+  das[tc * 32 + slot] = da[tc * 32 + slot] * (float)sum;
+}
+
+// Load-time planes.  Block = one row tile (32 rows) x one super-block; the 32 raw blocks are
+// staged in LDS (16-byte rows), then thread (p, cc) decodes chunk cc (sub-block cc) of row 32R+p:
+// its 32 codes into lane slots p and p+32 of the (R, c) 1 KiB block (the activation lane order),
+// and (d*sc, -dmin*m) into the SB plane at [R][super-block][cc][p].
+// Codes: byte 16 + 32g + l of a block holds element 64g + l (low nibble) and 64g + 32 + l (high
+// nibble); for sub-block j < 4, sc = s[j] & 63, m = s[j+4] & 63, for j >= 4,
+// sc = (s[j+4] & 15) | (s[j-4] >> 6) << 4, m = (s[j+4] >> 4) | (s[j] >> 6) << 4, s the 12 bytes
+// at offset 4 (the GGUF K-quant packing the pages follow).
+__global__ __launch_bounds__(256) void q4k_expand_kernel(const uint8_t* __restrict__ raw,
+                                                         int64_t m, int64_t nsb,
+                                                         uint8_t* __restrict__ codes,
+                                                         float* __restrict__ sbp) {
+  __shared__ __attribute__((aligned(16))) uint8_t blk[kTile * kQ4Block];
+  const int64_t R = blockIdx.x, sb = blockIdx.y, nchunk = nsb * 8;
+  for (int idx = threadIdx.x; idx < kTile * kQ4Block / 16; idx += 256) {
+    const int j = idx / (kQ4Block / 16), w = idx % (kQ4Block / 16);
+    const int64_t row = R * kTile + j;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < m) v = reinterpret_cast<const uint4*>(raw + (row * nsb + sb) * kQ4Block)[w];
+    reinterpret_cast<uint4*>(blk + j * kQ4Block)[w] = v;
+  }
+  __syncthreads();
+  const int p = threadIdx.x & 31, cc = threadIdx.x >> 5;
+  const uint8_t* b = blk + p * kQ4Block;
+  const int g = cc >> 1, hi = cc & 1;
+  int q[32];
+#pragma unroll
+  for (int l = 0; l < 32; ++l) {
+    const int byte = b[16 + 32 * g + l];
+    q[l] = hi ? (byte >> 4) : (byte & 15);
+  }
+  const uint8_t* s = b + 4;
+  int sc, mn;
+  if (cc < 4) {
+    sc = s[cc] & 63;
+    mn = s[cc + 4] & 63;
+  } else {
+    sc = (s[cc + 4] & 15) | ((s[cc - 4] >> 6) << 4);
+    mn = (s[cc + 4] >> 4) | ((s[cc] >> 6) << 4);
+  }
+  const float d = __half2float(__ushort_as_half((unsigned short)(b[0] | (b[1] << 8))));
+  const float dmin = __half2float(__ushort_as_half((unsigned short)(b[2] | (b[3] << 8))));
+  const int64_t c = sb * 8 + cc;
+  uint4 s0, s1;  // lane p: k 0..7 and 16..23; lane p + 32: k 8..15 and 24..31
+  s0.x = pack4(q[0], q[1], q[2], q[3]);
+  s0.y = pack4(q[4], q[5], q[6], q[7]);
+  s0.z = pack4(q[16], q[17], q[18], q[19]);
+  s0.w = pack4(q[20], q[21], q[22], q[23]);
+  s1.x = pack4(q[8], q[9], q[10], q[11]);
+  s1.y = pack4(q[12], q[13], q[14], q[15]);
+  s1.z = pack4(q[24], q[25], q[26], q[27]);
+  s1.w = pack4(q[28], q[29], q[30], q[31]);
+  uint4* dst = reinterpret_cast<uint4*>(codes + (R * nchunk + c) * 64 * kFragBytes);
+  dst[p] = s0;
+  dst[p + 32] = s1;
+  float2 pr;
+  pr.x = d * (float)sc;  // exact: an 11-bit significand times a 6-bit integer
+  pr.y = -(dmin * (float)mn);
+  if (R * kTile + p >= m) pr.x = pr.y = 0.0f;  // padding rows (their codes are zero too)
+  reinterpret_cast<float2*>(sbp)[((R * nsb + sb) * 8 + cc) * 32 + p] = pr;
+}
+
+// GEMM.  Workgroup = 4 waves = 64 tokens (token tiles 2*bx, 2*bx+1) x 128 weight rows (row tiles
+// 4*by .. 4*by+3); wave w computes token tile w%2 against row tiles 2*(w/2) and 2*(w/2)+1 (rows
+// of the MFMA = tokens, columns = weight rows, so each lane owns one weight row and 16 tokens).
+// Per chunk and tile one v_mfma_i32_32x32x32_i8 (the whole 32-element sub-block has one scale),
+// started from the bit pattern of 1.5*2^23 (|D| <= 32*127*15 < 2^22), then
+//     t   = fma(F, d*sc, -1.5*2^23*d*sc)     (= D*d*sc rounded once)
+//     acc = fma(t, da, acc)
+//     acc = fma(-dmin*m, da*S, acc)
+// three VALU per output.  Staging: a 4-slot ring of direct-to-LDS buffer loads (activation tiles
+// by waves 0 and 1, each wave its row tile's codes), and, once per super-block into a buffer of
+// that super-block's parity, da and da*S of the token tiles and the SB pairs of the row tiles.
+constexpr int kQ4SlotA = 0;       // 2 token tiles x 1 KiB
+constexpr int kQ4SlotB = 2048;    // 4 row tiles x 1 KiB
+constexpr int kQ4Slot = 6144;
+constexpr int kQ4Ring = 4;
+constexpr int kQ4SbDa = 0;        // per parity: 2 token tiles x 1 KiB of da
+constexpr int kQ4SbDas = 2048;    //             2 token tiles x 1 KiB of da*S
+constexpr int kQ4SbSb = 4096;     //             4 row tiles x 2 KiB of (d*sc, -dmin*m)
+constexpr int kQ4SbBytes = 12288;
+#ifndef Q4K_WG_PER_CU
+#define Q4K_WG_PER_CU 3
+#endif
+static_assert(Q4K_WG_PER_CU * (kQ4Ring * kQ4Slot + 2 * kQ4SbBytes) <= 160 * 1024, "LDS budget");
+
+struct Q4Src {
+  __amdgpu_buffer_rsrc_t a, da, das, b, sb;
+};
+
+// Loads of chunk ci (ci % 8 == CI8) into `slot`; chunks past the end repeat the last one so each
+// wave issues at least 1 load per chunk (2 for waves 0 and 1).  At a super-block's first chunk the
+// per-super-block planes follow (extra loads, only for real chunks): they go to the buffers of the
+// super-block's parity, last read for super-block s - 2 (before the barrier of iteration 8s - 8);
+// they are issued at iteration 8s - 3.
+template <int CI8>
+__device__ __forceinline__ void q4_issue(uint8_t* slot, uint8_t* sbuf, const Q4Src& src,
+                                         int64_t ci, int64_t nchunk, int wave, int lane) {
+  const bool live = ci < nchunk;
+  const uint32_t cl = (uint32_t)(live ? ci : nchunk - 1);
+  const uint32_t l16 = lane * 16;
+  bdma16(src.b, l16, cl * 1024, slot + kQ4SlotB + wave * 1024);
+  if (wave < kWgTokTiles) bdma16(src.a, l16, cl * 1024, slot + kQ4SlotA + wave * 1024);
+  if (CI8 == 0 && live) {
+    uint8_t* par = sbuf + ((ci >> 3) & 1) * kQ4SbBytes;
+    const uint32_t s = (uint32_t)(ci >> 3);
+    bdma16(src.sb, l16, s * 2048, par + kQ4SbSb + wave * 2048);
+    bdma16(src.sb, l16 + 1024, s * 2048, par + kQ4SbSb + wave * 2048 + 1024);
+    if (wave < kWgTokTiles) {
+      bdma16(src.da, l16, s * 1024, par + kQ4SbDa + wave * 1024);
+      bdma16(src.das, l16, s * 1024, par + kQ4SbDas + wave * 1024);
+    }
+  }
+}
+
+template <int CHUNKS>
+__device__ __forceinline__ void q4_wait(bool loads_a) {
+  if (loads_a)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 2) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 1) : "memory");
+}
+
+struct Q4Ctx {
+  uint8_t* smem;
+  uint8_t* sbuf;
+  Q4Src src;
+  int64_t nchunk, n, m, tok_base, col;
+  int32_t* dots;
+  uint32_t aa, bb, dd, ss;  // per-lane LDS addresses: A in slot 0, B in slot 0, da and SB (parity 0)
+  int wave, lane;
+  bool loads_a;
+};
+
+// An empty volatile statement that "modifies" a tile's accumulators: the instruction selector
+// cannot move the next step's loads and MFMAs above the rescale that produced them.
+__device__ __forceinline__ void q4_order(float (&v)[16]) {
+  asm volatile(""
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
+template <bool DOTS, int CC>
+__device__ __forceinline__ void q4_step(const Q4Ctx& k, int64_t s, uint32_t par, const v16i& bias,
+                                        float (&acc)[2][16]) {
+  const int64_t c = 8 * s + CC;
+  q4_wait<kQ4Ring - 3>(k.loads_a);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  q4_issue<(CC + kQ4Ring - 1) % 8>(k.smem + ((CC + kQ4Ring - 1) % kQ4Ring) * kQ4Slot, k.sbuf,
+                                   k.src, c + kQ4Ring - 1, k.nchunk, k.wave, k.lane);
+  constexpr int kS = (CC % kQ4Ring) * kQ4Slot;
+  v4i a, b0, b1;
+  v4f d0, d1, d2, d3, s0, s1, s2, s3;
+  v2f p0, p1;
+  const uint32_t ddp = k.dd + par, ssp = k.ss + par;
+  asm volatile(
+      "ds_read_b128 %0, %13 offset:%17\n\t"
+      "ds_read_b128 %1, %14 offset:%18\n\t"
+      "ds_read_b128 %2, %14 offset:%19\n\t"
+      "ds_read_b64 %3, %16 offset:%20\n\t"
+      "ds_read_b64 %4, %16 offset:%21\n\t"
+      "ds_read_b128 %5, %15 offset:%22\n\t"
+      "ds_read_b128 %6, %15 offset:%23\n\t"
+      "ds_read_b128 %7, %15 offset:%24\n\t"
+      "ds_read_b128 %8, %15 offset:%25\n\t"
+      "ds_read_b128 %9, %15 offset:%26\n\t"
+      "ds_read_b128 %10, %15 offset:%27\n\t"
+      "ds_read_b128 %11, %15 offset:%28\n\t"
+      "ds_read_b128 %12, %15 offset:%29\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b0), "=&v"(b1), "=&v"(p0), "=&v"(p1), "=&v"(d0), "=&v"(d1), "=&v"(d2),
+        "=&v"(d3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
+      : "v"(k.aa), "v"(k.bb), "v"(ddp), "v"(ssp), "n"(kS + kQ4SlotA), "n"(kS + kQ4SlotB),
+        "n"(kS + kQ4SlotB + 1024), "n"(CC * 256), "n"(CC * 256 + 2048), "n"(CC * 128),
+        "n"(CC * 128 + 16), "n"(CC * 128 + 32), "n"(CC * 128 + 48),
+        "n"(kQ4SbDas + CC * 128), "n"(kQ4SbDas + CC * 128 + 16),
+        "n"(kQ4SbDas + CC * 128 + 32), "n"(kQ4SbDas + CC * 128 + 48)
+      : "memory");
+  const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
+                         d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
+  const float dsv[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                         s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+  const v16i f0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, bias, 0, 0, 0);
+  const v16i f1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, bias, 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const v16i& f = u ? f1 : f0;
+    const v2f pr = u ? p1 : p0;
+    if (DOTS) {
+      const int g = k.lane >> 5;
+      const int64_t col = k.col + u * kTile;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t tok = k.tok_base + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (tok < k.n && col < k.m) k.dots[(tok * k.m + col) * k.nchunk + c] = f[r] - kBiasI;
+      }
+    } else {
+      const float nb = -kBiasF * pr.x;
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(f[r]), pr.x, nb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(t[r], dav[r], acc[u][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(pr.y, dsv[r], acc[u][r]);
+    }
+    q4_order(acc[u]);  // keep the steps in program order (bounded register lifetimes)
+  }
+}
+
+template <bool DOTS>
+__global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ da, const float* __restrict__ das,
+    const uint8_t* __restrict__ wcodes, const float* __restrict__ wsb, int64_t n, int64_t m,
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, int32_t* __restrict__ dots) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kQ4Ring * kQ4Slot + 2 * kQ4SbBytes];
+  Q4Ctx k;
+  k.smem = smem;
+  k.sbuf = smem + kQ4Ring * kQ4Slot;
+  k.lane = threadIdx.x & 63;
+  k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  k.loads_a = k.wave < kWgTokTiles;
+  const int tt = k.wave & 1, rp = k.wave >> 1;
+  const int64_t T = (int64_t)blockIdx.x * kWgTokTiles + tt;
+  const int64_t R0 = (int64_t)blockIdx.y * 4;
+  const int64_t Ta = (int64_t)blockIdx.x * kWgTokTiles + (k.loads_a ? k.wave : 0);
+  const int64_t nsb = nchunk / 8;
+  k.src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
+  k.src.da = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
+  k.src.das = make_rsrc(reinterpret_cast<const uint8_t*>(das) + Ta * nchunk * 128, nchunk * 128);
+  k.src.b = make_rsrc(wcodes + (R0 + k.wave) * nchunk * 1024, nchunk * 1024);
+  k.src.sb = make_rsrc(reinterpret_cast<const uint8_t*>(wsb) + (R0 + k.wave) * nsb * 2048,
+                       nsb * 2048);
+  k.nchunk = nchunk;
+  k.n = n;
+  k.m = m;
+  k.dots = dots;
+  const int p = k.lane & 31, g = k.lane >> 5;
+  k.tok_base = T * kTile;
+  k.col = (R0 + 2 * rp) * kTile + p;
+  k.aa = lds_addr(smem) + tt * 1024 + k.lane * 16;
+  k.bb = lds_addr(smem) + 2 * rp * 1024 + k.lane * 16;
+  k.dd = lds_addr(k.sbuf) + kQ4SbDa + tt * 1024 + g * 64;
+  k.ss = lds_addr(k.sbuf) + kQ4SbSb + 2 * rp * 2048 + p * 8;
+
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
+  float acc[2][16];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
+
+  q4_issue<0>(smem + 0 * kQ4Slot, k.sbuf, k.src, 0, nchunk, k.wave, k.lane);
+  q4_issue<1>(smem + 1 * kQ4Slot, k.sbuf, k.src, 1, nchunk, k.wave, k.lane);
+  q4_issue<2>(smem + 2 * kQ4Slot, k.sbuf, k.src, 2, nchunk, k.wave, k.lane);
+  q4_wait<kQ4Ring - 2>(k.loads_a);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  for (int64_t s = 0; s < nsb; ++s) {
+    const uint32_t par = (uint32_t)(s & 1) * kQ4SbBytes;
+    q4_step<DOTS, 0>(k, s, par, bias, acc);
+    q4_step<DOTS, 1>(k, s, par, bias, acc);
+    q4_step<DOTS, 2>(k, s, par, bias, acc);
+    q4_step<DOTS, 3>(k, s, par, bias, acc);
+    q4_step<DOTS, 4>(k, s, par, bias, acc);
+    q4_step<DOTS, 5>(k, s, par, bias, acc);
+    q4_step<DOTS, 6>(k, s, par, bias, acc);
+    q4_step<DOTS, 7>(k, s, par, bias, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
+
+  if (DOTS) return;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t mcol = k.col + u * kTile;
+    if (mcol >= m) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (tok < n) y[tok * ldy + mcol] = acc[u][r];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Host-side helpers
 // ---------------------------------------------------------------------------------------------
@@ -1010,9 +1337,105 @@ q6k_status quantize_common(const float* x, const float* up, int64_t n, int64_t k
   return launch_status();
 }
 
+template <bool DOTS>
+q6k_status q4k_gemm_common(const void* xq, const float* da, const float* das, int64_t n,
+                           const void* w, int64_t m, int64_t k, float* y, int64_t ldy,
+                           int32_t* dots, void* stream) {
+  if (n < 0 || m < 0) return Q6K_EINVAL;
+  if (k <= 0 || k % 256) return Q6K_ESHAPE;
+  if (n > kMaxDim || m > kMaxDim || k > kMaxDim) return Q6K_ESIZE;
+  if (k / 32 * 1024 > INT32_MAX) return Q6K_ESIZE;  // one 32-bit buffer range per tile
+  if (n == 0 || m == 0) return Q6K_OK;
+  if (!xq || !w || (!DOTS && (!da || !das))) return Q6K_EINVAL;
+  if (!aligned16(xq) || !aligned16(w) || (!DOTS && (!aligned16(da) || !aligned16(das))))
+    return Q6K_EALIGN;
+  if (DOTS) {
+    if (!dots) return Q6K_EINVAL;
+    if (((uintptr_t)dots & 3) != 0) return Q6K_EALIGN;
+  } else {
+    if (!y) return Q6K_EINVAL;
+    if (ldy < m) return Q6K_EINVAL;
+    if (((uintptr_t)y & 3) != 0) return Q6K_EALIGN;
+  }
+  const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
+  const int64_t gx = np / (kTile * 2), gy = mp / kWgRow;
+  if (gy > 65535 || gx > INT32_MAX) return Q6K_ESIZE;
+  const int64_t nchunk = k / 32;
+  const uint8_t* wc = static_cast<const uint8_t*>(w);
+  const float* ws = reinterpret_cast<const float*>(wc + (size_t)mp * (size_t)k);
+  // the test export reads no scales: point them at the codes, which are never dereferenced as such
+  const float* dap = DOTS ? reinterpret_cast<const float*>(xq) : da;
+  const float* dasp = DOTS ? reinterpret_cast<const float*>(xq) : das;
+  hipLaunchKernelGGL((q4k_gemm_kernel<DOTS>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(xq), dap, dasp,
+                     wc, ws, n, m, nchunk, y, ldy, dots);
+  const q6k_status st = launch_status();
+  if (st == Q6K_OK) g_q4k_launches.fetch_add(1, std::memory_order_relaxed);
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t q4k_weight_bytes(int64_t m, int64_t k) {
+  if (m < 0 || k <= 0 || k % 256 || m > kMaxDim || k > kMaxDim) return 0;
+  const int64_t mp = round_up(m, kWgRow);
+  if (mp != 0 && k > (int64_t)(SIZE_MAX / 16) / mp) return 0;
+  return (size_t)mp * (size_t)k + (size_t)mp * (size_t)(k / 32) * 8;
+}
+
+q6k_status q4k_expand_weights(const void* w_raw, int64_t m, int64_t k, void* w_out,
+                              size_t w_out_bytes, void* stream) {
+  if (m < 0) return Q6K_EINVAL;
+  if (k <= 0 || k % 256) return Q6K_ESHAPE;
+  const size_t need = q4k_weight_bytes(m, k);
+  if (need == 0 && m > 0) return Q6K_ESIZE;
+  if (m == 0) return Q6K_OK;
+  if (!w_raw || !w_out) return Q6K_EINVAL;
+  if (!aligned16(w_raw) || !aligned16(w_out)) return Q6K_EALIGN;
+  if (w_out_bytes < need) return Q6K_ESIZE;
+  const int64_t mp = round_up(m, kWgRow);
+  const int64_t nsb = k / 256;
+  if (mp / kTile > INT32_MAX || nsb > 65535) return Q6K_ESIZE;
+  uint8_t* codes = static_cast<uint8_t*>(w_out);
+  hipLaunchKernelGGL(q4k_expand_kernel, dim3((unsigned)(mp / kTile), (unsigned)nsb), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(w_raw), m, nsb,
+                     codes, reinterpret_cast<float*>(codes + (size_t)mp * (size_t)k));
+  return launch_status();
+}
+
+q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, float* das,
+                        size_t das_bytes, void* stream) {
+  if (n < 0) return Q6K_EINVAL;
+  if (k <= 0 || k % 256) return Q6K_ESHAPE;
+  size_t need_x, need_d;
+  if (!act_sizes(n, k, &need_x, &need_d)) return Q6K_ESIZE;
+  if (n == 0) return Q6K_OK;
+  if (!xq || !da || !das) return Q6K_EINVAL;
+  if (!aligned16(xq) || !aligned16(da) || !aligned16(das)) return Q6K_EALIGN;
+  if (das_bytes < need_d) return Q6K_ESIZE;
+  const int64_t ntile = round_up(n, kWgTok) / kTile, nchunk = k / 32;
+  const int64_t blocks = (ntile * nchunk * 32 + 255) / 256;
+  if (blocks > INT32_MAX) return Q6K_ESIZE;
+  hipLaunchKernelGGL(q4k_act_sums_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(xq), da, ntile,
+                     nchunk, das);
+  return launch_status();
+}
+
+q6k_status q4k_gemm(const void* xq, const float* da, const float* das, int64_t n, const void* w,
+                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream) {
+  return q4k_gemm_common<false>(xq, da, das, n, w, m, k, y, ldy, nullptr, stream);
+}
+
+q6k_status q4k_gemm_dots(const void* xq, int64_t n, const void* w, int64_t m, int64_t k,
+                         int32_t* dots, void* stream) {
+  return q4k_gemm_common<true>(xq, nullptr, nullptr, n, w, m, k, nullptr, 0, dots, stream);
+}
+
+uint64_t q4k_launches(void) { return g_q4k_launches.load(std::memory_order_relaxed); }
+
 
 size_t q6k_act_bytes(int64_t n, int64_t k, size_t* da_bytes) {
   size_t xb = 0, db = 0;

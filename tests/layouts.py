@@ -73,3 +73,16 @@ def untile_folded(buf, m, k):
     nsb = k // 256
     d = b[mp * k * 2: mp * k * 2 + mp * nsb * 4].view(np.float32).reshape(mp // 32, nsb, 32)
     return planes[0], planes[1], d.transpose(0, 2, 1).reshape(mp, nsb)
+
+
+def untile_q4k(buf, m, k):
+    """q4_K prepared weights -> (codes uint8 [MP][k], pairs f32 [MP][k/32][2] = (d*sc, -dmin*m))."""
+    mp = round_up(m, 128)
+    nchunk = k // 32
+    b = np.asarray(buf, np.uint8)
+    codes = b[: mp * k].reshape(mp // 32, nchunk, 2, 32, 2, 8)
+    codes = codes.transpose(0, 3, 1, 4, 2, 5).reshape(mp, k)
+    nsb = k // 256
+    pr = b[mp * k: mp * k + mp * nchunk * 8].view(np.float32).reshape(mp // 32, nsb, 8, 32, 2)
+    pairs = pr.transpose(0, 3, 1, 2, 4).reshape(mp, nchunk, 2)
+    return codes, pairs

@@ -15,14 +15,19 @@ def lib():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "q6k.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(q6k_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in ("q6k.h", "q4k.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(q[46]k_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 17, names
+    from q6_int8_prefill_amd import _lib as binding
+    assert sorted(binding.EXPORTS) == names
     L = lib()
     for name in names:
         assert hasattr(L, name), name
@@ -129,3 +134,22 @@ def test_swiglu_errors():
     assert L.q6k_swiglu_f32(FAKE, FAKE, 4, 256, 255, FAKE, 256, None) == -1
     assert L.q6k_swiglu_f32(FAKE, FAKE, 4, 256, 256, FAKE + 2, 256, None) == -3
     assert L.q6k_swiglu_f32(FAKE, FAKE, 0, 256, 256, None, 256, None) == 0
+
+
+def test_q4k_sizes_and_errors():
+    import q6_int8_prefill_amd as q6k
+    L = lib()
+    assert q6k.q4k_weight_bytes(40, 512) == 128 * 512 + 128 * 16 * 8
+    assert q6k.q4k_weight_bytes(40, 300) == 0
+    assert L.q4k_expand_weights(FAKE, 4, 300, FAKE, 1 << 30, None) == -2
+    assert L.q4k_expand_weights(FAKE + 8, 4, 256, FAKE, 1 << 30, None) == -3
+    assert L.q4k_expand_weights(FAKE, 4, 256, FAKE, 10, None) == -4
+    assert L.q4k_expand_weights(None, 0, 256, None, 0, None) == 0
+    assert L.q4k_act_sums(FAKE, FAKE, 4, 256, FAKE, 10, None) == -4
+    assert L.q4k_act_sums(FAKE, FAKE + 4, 4, 256, FAKE, 1 << 30, None) == -3
+    assert L.q4k_gemm(FAKE, FAKE, None, 4, FAKE, 8, 256, FAKE, 8, None) == -1      # null das
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 4, FAKE, 8, 256, FAKE, 7, None) == -1      # ldy < m
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 4, FAKE, 8, 100, FAKE, 8, None) == -2
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 0, FAKE, 8, 256, FAKE, 8, None) == 0
+    assert L.q4k_gemm_dots(FAKE, 4, FAKE, 8, 256, None, None) == -1
+    assert q6k.q4k_launches() >= 0
