@@ -211,3 +211,51 @@ def test_folded_rounding_no_worse_than_split(name):
     print(f"{name}: worst |err|/T layout 1 {worst[1]:.3e}, layout 2 {worst[2]:.3e}", flush=True)
     assert worst[2] <= 2 * worst[1]
     assert worst[2] < 1e-6
+
+
+def test_empty_problems_launch_nothing():
+    # n = 0 or m = 0 is a no-op that leaves the output untouched, for every layout
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    k = 256
+    raw = synthetic.weights(8, k, seed=1)
+    x = synthetic.activations(8, k, seed=1)
+    for layout in LAYOUTS:
+        xq, da, w = prepare(x, raw, 8, layout)
+        before = q6k.q6k_stats()
+        y = torch.full((8, 8), 3.0, dtype=torch.float32, device=gpu_util.DEV)
+        q6k.q6k_gemm(xq, da, 0, w, layout, 8, k, y, ldy=8)
+        q6k.q6k_gemm(xq, da, 8, w, layout, 0, k, y, ldy=8)
+        torch.cuda.synchronize()
+        assert (y == 3.0).all().item()
+        assert q6k.q6k_stats() == before
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_long_k(layout):
+    # 64 super-blocks per row (8 passes over the layout-2 ring's parity buffers)
+    import gpu_util
+    n, m, k = 33, 40, 16384
+    print(f"long k layout={layout}", flush=True)
+    raw = synthetic.weights(m, k, seed=21, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=22, kind="outlier")
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+    xq_ref, da_ref = oracle.quantize(x)
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y, y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_zero_scales_give_zero(layout):
+    # d = 0 on every super-block: every term is zero, so y must be exactly 0 (T = 0)
+    import gpu_util
+    n, m, k = 40, 72, 512
+    raw = synthetic.weights(m, k, seed=31)
+    raw.reshape(m, k // 256, 210)[:, :, 208:210] = 0
+    x = synthetic.activations(n, k, seed=31)
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+    assert (y == 0).all()
