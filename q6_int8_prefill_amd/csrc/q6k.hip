@@ -18,6 +18,7 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -895,6 +896,388 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// folded2_kernel<DOTS>: layout 2, second form, with fewer synchronisations per chunk.
+//
+// Same arithmetic and output as folded_kernel (two K=32 MFMAs per tile and chunk on the digit
+// planes, three VALU operations per output and chunk, d once per super-block); what changes is
+// how operands reach the MFMAs:
+//   - the digit planes of a wave's row tile are private to that wave, so each wave loads them
+//     straight into registers (a 4-entry register ring, 3 chunks ahead) instead of through LDS;
+//   - only the activations and their da, shared by the 4 waves, go through LDS: one ring slot
+//     holds a whole super-block (2 token tiles x 8 chunks x 1 KiB + 2 x 1 KiB of da), the ring
+//     has 4 slots and runs 3 super-blocks ahead, so the workgroup meets at a barrier once per
+//     super-block instead of once per chunk;
+//   - the rescale of tile 1 runs one step late, while the MFMAs of the next chunk's tile 0 run;
+//   - 2 workgroups per CU (up to 256 VGPRs per wave).
+// Work split: the output tiles (64 tokens x 128 rows) are dealt out in rounds of one tile per
+// workgroup slot of the GPU.  When the last round would leave slots idle, its tiles are split
+// along k into `pieces` pieces of whole super-blocks that run side by side and add their partial
+// sums into y, which a small kernel has zeroed first (float atomics: the summation order of the
+// pieces, and so the last bits of those outputs, may differ from run to run).
+// ---------------------------------------------------------------------------------------------
+#ifndef Q6K_FOLDED_KERNEL
+#define Q6K_FOLDED_KERNEL 2
+#endif
+#ifndef Q6K_FOLDED2_WG_PER_CU
+#define Q6K_FOLDED2_WG_PER_CU 2
+#endif
+constexpr int kG2SlotDa = 16384;  // after 2 tiles x 8 chunks x 1 KiB of activations
+constexpr int kG2Slot = 18432;
+constexpr int kG2Ring = 4;
+constexpr int kG2Ahead = 3;  // super-blocks whose activations are in flight
+static_assert(Q6K_FOLDED2_WG_PER_CU * kG2Ring * kG2Slot <= 160 * 1024, "LDS budget");
+static_assert(kG2Ahead < kG2Ring, "ring slot reuse");
+
+struct G2Ctx {
+  __amdgpu_buffer_rsrc_t a, da, b, w;  // both token tiles, their da, row tile planes, row tile d
+  uint8_t* smem;
+  uint32_t l16, dvoff;      // lane * 16; byte offset of this lane's d values in a super-block
+  int wave, lane;
+  int64_t nchunk, c_begin, s_end;  // this piece's first chunk and super-block end
+  uint32_t c_end;                  // and chunk end
+  int64_t n, m, tok0, row0;
+  int32_t* dots;
+};
+
+struct G2State {
+  float acc[2][16], sb[2][16];
+  v16i fh1, fl1;     // MFMA results of tile 1, rescaled one step late
+  float da1p;        // da of tile 1 for those results
+  v4i x0, x1;        // activations of the current chunk, token tiles 0 and 1
+  float da0, da1;    // their da (this lane's token)
+  v4i blo[4], bhi[4];  // digit planes of chunk c in entry c % 4
+  float d[16];       // d of this lane's 16 rows, for the super-block being finished
+};
+
+// The XCD-aware tile order of folded_kernel: tile t = x + gx * y of the dispatch order goes to
+// XCD t % 8, and XCD j takes one (gx/2) x (gy/4) rectangle of the output when the grid splits
+// evenly.
+__device__ __forceinline__ void g2_tile(uint32_t t, uint32_t gx, uint32_t gy, uint32_t* bx,
+                                        uint32_t* by) {
+  if (gx % 2 == 0 && gy % 4 == 0) {
+    const uint32_t xcd = t % 8, local = t / 8, rw = gx / 2, rh = gy / 4;
+    *bx = (xcd % 2) * rw + local % rw;
+    *by = (xcd / 2) * rh + local / rw;
+  } else {
+    *bx = t % gx;
+    *by = t / gx;
+  }
+}
+
+// Digit planes of chunk c (clamped to the piece's last chunk, so every load stays in range).
+__device__ __forceinline__ void g2_load_b(const G2Ctx& k, int64_t c, v4i& lo, v4i& hi) {
+  const uint32_t cc = min((uint32_t)c, k.c_end - 1);
+  lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(k.b, k.l16, cc * 2048, 0));
+  hi = __builtin_bit_cast(v4i,
+                          __builtin_amdgcn_raw_buffer_load_b128(k.b, k.l16 + 1024, cc * 2048, 0));
+}
+
+// d of super-block s for this lane's rows 8q + 4g + i (q, i = 0..3).
+__device__ __forceinline__ void g2_load_d(const G2Ctx& k, int64_t s, float (&d)[16]) {
+  const uint32_t so = (uint32_t)s * 128;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v4f v =
+        __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(k.w, k.dvoff + 32 * q, so, 0));
+    d[4 * q] = v.x;
+    d[4 * q + 1] = v.y;
+    d[4 * q + 2] = v.z;
+    d[4 * q + 3] = v.w;
+  }
+}
+
+// This wave's share of super-block s's activations and da, direct to LDS slot s % 4: four 1 KiB
+// chunk tiles of token tile wave/2 and the da of token tile wave%2 (waves 2 and 3 write the same
+// da bytes as waves 0 and 1).  Nothing is loaded past the piece's last super-block.
+__device__ __forceinline__ void g2_dma(const G2Ctx& k, int64_t s) {
+  if (s >= k.s_end) return;
+  uint8_t* slot = k.smem + (s % kG2Ring) * kG2Slot;
+  const int u = k.wave >> 1, j0 = 4 * (k.wave & 1), ud = k.wave & 1;
+  const uint32_t abase = (uint32_t)((u * k.nchunk + 8 * s + j0) * 1024);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bdma16(k.a, k.l16, abase + i * 1024, slot + u * 8192 + (j0 + i) * 1024);
+  bdma16(k.da, k.l16, (uint32_t)((ud * k.nchunk + 8 * s) * 128), slot + kG2SlotDa + ud * 1024);
+}
+
+// LDS reads of one chunk's activations and da (immediate offsets within the slot).  The previous
+// values are inputs, so the new ones land in other registers than those the MFMAs just issued
+// are reading.
+template <int OFFX, int OFFD>
+__device__ __forceinline__ void g2_read(uint32_t xb, uint32_t dab, G2State& st) {
+  v4i x0, x1;
+  float d0, d1;
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%6\n\t"
+      "ds_read_b128 %1, %4 offset:%7\n\t"
+      "ds_read_b32 %2, %5 offset:%8\n\t"
+      "ds_read_b32 %3, %5 offset:%9"
+      : "=&v"(x0), "=&v"(x1), "=&v"(d0), "=&v"(d1)
+      : "v"(xb), "v"(dab), "n"(OFFX), "n"(OFFX + 8192), "n"(OFFD), "n"(OFFD + 1024),
+        "v"(st.x0), "v"(st.x1)
+      : "memory");
+  st.x0 = x0;
+  st.x1 = x1;
+  st.da0 = d0;
+  st.da1 = d1;
+}
+
+// sb (+)= e * da, or the store of e for the test export (chunks before the piece's first are the
+// placeholder of the first step and are not stored).
+template <bool DOTS, bool FIRST>
+__device__ __forceinline__ void g2_rescale(float (&sb)[16], const float (&e)[16], float dav,
+                                           const G2Ctx& k, int64_t c, int u) {
+  if (DOTS) {
+    if (c < k.c_begin) return;
+    const int g = k.lane >> 5;
+    const int64_t tok = k.tok0 + kTile * u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = k.row0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (tok < k.n && row < k.m) k.dots[(tok * k.m + row) * k.nchunk + c] = (int32_t)e[r];
+    }
+  } else if (FIRST) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[r] = e[r] * dav;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sb[r] = __builtin_fmaf(e[r], dav, sb[r]);
+  }
+}
+
+__device__ __forceinline__ void g2_order(v4i& x, float (&v)[16]) {
+  asm volatile(""
+               : "+v"(x), "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),
+                 "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]),
+                 "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
+// Chunk c = 8s + J.  xb/dab: this lane's LDS addresses in super-block s's slot; xn/dn: in slot
+// s + 1 (read by the last step).
+template <bool DOTS, int J>
+__device__ __forceinline__ void g2_step(const G2Ctx& k, int64_t s, uint32_t xb, uint32_t dab,
+                                        uint32_t xn, uint32_t dn, G2State& st,
+                                        const v16i& bias) {
+  const int64_t c = 8 * s + J;
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(st.x0), "+v"(st.x1), "+v"(st.da0), "+v"(st.da1));
+  const v4i lo = st.blo[J % 4], hi = st.bhi[J % 4];
+  v16i fh0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x0, bias, 0, 0, 0);
+  v16i fl0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, st.x0, bias, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // tile 1 of chunk c - 1, while tile 0's MFMAs run
+  {
+    float e1[16];
+    fold_digits(e1, st.fh1, st.fl1);
+    g2_rescale<DOTS, J == 1>(st.sb[1], e1, st.da1p, k, c - 1, 1);
+  }
+  if (J == 0) {
+    // both tiles have finished super-block s - 1: apply its d, then fetch super-block s's
+    if (!DOTS) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[u][r] = __builtin_fmaf(st.sb[u][r], st.d[r], st.acc[u][r]);
+    }
+    g2_load_d(k, s, st.d);
+  }
+  g2_order(st.x1, st.sb[1]);
+  const v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x1, bias, 0, 0, 0);
+  const v16i fl1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, st.x1, bias, 0, 0, 0);
+  const float da0 = st.da0;
+  st.da1p = st.da1;
+  __builtin_amdgcn_sched_barrier(0);
+  g2_load_b(k, c + 3, st.blo[(J + 3) % 4], st.bhi[(J + 3) % 4]);
+  if (J == 0) g2_dma(k, s + kG2Ahead);
+  if (J == 7) {
+    // super-block s + 1's slot: this wave's share of it has landed, and after the barrier every
+    // wave's has.  Its loads were issued at least two iterations ago, before the planes of
+    // chunks 8s+3 .. 8s+6 (issued in steps 0-3 of this iteration, and feeding MFMAs whose
+    // results reach volatile statements ahead of this one, so the compiler cannot sink them
+    // below it): with at most those 8 loads outstanding, the slot's loads are complete.  (The
+    // compiler is free to move the plane loads relative to the direct-to-LDS ones otherwise, so
+    // no tighter count is safe.)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    g2_read<0, 0>(xn, dn, st);
+  } else {
+    g2_read<(J + 1) * 1024, (J + 1) * 128>(xb, dab, st);
+  }
+  asm volatile("" : "+v"(fh0), "+v"(fl0));
+  {
+    float e0[16];
+    fold_digits(e0, fh0, fl0);
+    g2_rescale<DOTS, J == 0>(st.sb[0], e0, da0, k, c, 0);
+  }
+  st.fh1 = fh1;
+  st.fl1 = fl1;
+}
+
+template <bool DOTS>
+__global__ __launch_bounds__(256, Q6K_FOLDED2_WG_PER_CU) void folded2_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ da,
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
+    int32_t* __restrict__ dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kG2Ring * kG2Slot];
+  const uint32_t pid = blockIdx.x;
+  const bool split = pid >= n_full;
+  const uint32_t tile = split ? n_full + (pid - n_full) / pieces : pid;
+  const int64_t piece = split ? (pid - n_full) % pieces : 0;
+  const int64_t npieces = split ? pieces : 1;
+  uint32_t bx, by;
+  g2_tile(tile, gx, gy, &bx, &by);
+  const int64_t nsb = nchunk / 8;
+  const int64_t s0 = nsb * piece / npieces, s1 = nsb * (piece + 1) / npieces;
+
+  G2Ctx k;
+  k.smem = smem;
+  k.lane = threadIdx.x & 63;
+  k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = k.lane & 31, g = k.lane >> 5;
+  const int64_t T0 = (int64_t)bx * kWgTokTiles, R = (int64_t)by * 4 + k.wave;
+  k.a = make_rsrc(xq + T0 * nchunk * 1024, 2 * nchunk * 1024);
+  k.da = make_rsrc(reinterpret_cast<const uint8_t*>(da) + T0 * nchunk * 128, 2 * nchunk * 128);
+  k.b = make_rsrc(wcodes + R * nchunk * 2048, nchunk * 2048);
+  k.w = make_rsrc(wd + R * nsb * 128, nsb * 128);
+  k.l16 = k.lane * 16;
+  k.dvoff = 16 * g;
+  k.nchunk = nchunk;
+  k.c_begin = 8 * s0;
+  k.c_end = (uint32_t)(8 * s1);
+  k.s_end = s1;
+  k.n = n;
+  k.m = m;
+  k.tok0 = T0 * kTile + p;
+  k.row0 = R * kTile;
+  k.dots = dots;
+  // this lane's LDS addresses in slot 0: its 16 activation bytes, its token's da
+  // (da of token p sits at position 16*((p/4)%2) + 4*(p/8) + p%4 of a chunk's 32 floats)
+  const uint32_t xb0 = lds_addr(smem) + k.l16;
+  const uint32_t db0 =
+      lds_addr(smem) + kG2SlotDa + 4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
+
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
+  G2State st;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[u][r] = st.sb[u][r] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st.d[r] = 0.0f;
+  st.fh1 = bias;  // the first step's late rescale of tile 1 then adds 0 * 0
+  st.fl1 = bias;
+  st.da1p = 0.0f;
+
+  // prologue: super-blocks s0 .. s0+2 of activations, chunks c0 .. c0+2 of digit planes; wait
+  // for all of them, meet, read chunk c0's operands
+#pragma unroll
+  for (int i = 0; i < kG2Ahead; ++i) g2_dma(k, s0 + i);
+  g2_load_b(k, 8 * s0 + 0, st.blo[0], st.bhi[0]);
+  g2_load_b(k, 8 * s0 + 1, st.blo[1], st.bhi[1]);
+  g2_load_b(k, 8 * s0 + 2, st.blo[2], st.bhi[2]);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  st.x0 = st.x1 = v4i{0, 0, 0, 0};
+  const uint32_t slot0 = (uint32_t)(s0 % kG2Ring) * kG2Slot;
+  g2_read<0, 0>(xb0 + slot0, db0 + slot0, st);
+
+  for (int64_t s = s0; s < s1; ++s) {
+    const uint32_t cur = (uint32_t)(s % kG2Ring) * kG2Slot;
+    const uint32_t nxt = (uint32_t)((s + 1) % kG2Ring) * kG2Slot;
+    const uint32_t xb = xb0 + cur, dab = db0 + cur, xn = xb0 + nxt, dn = db0 + nxt;
+    g2_step<DOTS, 0>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 1>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 2>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 3>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 4>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 5>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 6>(k, s, xb, dab, xn, dn, st, bias);
+    g2_step<DOTS, 7>(k, s, xb, dab, xn, dn, st, bias);
+  }
+  // tile 1 of the last chunk, then the last super-block's d
+  {
+    float e1[16];
+    fold_digits(e1, st.fh1, st.fl1);
+    g2_rescale<DOTS, false>(st.sb[1], e1, st.da1p, k, k.c_end - 1, 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // drain the trailing loads
+  if (DOTS) return;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[u][r] = __builtin_fmaf(st.sb[u][r], st.d[r], st.acc[u][r]);
+
+  // The workgroup's 64-token x 128-row output tile goes through LDS (the ring is free once every
+  // wave has passed the first barrier), so that each store or atomic instruction below covers
+  // consecutive rows of one token instead of 64 scattered 4-row pieces.
+  constexpr int kOutLd = 132;  // floats per token in LDS: 128 rows + 4 of padding
+  static_assert(64 * kOutLd * 4 <= kG2Ring * kG2Slot, "output tile fits the ring");
+  float* out = reinterpret_cast<float*>(smem);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(out + (kTile * u + p) * kOutLd + kTile * k.wave + 8 * q + 4 * g) =
+          make_float4(st.acc[u][4 * q], st.acc[u][4 * q + 1], st.acc[u][4 * q + 2],
+                      st.acc[u][4 * q + 3]);
+  __syncthreads();
+  const int64_t tok_base = T0 * kTile, row_base = (int64_t)by * kWgRow;
+  if (!split && vec_store) {
+    // two tokens per instruction, 4 rows per lane: 2 x 512 contiguous bytes
+    const int half = k.lane >> 5, r4 = 4 * (k.lane & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 16 * k.wave + 2 * i + half;
+      const int64_t tok = tok_base + t, row = row_base + r4;
+      if (tok >= n || row >= m) continue;
+      const float4 v = *reinterpret_cast<const float4*>(out + t * kOutLd + r4);
+      float* dst = y + tok * ldy + row;
+      if (row + 3 < m) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        dst[0] = v.x;
+        if (row + 1 < m) dst[1] = v.y;
+        if (row + 2 < m) dst[2] = v.z;
+      }
+    }
+  } else {
+    // one token per instruction, one row per lane: 256 contiguous bytes
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * k.wave + i;
+      const int64_t tok = tok_base + t;
+      if (tok >= n) break;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t row = row_base + 64 * h + k.lane;
+        if (row >= m) continue;
+        const float v = out[t * kOutLd + 64 * h + k.lane];
+        if (split)
+          unsafeAtomicAdd(y + tok * ldy + row, v);
+        else
+          y[tok * ldy + row] = v;
+      }
+    }
+  }
+}
+
+// Zero y over the tiles that folded2_kernel splits along k (tiles n_full .. gx*gy-1 of its
+// order), one workgroup per tile.
+__global__ __launch_bounds__(256) void g2_zero_kernel(float* __restrict__ y, int64_t ldy,
+                                                      int64_t n, int64_t m, uint32_t gx,
+                                                      uint32_t gy, uint32_t n_full) {
+  uint32_t bx, by;
+  g2_tile(n_full + blockIdx.x, gx, gy, &bx, &by);
+  const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
+  if (r >= m) return;
+#pragma unroll 4
+  for (int t = threadIdx.x >> 7; t < 64; t += 2) {
+    const int64_t tok = (int64_t)bx * 64 + t;
+    if (tok < n) y[tok * ldy + r] = 0.0f;
+  }
+}
+
 // =============================================================================================
 // q4_K variant ("r18: Load-time B pre-expansion — staging becomes a bulk copy (W_exp's debut,
 // REVERTED)"): 144-byte super-blocks of 256 weights, f16 d and dmin, eight 6-bit (sc, m) pairs,
@@ -1258,6 +1641,19 @@ bool weight_sizes(int64_t m, int64_t k, int layout, size_t* codes, size_t* scale
   return true;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev < 0 || dev >= 64) return -1;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 q6k_status launch_status() {
   return hipGetLastError() == hipSuccess ? Q6K_OK : Q6K_EHIP;
 }
@@ -1301,8 +1697,28 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   constexpr bool kDots = OUT != kOutY;
   if (layout == Q6K_LAYOUT_FOLDED) {
     const int vec_store = OUT == kOutY && aligned16(y) && ldy % 4 == 0;
+#if Q6K_FOLDED_KERNEL == 2
+    // deal the tiles out in rounds of one per workgroup slot; split the tiles of a partial last
+    // round along k so that its pieces fill the slots
+    const int cus = device_cus();
+    if (cus <= 0) return Q6K_EHIP;
+    const int64_t ntiles = gx * gy, slots = (int64_t)Q6K_FOLDED2_WG_PER_CU * cus;
+    const int64_t rem = ntiles % slots;
+    int64_t pieces = rem ? std::min<int64_t>(slots / rem, k / 256) : 1;
+    if (pieces < 2) pieces = 1;
+    const int64_t n_full = pieces > 1 ? ntiles - rem : ntiles;
+    const int64_t nblocks = n_full + (ntiles - n_full) * pieces;
+    if (nblocks > INT32_MAX) return Q6K_ESIZE;
+    if (OUT == kOutY && n_full < ntiles)
+      hipLaunchKernelGGL(g2_zero_kernel, dim3((unsigned)(ntiles - n_full)), dim3(256), 0, s, y,
+                         ldy, n, m, (uint32_t)gx, (uint32_t)gy, (uint32_t)n_full);
+    hipLaunchKernelGGL((folded2_kernel<kDots>), dim3((unsigned)nblocks), block, 0, s, a, da, wc,
+                       ws, n, m, nchunk, y, ldy, vec_store, dots, (uint32_t)gx, (uint32_t)gy,
+                       (uint32_t)n_full, (uint32_t)pieces);
+#else
     hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, ws, n, m, nchunk, y,
                        ldy, vec_store, dots);
+#endif
   } else if (layout == Q6K_LAYOUT_EXPANDED) {
     hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_EXPANDED, kDots>), grid, block, 0, s, a, da, wc,
                        ws, n, m, nchunk, y, ldy, dots);
