@@ -584,24 +584,8 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 // register r of a tile holds weight row 8*(r/4) + 4*(l/32) + r%4 and token l%32: each lane needs a
 // single da per token tile and chunk.  Workgroup = 4 waves = 64 tokens (token tiles 2*bx, 2*bx+1)
 // x 128 weight rows (row tiles 4*by .. 4*by+3); wave w computes row tile 4*by + w against both
-// token tiles.  The staging ring is the one of gemm_kernel: each wave loads its row tile's two
-// digit planes (and, for the last chunk of a super-block, its 32 d values); waves 0 and 1 load the
-// activations and da of token tile w.
+// token tiles.
 // ---------------------------------------------------------------------------------------------
-#ifndef Q6K_FOLDED_WG_PER_CU
-#define Q6K_FOLDED_WG_PER_CU 3
-#endif
-constexpr int kFSlotA = 0;      // 2 token tiles x 1 KiB of int8 activations
-constexpr int kFSlotB = 2048;   // 4 row tiles x (1 KiB low digits + 1 KiB high digits)
-constexpr int kFSlotW = 10240;  // 4 row tiles x 32 d f32 (filled for a super-block's last chunk)
-constexpr int kFSlot = 10752;
-// da of a whole super-block (8 chunks x 32 floats = 1 KiB per token tile) is loaded with one
-// full-wave load, into one of two buffers (super-block parity) outside the ring
-constexpr int kFDaBytes = 2 * 2 * 1024;
-// 4 slots: loads run 3 chunks ahead, and 4 divides the 8 chunks of a super-block, so that with
-// the loop unrolled over a super-block every slot index is a compile-time constant
-constexpr int kFRing = 4;
-static_assert(Q6K_FOLDED_WG_PER_CU * (kFRing * kFSlot + kFDaBytes) <= 160 * 1024, "LDS budget");
 constexpr float kFoldK = -65.0f * kBiasF;  // exact: 195 * 2^22
 
 // Direct-to-LDS load of 16 bytes per lane through a buffer resource: the wave's LDS base goes in
@@ -618,67 +602,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
                                            0x00020000);
 }
 
-struct FoldSrc {
-  __amdgpu_buffer_rsrc_t a, d, b, w;  // activations, da, digit planes, d of this wave's tiles
-};
-
-// Issue this wave's loads of chunk ci (ci % 8 == CI8) into `slot`.  A chunk past the end is
-// replaced by the last chunk, so that every wave issues at least 2 loads per chunk (3 for waves 0
-// and 1), which the count-based waits rely on; the d load of a super-block's last chunk and the
-// da load of its first are extra and are only issued for real chunks.  The da of super-block s
-// goes to buffer s % 2, last read for super-block s - 2, whose reads ended before the barrier of
-// iteration 8s - 8; it is issued at iteration 8s - 3.
-template <int CI8>
-__device__ __forceinline__ void issue_folded(uint8_t* slot, uint8_t* da_buf, const FoldSrc& src,
-                                             int64_t ci, int64_t nchunk, int wave, int lane) {
-  const bool live = ci < nchunk;
-  const uint32_t cl = (uint32_t)(live ? ci : nchunk - 1);
-  const uint32_t l16 = lane * 16;
-  bdma16(src.b, l16, cl * 2048, slot + kFSlotB + wave * 2048);
-  bdma16(src.b, l16 + 1024, cl * 2048, slot + kFSlotB + wave * 2048 + 1024);
-  if (CI8 == 7 && live && lane < 8)
-    bdma16(src.w, l16, (uint32_t)(ci >> 3) * 128, slot + kFSlotW + wave * 128);
-  if (wave < kWgTokTiles) {
-    bdma16(src.a, l16, cl * 1024, slot + kFSlotA + wave * 1024);
-    if (CI8 == 0 && live)
-      bdma16(src.d, l16, (uint32_t)ci * 128, da_buf + ((ci >> 3) & 1) * 2048 + wave * 1024);
-  }
-}
-
-// s_waitcnt vmcnt(chunks * the fewest loads this wave issues per chunk)
-template <int CHUNKS>
-__device__ __forceinline__ void wait_folded(bool loads_a) {
-  if (loads_a)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 3) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 2) : "memory");
-}
-
-// One chunk's operands in registers: the wave's row tile (both digit planes), the two token
-// tiles and their da for this lane's token.
-struct FoldOps {
-  v4i lo, hi, x0, x1;
-  v2f dav;
-};
-
-// Start the LDS reads of one chunk's operands; the data is waited for (lgkmcnt) before use.
-// bb, xa, dd are per-lane LDS addresses of slot 0 / of the current da buffer; the slot and chunk
-// offsets are immediates, so that no per-slot address is kept in a register.
-template <int OFF_SLOT, int OFF_DA>
-__device__ __forceinline__ void read_ops(FoldOps& o, uint32_t bb, uint32_t xa, uint32_t dd) {
-  asm volatile(
-      "ds_read_b128 %0, %6 offset:%9\n\t"
-      "ds_read_b128 %1, %6 offset:%10\n\t"
-      "ds_read_b128 %2, %7 offset:%11\n\t"
-      "ds_read_b32 %3, %8 offset:%12\n\t"
-      "ds_read_b32 %4, %8 offset:%13\n\t"
-      "ds_read_b128 %5, %7 offset:%14"
-      : "=&v"(o.lo), "=&v"(o.hi), "=&v"(o.x0), "=&v"(o.dav.x), "=&v"(o.dav.y), "=&v"(o.x1)
-      : "v"(bb), "v"(xa), "v"(dd), "n"(OFF_SLOT), "n"(OFF_SLOT + 1024), "n"(OFF_SLOT),
-        "n"(OFF_DA), "n"(OFF_DA + 1024), "n"(OFF_SLOT + 1024)
-      : "memory");
-}
-
 // e = 64*E_hi + E_lo from the two biased digit products (exact, see above), in two phases of 16
 // independent operations (no VALU instruction depends on the one before it).
 __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, const v16i& fl) {
@@ -688,220 +611,8 @@ __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, cons
   for (int r = 0; r < 16; ++r) e[r] += __int_as_float(fl[r]);
 }
 
-// sb (+)= e * da -- the first chunk of a super-block starts sb afresh -- or, for the test export,
-// the store of e.
-template <bool DOTS, bool FIRST>
-__device__ __forceinline__ void rescale(float (&sb)[16], const float (&e)[16], float dav, int lane,
-                                        int64_t c, int64_t tok, int64_t row0, int64_t n,
-                                        int64_t m, int64_t nchunk, int32_t* __restrict__ dots) {
-  if (DOTS) {
-    const int g = lane >> 5;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = row0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < n && row < m) dots[(tok * m + row) * nchunk + c] = (int32_t)e[r];
-    }
-  } else if (FIRST) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sb[r] = e[r] * dav;
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sb[r] = __builtin_fmaf(e[r], dav, sb[r]);
-  }
-}
-
-// An empty statement that the compiler must keep in program order with the other volatile
-// statements (barriers, LDS reads) and that "modifies" the operands and the accumulators: code
-// that reads them after it cannot move above it, code that writes them before cannot move below.
-__device__ __forceinline__ void order_after(FoldOps& o, float (&v)[16]) {
-  asm volatile(""
-               : "+v"(o.lo), "+v"(o.hi), "+v"(o.x1), "+v"(v[0]), "+v"(v[1]), "+v"(v[2]),
-                 "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]),
-                 "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]),
-                 "+v"(v[15]));
-}
-
-struct FoldCtx {
-  uint8_t* smem;
-  uint8_t* da_buf;
-  FoldSrc src;
-  int64_t nchunk, n, m, tok0, row0;
-  int32_t* dots;
-  uint32_t bb, xa, wa;  // per-lane LDS addresses in slot 0: digits, activations, d
-  int wave, lane;
-  bool loads_a;
-};
-
-// Chunk c = 8s + CC of the main loop.
-// Chunk c = 8s + CC of the main loop.  `o` holds this chunk's operands (read during the previous
-// step); once the last MFMA has taken them, the reads of chunk c+1 are started into the same
-// registers and complete while the second tile is rescaled.  dcur / dnext: this lane's da
-// address in the da buffer of super-block s / s + 1.
-template <bool DOTS, int CC>
-__device__ __forceinline__ void folded_step(const FoldCtx& k, int64_t s, uint32_t dcur,
-                                            uint32_t dnext, FoldOps& o, const v16i& bias,
-                                            float (&acc)[2][16], float (&sb)[2][16]) {
-  const int64_t c = 8 * s + CC;
-  // this wave's loads of chunk c+1 have landed (one newer chunk may still be in flight); after
-  // the barrier every wave's have, and every wave is done with chunk c-1's slot
-  wait_folded<kFRing - 3>(k.loads_a);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"
-               : "+v"(o.lo), "+v"(o.hi), "+v"(o.x0), "+v"(o.x1), "+v"(o.dav)::"memory");
-  constexpr int kIssue = (CC + kFRing - 1) % kFRing;
-  issue_folded<(CC + kFRing - 1) % 8>(k.smem + kIssue * kFSlot, k.da_buf, k.src,
-                                      c + kFRing - 1, k.nchunk, k.wave, k.lane);
-  const v16i fh0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.hi, o.x0, bias, 0, 0, 0);
-  const v16i fl0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.lo, o.x0, bias, 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  float e0[16];
-  fold_digits(e0, fh0, fl0);
-  rescale<DOTS, CC == 0>(sb[0], e0, o.dav.x, k.lane, c, k.tok0, k.row0, k.n, k.m, k.nchunk,
-                         k.dots);
-  // order point: the second tile's MFMAs read operands that pass through this statement after
-  // the first tile's rescale, so the instruction selector cannot hoist them (four live MFMA
-  // results would not fit the register budget)
-  order_after(o, sb[0]);
-  const v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.hi, o.x1, bias, 0, 0, 0);
-  const v16i fl1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.lo, o.x1, bias, 0, 0, 0);
-  const float da1 = o.dav.y;
-  __builtin_amdgcn_sched_barrier(0);
-  // (after the last chunk this reads a stale slot whose values are never used: all addresses
-  // stay inside the LDS arrays, and it keeps the step a single basic block)
-  read_ops<((CC + 1) % kFRing) * kFSlot, ((CC + 1) % 8) * 128>(o, k.bb, k.xa,
-                                                                CC == 7 ? dnext : dcur);
-  __builtin_amdgcn_sched_barrier(0);
-  float e1[16];
-  fold_digits(e1, fh1, fl1);
-  rescale<DOTS, CC == 0>(sb[1], e1, da1, k.lane, c, k.tok0 + kTile, k.row0, k.n, k.m,
-                         k.nchunk, k.dots);
-  order_after(o, sb[1]);  // the next step starts after this one's rescale
-  if (!DOTS && CC == 7) {
-    // end of a super-block: apply the d of each of this lane's 16 rows (in this chunk's slot)
-    constexpr int kW = (CC % kFRing) * kFSlot;
-    v4f d0, d1, d2, d3;
-    asm volatile(
-        "ds_read_b128 %0, %9 offset:%10\n\t"
-        "ds_read_b128 %1, %9 offset:%11\n\t"
-        "ds_read_b128 %2, %9 offset:%12\n\t"
-        "ds_read_b128 %3, %9 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "+v"(o.lo), "+v"(o.hi), "+v"(o.x0),
-          "+v"(o.x1), "+v"(o.dav)
-        : "v"(k.wa), "n"(kW), "n"(kW + 32), "n"(kW + 64), "n"(kW + 96)
-        : "memory");
-    const float dv[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
-                          d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(sb[u][r], dv[r], acc[u][r]);
-  }
-}
-
-template <bool DOTS>
-__global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
-    const uint8_t* __restrict__ xq, const float* __restrict__ da,
-    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
-    int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
-    int32_t* __restrict__ dots) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot + kFDaBytes];
-  FoldCtx k;
-  k.smem = smem;
-  k.da_buf = smem + kFRing * kFSlot;
-  k.lane = threadIdx.x & 63;
-  k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  k.loads_a = k.wave < kWgTokTiles;
-  // XCD-aware tile order: workgroup pid = x + gx*y runs on XCD pid % 8, and each XCD has its own
-  // L2.  When the grid splits evenly, XCD j takes one (gx/2) x (gy/4) rectangle of the output,
-  // so each activation tile is fetched into 4 of the 8 L2s and each weight tile into 2
-  // (dispatch order would otherwise spread every tile over all 8).
-  int64_t bx = blockIdx.x, by = blockIdx.y;
-  if (gridDim.x % 2 == 0 && gridDim.y % 4 == 0) {
-    const int64_t pid = blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
-    const int64_t xcd = pid % 8, local = pid / 8;
-    const int64_t rw = gridDim.x / 2, rh = gridDim.y / 4;
-    bx = (xcd % 2) * rw + local % rw;
-    by = (xcd / 2) * rh + local / rw;
-  }
-  const int64_t T0 = bx * kWgTokTiles;     // the workgroup's first token tile
-  const int64_t R = by * 4 + k.wave;       // this wave's row tile
-  const int64_t Ta = T0 + (k.loads_a ? k.wave : 0);
-  const int64_t nsb = nchunk / 8;
-  k.src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
-  k.src.d = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
-  k.src.b = make_rsrc(wcodes + R * nchunk * 2048, nchunk * 2048);
-  k.src.w = make_rsrc(wd + R * nsb * 128, nsb * 128);
-  k.nchunk = nchunk;
-  k.n = n;
-  k.m = m;
-  k.dots = dots;
-  const int p = k.lane & 31, g = k.lane >> 5;
-  k.tok0 = T0 * kTile + p;
-  k.row0 = R * kTile;
-  k.bb = lds_addr(smem) + kFSlotB + k.wave * 2048 + k.lane * 16;
-  k.xa = lds_addr(smem) + kFSlotA + k.lane * 16;
-  k.wa = lds_addr(smem) + kFSlotW + k.wave * 128 + g * 16;
-  // da of token p sits at position 16*((p/4)%2) + 4*(p/8) + p%4 of a tile's 32 floats
-  const uint32_t d0 = lds_addr(k.da_buf) + 4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
-
-  v16i bias;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
-  float acc[2][16], sb[2][16];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[u][r] = sb[u][r] = 0.0f;
-
-  // Prologue: chunks 0 .. 2 in flight; chunk 0 ready in its slot and read into registers.
-  issue_folded<0>(smem + 0 * kFSlot, k.da_buf, k.src, 0, nchunk, k.wave, k.lane);
-  issue_folded<1>(smem + 1 * kFSlot, k.da_buf, k.src, 1, nchunk, k.wave, k.lane);
-  issue_folded<2>(smem + 2 * kFSlot, k.da_buf, k.src, 2, nchunk, k.wave, k.lane);
-  wait_folded<kFRing - 2>(k.loads_a);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  FoldOps ops;
-  read_ops<0, 0>(ops, k.bb, k.xa, d0);
-
-  for (int64_t s = 0; s < nsb; ++s) {
-    const uint32_t dcur = d0 + (s & 1) * 2048, dnext = d0 + ((s + 1) & 1) * 2048;
-    folded_step<DOTS, 0>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 1>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 2>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 3>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 4>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 5>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 6>(k, s, dcur, dnext, ops, bias, acc, sb);
-    folded_step<DOTS, 7>(k, s, dcur, dnext, ops, bias, acc, sb);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
-
-  if (DOTS) return;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t tok = (T0 + u) * kTile + p;
-    if (tok >= n) continue;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t row0 = R * kTile + 8 * q + 4 * g;
-      float* dst = y + tok * ldy + row0;
-      if (vec_store && row0 + 3 < m) {
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]);
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (row0 + rr < m) dst[rr] = acc[u][4 * q + rr];
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
-// folded2_kernel<DOTS>: layout 2, second form, with fewer synchronisations per chunk.
-//
-// Same arithmetic and output as folded_kernel (two K=32 MFMAs per tile and chunk on the digit
-// planes, three VALU operations per output and chunk, d once per super-block); what changes is
-// how operands reach the MFMAs:
+// folded_kernel<DOTS>: how the operands reach the MFMAs, with few synchronisations per chunk:
 //   - the digit planes of a wave's row tile are private to that wave, so each wave loads them
 //     straight into registers (a 4-entry register ring, 3 chunks ahead) instead of through LDS;
 //   - only the activations and their da, shared by the 4 waves, go through LDS: one ring slot
@@ -916,20 +627,17 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
 // sums into y, which a small kernel has zeroed first (float atomics: the summation order of the
 // pieces, and so the last bits of those outputs, may differ from run to run).
 // ---------------------------------------------------------------------------------------------
-#ifndef Q6K_FOLDED_KERNEL
-#define Q6K_FOLDED_KERNEL 2
+#ifndef Q6K_FOLDED_WG_PER_CU
+#define Q6K_FOLDED_WG_PER_CU 2
 #endif
-#ifndef Q6K_FOLDED2_WG_PER_CU
-#define Q6K_FOLDED2_WG_PER_CU 2
-#endif
-constexpr int kG2SlotDa = 16384;  // after 2 tiles x 8 chunks x 1 KiB of activations
-constexpr int kG2Slot = 18432;
-constexpr int kG2Ring = 4;
-constexpr int kG2Ahead = 3;  // super-blocks whose activations are in flight
-static_assert(Q6K_FOLDED2_WG_PER_CU * kG2Ring * kG2Slot <= 160 * 1024, "LDS budget");
-static_assert(kG2Ahead < kG2Ring, "ring slot reuse");
+constexpr int kFSlotDa = 16384;  // after 2 tiles x 8 chunks x 1 KiB of activations
+constexpr int kFSlot = 18432;
+constexpr int kFRing = 4;
+constexpr int kFAhead = 3;  // super-blocks whose activations are in flight
+static_assert(Q6K_FOLDED_WG_PER_CU * kFRing * kFSlot <= 160 * 1024, "LDS budget");
+static_assert(kFAhead < kFRing, "ring slot reuse");
 
-struct G2Ctx {
+struct FoldCtx {
   __amdgpu_buffer_rsrc_t a, da, b, w;  // both token tiles, their da, row tile planes, row tile d
   uint8_t* smem;
   uint32_t l16, dvoff;      // lane * 16; byte offset of this lane's d values in a super-block
@@ -940,7 +648,7 @@ struct G2Ctx {
   int32_t* dots;
 };
 
-struct G2State {
+struct FoldState {
   float acc[2][16], sb[2][16];
   v16i fh1, fl1;     // MFMA results of tile 1, rescaled one step late
   float da1p;        // da of tile 1 for those results
@@ -950,10 +658,10 @@ struct G2State {
   float d[16];       // d of this lane's 16 rows, for the super-block being finished
 };
 
-// The XCD-aware tile order of folded_kernel: tile t = x + gx * y of the dispatch order goes to
-// XCD t % 8, and XCD j takes one (gx/2) x (gy/4) rectangle of the output when the grid splits
-// evenly.
-__device__ __forceinline__ void g2_tile(uint32_t t, uint32_t gx, uint32_t gy, uint32_t* bx,
+// XCD-aware tile order: workgroup t of the dispatch order runs on XCD t % 8, and each XCD has its
+// own L2; when the grid splits evenly, XCD j takes one (gx/2) x (gy/4) rectangle of the output
+// tiles, so each activation tile is fetched into 4 of the 8 L2s and each weight tile into 2.
+__device__ __forceinline__ void fold_tile(uint32_t t, uint32_t gx, uint32_t gy, uint32_t* bx,
                                         uint32_t* by) {
   if (gx % 2 == 0 && gy % 4 == 0) {
     const uint32_t xcd = t % 8, local = t / 8, rw = gx / 2, rh = gy / 4;
@@ -966,7 +674,7 @@ __device__ __forceinline__ void g2_tile(uint32_t t, uint32_t gx, uint32_t gy, ui
 }
 
 // Digit planes of chunk c (clamped to the piece's last chunk, so every load stays in range).
-__device__ __forceinline__ void g2_load_b(const G2Ctx& k, int64_t c, v4i& lo, v4i& hi) {
+__device__ __forceinline__ void fold_load_planes(const FoldCtx& k, int64_t c, v4i& lo, v4i& hi) {
   const uint32_t cc = min((uint32_t)c, k.c_end - 1);
   lo = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(k.b, k.l16, cc * 2048, 0));
   hi = __builtin_bit_cast(v4i,
@@ -974,7 +682,7 @@ __device__ __forceinline__ void g2_load_b(const G2Ctx& k, int64_t c, v4i& lo, v4
 }
 
 // d of super-block s for this lane's rows 8q + 4g + i (q, i = 0..3).
-__device__ __forceinline__ void g2_load_d(const G2Ctx& k, int64_t s, float (&d)[16]) {
+__device__ __forceinline__ void fold_load_d(const FoldCtx& k, int64_t s, float (&d)[16]) {
   const uint32_t so = (uint32_t)s * 128;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -990,21 +698,21 @@ __device__ __forceinline__ void g2_load_d(const G2Ctx& k, int64_t s, float (&d)[
 // This wave's share of super-block s's activations and da, direct to LDS slot s % 4: four 1 KiB
 // chunk tiles of token tile wave/2 and the da of token tile wave%2 (waves 2 and 3 write the same
 // da bytes as waves 0 and 1).  Nothing is loaded past the piece's last super-block.
-__device__ __forceinline__ void g2_dma(const G2Ctx& k, int64_t s) {
+__device__ __forceinline__ void fold_dma(const FoldCtx& k, int64_t s) {
   if (s >= k.s_end) return;
-  uint8_t* slot = k.smem + (s % kG2Ring) * kG2Slot;
+  uint8_t* slot = k.smem + (s % kFRing) * kFSlot;
   const int u = k.wave >> 1, j0 = 4 * (k.wave & 1), ud = k.wave & 1;
   const uint32_t abase = (uint32_t)((u * k.nchunk + 8 * s + j0) * 1024);
 #pragma unroll
   for (int i = 0; i < 4; ++i) bdma16(k.a, k.l16, abase + i * 1024, slot + u * 8192 + (j0 + i) * 1024);
-  bdma16(k.da, k.l16, (uint32_t)((ud * k.nchunk + 8 * s) * 128), slot + kG2SlotDa + ud * 1024);
+  bdma16(k.da, k.l16, (uint32_t)((ud * k.nchunk + 8 * s) * 128), slot + kFSlotDa + ud * 1024);
 }
 
 // LDS reads of one chunk's activations and da (immediate offsets within the slot).  The previous
 // values are inputs, so the new ones land in other registers than those the MFMAs just issued
 // are reading.
 template <int OFFX, int OFFD>
-__device__ __forceinline__ void g2_read(uint32_t xb, uint32_t dab, G2State& st) {
+__device__ __forceinline__ void fold_read(uint32_t xb, uint32_t dab, FoldState& st) {
   v4i x0, x1;
   float d0, d1;
   asm volatile(
@@ -1025,8 +733,8 @@ __device__ __forceinline__ void g2_read(uint32_t xb, uint32_t dab, G2State& st) 
 // sb (+)= e * da, or the store of e for the test export (chunks before the piece's first are the
 // placeholder of the first step and are not stored).
 template <bool DOTS, bool FIRST>
-__device__ __forceinline__ void g2_rescale(float (&sb)[16], const float (&e)[16], float dav,
-                                           const G2Ctx& k, int64_t c, int u) {
+__device__ __forceinline__ void fold_rescale(float (&sb)[16], const float (&e)[16], float dav,
+                                           const FoldCtx& k, int64_t c, int u) {
   if (DOTS) {
     if (c < k.c_begin) return;
     const int g = k.lane >> 5;
@@ -1045,7 +753,7 @@ __device__ __forceinline__ void g2_rescale(float (&sb)[16], const float (&e)[16]
   }
 }
 
-__device__ __forceinline__ void g2_order(v4i& x, float (&v)[16]) {
+__device__ __forceinline__ void fold_order(v4i& x, float (&v)[16]) {
   asm volatile(""
                : "+v"(x), "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),
                  "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]),
@@ -1055,8 +763,8 @@ __device__ __forceinline__ void g2_order(v4i& x, float (&v)[16]) {
 // Chunk c = 8s + J.  xb/dab: this lane's LDS addresses in super-block s's slot; xn/dn: in slot
 // s + 1 (read by the last step).
 template <bool DOTS, int J>
-__device__ __forceinline__ void g2_step(const G2Ctx& k, int64_t s, uint32_t xb, uint32_t dab,
-                                        uint32_t xn, uint32_t dn, G2State& st,
+__device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t xb, uint32_t dab,
+                                        uint32_t xn, uint32_t dn, FoldState& st,
                                         const v16i& bias) {
   const int64_t c = 8 * s + J;
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(st.x0), "+v"(st.x1), "+v"(st.da0), "+v"(st.da1));
@@ -1068,7 +776,7 @@ __device__ __forceinline__ void g2_step(const G2Ctx& k, int64_t s, uint32_t xb, 
   {
     float e1[16];
     fold_digits(e1, st.fh1, st.fl1);
-    g2_rescale<DOTS, J == 1>(st.sb[1], e1, st.da1p, k, c - 1, 1);
+    fold_rescale<DOTS, J == 1>(st.sb[1], e1, st.da1p, k, c - 1, 1);
   }
   if (J == 0) {
     // both tiles have finished super-block s - 1: apply its d, then fetch super-block s's
@@ -1078,16 +786,16 @@ __device__ __forceinline__ void g2_step(const G2Ctx& k, int64_t s, uint32_t xb, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.acc[u][r] = __builtin_fmaf(st.sb[u][r], st.d[r], st.acc[u][r]);
     }
-    g2_load_d(k, s, st.d);
+    fold_load_d(k, s, st.d);
   }
-  g2_order(st.x1, st.sb[1]);
+  fold_order(st.x1, st.sb[1]);
   const v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x1, bias, 0, 0, 0);
   const v16i fl1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, st.x1, bias, 0, 0, 0);
   const float da0 = st.da0;
   st.da1p = st.da1;
   __builtin_amdgcn_sched_barrier(0);
-  g2_load_b(k, c + 3, st.blo[(J + 3) % 4], st.bhi[(J + 3) % 4]);
-  if (J == 0) g2_dma(k, s + kG2Ahead);
+  fold_load_planes(k, c + 3, st.blo[(J + 3) % 4], st.bhi[(J + 3) % 4]);
+  if (J == 0) fold_dma(k, s + kFAhead);
   if (J == 7) {
     // super-block s + 1's slot: this wave's share of it has landed, and after the barrier every
     // wave's has.  Its loads were issued at least two iterations ago, before the planes of
@@ -1097,38 +805,38 @@ __device__ __forceinline__ void g2_step(const G2Ctx& k, int64_t s, uint32_t xb, 
     // compiler is free to move the plane loads relative to the direct-to-LDS ones otherwise, so
     // no tighter count is safe.)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    g2_read<0, 0>(xn, dn, st);
+    fold_read<0, 0>(xn, dn, st);
   } else {
-    g2_read<(J + 1) * 1024, (J + 1) * 128>(xb, dab, st);
+    fold_read<(J + 1) * 1024, (J + 1) * 128>(xb, dab, st);
   }
   asm volatile("" : "+v"(fh0), "+v"(fl0));
   {
     float e0[16];
     fold_digits(e0, fh0, fl0);
-    g2_rescale<DOTS, J == 0>(st.sb[0], e0, da0, k, c, 0);
+    fold_rescale<DOTS, J == 0>(st.sb[0], e0, da0, k, c, 0);
   }
   st.fh1 = fh1;
   st.fl1 = fl1;
 }
 
 template <bool DOTS>
-__global__ __launch_bounds__(256, Q6K_FOLDED2_WG_PER_CU) void folded2_kernel(
+__global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
     int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
     int32_t* __restrict__ dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kG2Ring * kG2Slot];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot];
   const uint32_t pid = blockIdx.x;
   const bool split = pid >= n_full;
   const uint32_t tile = split ? n_full + (pid - n_full) / pieces : pid;
   const int64_t piece = split ? (pid - n_full) % pieces : 0;
   const int64_t npieces = split ? pieces : 1;
   uint32_t bx, by;
-  g2_tile(tile, gx, gy, &bx, &by);
+  fold_tile(tile, gx, gy, &bx, &by);
   const int64_t nsb = nchunk / 8;
   const int64_t s0 = nsb * piece / npieces, s1 = nsb * (piece + 1) / npieces;
 
-  G2Ctx k;
+  FoldCtx k;
   k.smem = smem;
   k.lane = threadIdx.x & 63;
   k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1153,12 +861,12 @@ __global__ __launch_bounds__(256, Q6K_FOLDED2_WG_PER_CU) void folded2_kernel(
   // (da of token p sits at position 16*((p/4)%2) + 4*(p/8) + p%4 of a chunk's 32 floats)
   const uint32_t xb0 = lds_addr(smem) + k.l16;
   const uint32_t db0 =
-      lds_addr(smem) + kG2SlotDa + 4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
+      lds_addr(smem) + kFSlotDa + 4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
 
   v16i bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
-  G2State st;
+  FoldState st;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -1172,33 +880,33 @@ __global__ __launch_bounds__(256, Q6K_FOLDED2_WG_PER_CU) void folded2_kernel(
   // prologue: super-blocks s0 .. s0+2 of activations, chunks c0 .. c0+2 of digit planes; wait
   // for all of them, meet, read chunk c0's operands
 #pragma unroll
-  for (int i = 0; i < kG2Ahead; ++i) g2_dma(k, s0 + i);
-  g2_load_b(k, 8 * s0 + 0, st.blo[0], st.bhi[0]);
-  g2_load_b(k, 8 * s0 + 1, st.blo[1], st.bhi[1]);
-  g2_load_b(k, 8 * s0 + 2, st.blo[2], st.bhi[2]);
+  for (int i = 0; i < kFAhead; ++i) fold_dma(k, s0 + i);
+  fold_load_planes(k, 8 * s0 + 0, st.blo[0], st.bhi[0]);
+  fold_load_planes(k, 8 * s0 + 1, st.blo[1], st.bhi[1]);
+  fold_load_planes(k, 8 * s0 + 2, st.blo[2], st.bhi[2]);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   st.x0 = st.x1 = v4i{0, 0, 0, 0};
-  const uint32_t slot0 = (uint32_t)(s0 % kG2Ring) * kG2Slot;
-  g2_read<0, 0>(xb0 + slot0, db0 + slot0, st);
+  const uint32_t slot0 = (uint32_t)(s0 % kFRing) * kFSlot;
+  fold_read<0, 0>(xb0 + slot0, db0 + slot0, st);
 
   for (int64_t s = s0; s < s1; ++s) {
-    const uint32_t cur = (uint32_t)(s % kG2Ring) * kG2Slot;
-    const uint32_t nxt = (uint32_t)((s + 1) % kG2Ring) * kG2Slot;
+    const uint32_t cur = (uint32_t)(s % kFRing) * kFSlot;
+    const uint32_t nxt = (uint32_t)((s + 1) % kFRing) * kFSlot;
     const uint32_t xb = xb0 + cur, dab = db0 + cur, xn = xb0 + nxt, dn = db0 + nxt;
-    g2_step<DOTS, 0>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 1>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 2>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 3>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 4>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 5>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 6>(k, s, xb, dab, xn, dn, st, bias);
-    g2_step<DOTS, 7>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 0>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 1>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 2>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 3>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 4>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 5>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 6>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 7>(k, s, xb, dab, xn, dn, st, bias);
   }
   // tile 1 of the last chunk, then the last super-block's d
   {
     float e1[16];
     fold_digits(e1, st.fh1, st.fl1);
-    g2_rescale<DOTS, false>(st.sb[1], e1, st.da1p, k, k.c_end - 1, 1);
+    fold_rescale<DOTS, false>(st.sb[1], e1, st.da1p, k, k.c_end - 1, 1);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // drain the trailing loads
   if (DOTS) return;
@@ -1211,7 +919,7 @@ __global__ __launch_bounds__(256, Q6K_FOLDED2_WG_PER_CU) void folded2_kernel(
   // wave has passed the first barrier), so that each store or atomic instruction below covers
   // consecutive rows of one token instead of 64 scattered 4-row pieces.
   constexpr int kOutLd = 132;  // floats per token in LDS: 128 rows + 4 of padding
-  static_assert(64 * kOutLd * 4 <= kG2Ring * kG2Slot, "output tile fits the ring");
+  static_assert(64 * kOutLd * 4 <= kFRing * kFSlot, "output tile fits the ring");
   float* out = reinterpret_cast<float*>(smem);
   __syncthreads();
 #pragma unroll
@@ -1262,13 +970,13 @@ __global__ __launch_bounds__(256, Q6K_FOLDED2_WG_PER_CU) void folded2_kernel(
   }
 }
 
-// Zero y over the tiles that folded2_kernel splits along k (tiles n_full .. gx*gy-1 of its
+// Zero y over the tiles that folded_kernel splits along k (tiles n_full .. gx*gy-1 of its
 // order), one workgroup per tile.
-__global__ __launch_bounds__(256) void g2_zero_kernel(float* __restrict__ y, int64_t ldy,
+__global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, int64_t ldy,
                                                       int64_t n, int64_t m, uint32_t gx,
                                                       uint32_t gy, uint32_t n_full) {
   uint32_t bx, by;
-  g2_tile(n_full + blockIdx.x, gx, gy, &bx, &by);
+  fold_tile(n_full + blockIdx.x, gx, gy, &bx, &by);
   const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
   if (r >= m) return;
 #pragma unroll 4
@@ -1697,12 +1405,11 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   constexpr bool kDots = OUT != kOutY;
   if (layout == Q6K_LAYOUT_FOLDED) {
     const int vec_store = OUT == kOutY && aligned16(y) && ldy % 4 == 0;
-#if Q6K_FOLDED_KERNEL == 2
     // deal the tiles out in rounds of one per workgroup slot; split the tiles of a partial last
     // round along k so that its pieces fill the slots
     const int cus = device_cus();
     if (cus <= 0) return Q6K_EHIP;
-    const int64_t ntiles = gx * gy, slots = (int64_t)Q6K_FOLDED2_WG_PER_CU * cus;
+    const int64_t ntiles = gx * gy, slots = (int64_t)Q6K_FOLDED_WG_PER_CU * cus;
     const int64_t rem = ntiles % slots;
     int64_t pieces = rem ? std::min<int64_t>(slots / rem, k / 256) : 1;
     if (pieces < 2) pieces = 1;
@@ -1710,15 +1417,11 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
     const int64_t nblocks = n_full + (ntiles - n_full) * pieces;
     if (nblocks > INT32_MAX) return Q6K_ESIZE;
     if (OUT == kOutY && n_full < ntiles)
-      hipLaunchKernelGGL(g2_zero_kernel, dim3((unsigned)(ntiles - n_full)), dim3(256), 0, s, y,
+      hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)(ntiles - n_full)), dim3(256), 0, s, y,
                          ldy, n, m, (uint32_t)gx, (uint32_t)gy, (uint32_t)n_full);
-    hipLaunchKernelGGL((folded2_kernel<kDots>), dim3((unsigned)nblocks), block, 0, s, a, da, wc,
+    hipLaunchKernelGGL((folded_kernel<kDots>), dim3((unsigned)nblocks), block, 0, s, a, da, wc,
                        ws, n, m, nchunk, y, ldy, vec_store, dots, (uint32_t)gx, (uint32_t)gy,
                        (uint32_t)n_full, (uint32_t)pieces);
-#else
-    hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, ws, n, m, nchunk, y,
-                       ldy, vec_store, dots);
-#endif
   } else if (layout == Q6K_LAYOUT_EXPANDED) {
     hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_EXPANDED, kDots>), grid, block, 0, s, a, da, wc,
                        ws, n, m, nchunk, y, ldy, dots);

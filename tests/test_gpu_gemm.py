@@ -234,7 +234,7 @@ def test_empty_problems_launch_nothing():
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_gemm_long_k(layout):
-    # 64 super-blocks per row (8 passes over the layout-2 ring's parity buffers)
+    # 64 super-blocks per row (on layout 2 these few tiles are split along k into many pieces)
     import gpu_util
     n, m, k = 33, 40, 16384
     print(f"long k layout={layout}", flush=True)
@@ -259,3 +259,27 @@ def test_gemm_zero_scales_give_zero(layout):
     xq, da, w = prepare(x, raw, m, layout)
     y = gpu_util.gemm(xq, da, n, w, layout, m, k)
     assert (y == 0).all()
+
+
+@pytest.mark.parametrize("n,m,k", [(1024, 1024, 2560), (256, 256, 25600)])
+def test_folded_split_k_pieces(n, m, k):
+    """Layout 2 deals its 64-token x 128-row output tiles out in rounds of one per workgroup slot
+    and splits the tiles of a partial last round along k into pieces of whole super-blocks, whose
+    partial sums are added into y after a zeroing pass.  On a 256-CU device these shapes give
+    pieces of unequal length (10 super-blocks over 4 pieces; 100 over 64).  The integer numerators
+    must stay bit-exact and the outputs within tolerance, checked on a sample of tokens."""
+    import gpu_util
+    print(f"split-k pieces n={n} m={m} k={k}", flush=True)
+    raw = synthetic.weights(m, k, seed=k + m, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=n + 5, kind="outlier")
+    xq, da, w = prepare(x, raw, m, 2)
+    rows = sampled_tokens(n, 12, seed=k)
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    dots = gpu_util.chunkdots(xq, da, n, w, 2, m, k)[rows]
+    np.testing.assert_array_equal(dots, oracle.chunkdots(xq_ref, raw, m))
+    del dots
+    y = gpu_util.gemm(xq, da, n, w, 2, m, k)
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y[rows], y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+    assert np.isfinite(y).all()
