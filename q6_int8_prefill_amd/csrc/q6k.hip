@@ -642,8 +642,8 @@ struct FoldCtx {
   uint8_t* smem;
   uint32_t l16, dvoff;      // lane * 16; byte offset of this lane's d values in a super-block
   int wave, lane;
-  int64_t nchunk, c_begin, s_end;  // this piece's first chunk and super-block end
-  uint32_t c_end;                  // and chunk end
+  int64_t nchunk, c_begin;  // this piece's first chunk
+  uint32_t c_end, s_end;    // and its chunk and super-block ends
   int64_t n, m, tok0, row0;
   int32_t* dots;
 };
@@ -682,12 +682,25 @@ __device__ __forceinline__ void fold_load_planes(const FoldCtx& k, int64_t c, v4
 }
 
 // d of super-block s for this lane's rows 8q + 4g + i (q, i = 0..3).
-__device__ __forceinline__ void fold_load_d(const FoldCtx& k, int64_t s, float (&d)[16]) {
+// The lane offset passes through an empty statement that reads the accumulators just updated
+// with the previous d, so the loads cannot be hoisted above that update and the new values can
+// take the old ones' registers (no copies at the loop's back edge).
+__device__ __forceinline__ void fold_load_d(const FoldCtx& k, int64_t s, float (&d)[16],
+                                            const float (&a0)[16], const float (&a1)[16]) {
   const uint32_t so = (uint32_t)s * 128;
+  uint32_t voff = k.dvoff;
+  asm volatile(""
+               : "+v"(voff)
+               : "v"(a0[0]), "v"(a0[1]), "v"(a0[2]), "v"(a0[3]), "v"(a0[4]), "v"(a0[5]),
+                 "v"(a0[6]), "v"(a0[7]), "v"(a0[8]), "v"(a0[9]), "v"(a0[10]), "v"(a0[11]),
+                 "v"(a0[12]), "v"(a0[13]), "v"(a0[14]), "v"(a0[15]), "v"(a1[0]), "v"(a1[1]),
+                 "v"(a1[2]), "v"(a1[3]), "v"(a1[4]), "v"(a1[5]), "v"(a1[6]), "v"(a1[7]),
+                 "v"(a1[8]), "v"(a1[9]), "v"(a1[10]), "v"(a1[11]), "v"(a1[12]), "v"(a1[13]),
+                 "v"(a1[14]), "v"(a1[15]));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const v4f v =
-        __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(k.w, k.dvoff + 32 * q, so, 0));
+        __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(k.w, voff + 32 * q, so, 0));
     d[4 * q] = v.x;
     d[4 * q + 1] = v.y;
     d[4 * q + 2] = v.z;
@@ -699,7 +712,7 @@ __device__ __forceinline__ void fold_load_d(const FoldCtx& k, int64_t s, float (
 // chunk tiles of token tile wave/2 and the da of token tile wave%2 (waves 2 and 3 write the same
 // da bytes as waves 0 and 1).  Nothing is loaded past the piece's last super-block.
 __device__ __forceinline__ void fold_dma(const FoldCtx& k, int64_t s) {
-  if (s >= k.s_end) return;
+  if ((uint32_t)s >= k.s_end) return;
   uint8_t* slot = k.smem + (s % kFRing) * kFSlot;
   const int u = k.wave >> 1, j0 = 4 * (k.wave & 1), ud = k.wave & 1;
   const uint32_t abase = (uint32_t)((u * k.nchunk + 8 * s + j0) * 1024);
@@ -753,11 +766,13 @@ __device__ __forceinline__ void fold_rescale(float (&sb)[16], const float (&e)[1
   }
 }
 
-__device__ __forceinline__ void fold_order(v4i& x, float (&v)[16]) {
+__device__ __forceinline__ void fold_order(v4i& x, const float (&v)[16]) {
+  // v are inputs only: tied in/out operands would make the register allocator copy them
   asm volatile(""
-               : "+v"(x), "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),
-                 "+v"(v[5]), "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]),
-                 "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+               : "+v"(x)
+               : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]),
+                 "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]),
+                 "v"(v[13]), "v"(v[14]), "v"(v[15]));
 }
 
 // Chunk c = 8s + J.  xb/dab: this lane's LDS addresses in super-block s's slot; xn/dn: in slot
@@ -786,7 +801,7 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.acc[u][r] = __builtin_fmaf(st.sb[u][r], st.d[r], st.acc[u][r]);
     }
-    fold_load_d(k, s, st.d);
+    fold_load_d(k, s, st.d, st.acc[0], st.acc[1]);
   }
   fold_order(st.x1, st.sb[1]);
   const v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x1, bias, 0, 0, 0);
@@ -851,7 +866,7 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   k.nchunk = nchunk;
   k.c_begin = 8 * s0;
   k.c_end = (uint32_t)(8 * s1);
-  k.s_end = s1;
+  k.s_end = (uint32_t)s1;
   k.n = n;
   k.m = m;
   k.tok0 = T0 * kTile + p;
