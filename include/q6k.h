@@ -129,7 +129,12 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
  * ("r38 ..." sec. 2.2, 2.4).  Layouts 0 and 1 accumulate each 32-k chunk as two independent f32
  * additions, one per 16-k half.  Layout 2 forms the chunk's exact integer
  * E = sc[2c]*D[2c] + sc[2c+1]*D[2c+1] and adds da * E once per chunk, then applies d once per
- * super-block; the result differs from layouts 0/1 only in f32 rounding.
+ * super-block; the result differs from layouts 0/1 only in f32 rounding.  When its output tiles
+ * (64 tokens x 128 rows) do not fill whole rounds of the GPU's workgroup slots, layout 2 splits
+ * the tiles of the last round along k: it first zeroes them in y, then adds the pieces' partial
+ * sums with float atomics in no fixed order, so the last bits of those outputs may vary from run
+ * to run (always within the rounding of one f32 addition per piece).  Two calls that write the
+ * same y concurrently on different streams race.
  *   xq, da  : outputs of q6k_quantize_act for the same n, k
  *   w       : output of q6k_expand_weights for the same m, k and `layout`
  *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned; only y[0..n)[0..m) is
