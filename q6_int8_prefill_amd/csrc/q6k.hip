@@ -290,6 +290,71 @@ __device__ __forceinline__ uint32_t center4(uint32_t nib, uint32_t fld) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Work split shared by the GEMM kernels.  Every GEMM workgroup computes one 64-token x 128-row
+// output tile (gx x gy tiles).  The tiles are dealt out in rounds of one per workgroup slot of
+// the GPU (workgroups per CU x CUs); when the last round would leave slots idle, its tiles are
+// split along k into `pieces` pieces of whole super-blocks that run side by side and add their
+// partial sums into y, which split_zero_kernel zeroes first (float atomics: the order in which
+// the pieces add, and so the last bits of those outputs, may differ from run to run).
+// Workgroups 0 .. n_full-1 take whole tiles, the rest take pieces.
+// ---------------------------------------------------------------------------------------------
+// XCD-aware tile order: workgroup t of the dispatch order runs on XCD t % 8, and each XCD has its
+// own L2; when the grid splits evenly, XCD j takes one (gx/2) x (gy/4) rectangle of the output
+// tiles, so each activation tile is fetched into 4 of the 8 L2s and each weight tile into 2.
+__device__ __forceinline__ void tile_of(uint32_t t, uint32_t gx, uint32_t gy, uint32_t* bx,
+                                        uint32_t* by) {
+  if (gx % 2 == 0 && gy % 4 == 0) {
+    const uint32_t xcd = t % 8, local = t / 8, rw = gx / 2, rh = gy / 4;
+    *bx = (xcd % 2) * rw + local % rw;
+    *by = (xcd / 2) * rh + local / rw;
+  } else {
+    *bx = t % gx;
+    *by = t / gx;
+  }
+}
+
+struct TileWork {
+  uint32_t bx, by;  // token-tile pair and row-tile quad of the output tile
+  int64_t s0, s1;   // super-blocks [s0, s1) of k
+  bool split;       // a piece of a split tile: add into y atomically
+};
+
+template <bool XCD_ORDER>
+__device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_t gy,
+                                              uint32_t n_full, uint32_t pieces, int64_t nsb) {
+  TileWork w;
+  w.split = pid >= n_full;
+  const uint32_t tile = w.split ? n_full + (pid - n_full) / pieces : pid;
+  const int64_t piece = w.split ? (pid - n_full) % pieces : 0;
+  const int64_t npieces = w.split ? pieces : 1;
+  if (XCD_ORDER) {
+    tile_of(tile, gx, gy, &w.bx, &w.by);
+  } else {
+    w.bx = tile % gx;
+    w.by = tile / gx;
+  }
+  w.s0 = nsb * piece / npieces;
+  w.s1 = nsb * (piece + 1) / npieces;
+  return w;
+}
+
+// Zero y over the tiles that a GEMM splits along k (tiles n_full .. gx*gy-1 of the tile order),
+// one workgroup per tile.
+__global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, int64_t ldy,
+                                                      int64_t n, int64_t m, uint32_t gx,
+                                                      uint32_t gy, uint32_t n_full) {
+  uint32_t bx, by;
+  tile_of(n_full + blockIdx.x, gx, gy, &bx, &by);
+  const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
+  if (r >= m) return;
+#pragma unroll 4
+  for (int t = threadIdx.x >> 7; t < 64; t += 2) {
+    const int64_t tok = (int64_t)bx * 64 + t;
+    if (tok < n) y[tok * ldy + r] = 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // GEMM.  Workgroup = 4 waves = 64 tokens (token tiles 2*bx, 2*bx+1) x 128 weight rows (row tiles
 // 4*by .. 4*by+3).  Wave w computes token tile w%2 against row tiles 2*(w/2) and 2*(w/2)+1: two
 // 32x32 output tiles, 32 f32 accumulators per lane.
@@ -315,6 +380,9 @@ __device__ __forceinline__ uint32_t center4(uint32_t nib, uint32_t fld) {
 // Output layout of the MFMA: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4 (a token)
 // and column l%32 (a weight row).
 // ---------------------------------------------------------------------------------------------
+#ifndef Q6K_GEMM01_XCD_ORDER
+#define Q6K_GEMM01_XCD_ORDER 0
+#endif
 #ifndef Q6K_WG_PER_CU
 #define Q6K_WG_PER_CU 4
 #endif
@@ -342,31 +410,46 @@ struct RingSize {
 __device__ __forceinline__ constexpr int loads_per_chunk(bool loads_a) { return loads_a ? 4 : 2; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)(p);
 }
 
-__device__ __forceinline__ void dma16(const uint8_t* gsrc, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc), (lds_void_t*)(lds_wave_base), 16, 0, 0);
+// Direct-to-LDS load of 16 bytes per lane through a buffer resource: the wave's LDS base goes in
+// M0, the lane offset is a constant register and the chunk offset a scalar, so no per-load
+// address arithmetic runs on the vector ALU.  Lanes past the resource's size read zeros.
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                       uint8_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_wave_base), 16, voff, soff, 0, 0);
 }
+
+// Buffer resource over `bytes` bytes at p (raw, no stride; 32-bit range, checked on the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Buffer resources of one workgroup's operands: this wave's row tile (codes and scales) and, for
+// waves 0 and 1, token tile `wave` (activations and da).
+struct GemmSrc {
+  __amdgpu_buffer_rsrc_t a, d, b, s;
+};
 
 // Issue this wave's loads of chunk c (already clamped to a valid chunk) into `slot`.
 template <int LAYOUT>
-__device__ __forceinline__ void issue_chunk(uint8_t* slot, const uint8_t* a_src,
-                                            const uint8_t* b_src, const uint8_t* s_src,
-                                            const uint8_t* d_src, int64_t c, int wave, int lane) {
+__device__ __forceinline__ void issue_chunk(uint8_t* slot, const GemmSrc& src, int64_t c, int wave,
+                                            int lane) {
+  const uint32_t l16 = lane * 16, cc = (uint32_t)c;
   if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
-    dma16(b_src + c * 1024 + lane * 16, slot + kSlotB + wave * 1024);
-    if (lane < 16) dma16(s_src + c * 256 + lane * 16, slot + kSlotS + wave * 256);
+    bdma16(src.b, l16, cc * 1024, slot + kSlotB + wave * 1024);
+    if (lane < 16) bdma16(src.s, l16, cc * 256, slot + kSlotS + wave * 256);
   } else {
-    if (lane < 48) dma16(b_src + c * 768 + lane * 16, slot + kSlotRawB + wave * 768);
-    if (lane < 8) dma16(s_src + c * 128 + lane * 16, slot + kSlotRawS + wave * 128);
+    if (lane < 48) bdma16(src.b, l16, cc * 768, slot + kSlotRawB + wave * 768);
+    if (lane < 8) bdma16(src.s, l16, cc * 128, slot + kSlotRawS + wave * 128);
   }
   if (wave < kWgTokTiles) {
-    dma16(a_src + c * 1024 + lane * 16, slot + kSlotA + wave * 1024);
-    if (lane < 8) dma16(d_src + c * 128 + lane * 16, slot + kSlotD + wave * 128);
+    bdma16(src.a, l16, cc * 1024, slot + kSlotA + wave * 1024);
+    if (lane < 8) bdma16(src.d, l16, cc * 128, slot + kSlotD + wave * 128);
   }
 }
 
@@ -455,7 +538,9 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
                                                       const uint8_t* __restrict__ wscales,
                                                       int64_t n, int64_t m, int64_t nchunk,
                                                       float* __restrict__ y, int64_t ldy,
-                                                      int32_t* __restrict__ dots) {
+                                                      int32_t* __restrict__ dots, uint32_t gx,
+                                                      uint32_t gy, uint32_t n_full,
+                                                      uint32_t pieces) {
   constexpr int kSlot = SlotSize<LAYOUT>::value;
   constexpr int kRing = RingSize<LAYOUT>::value;
   static_assert(Q6K_WG_PER_CU * kRing * kSlot <= 160 * 1024, "LDS budget");
@@ -465,20 +550,21 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   const bool loads_a = wave < kWgTokTiles;
   const int tt = wave & 1;                              // token tile of this wave in the workgroup
   const int rp = wave >> 1;                             // row-tile pair of this wave
-  const int64_t T = (int64_t)blockIdx.x * kWgTokTiles + tt;
-  const int64_t R0 = (int64_t)blockIdx.y * 4;           // the workgroup's first row tile
-  const int64_t Ta = (int64_t)blockIdx.x * kWgTokTiles + (loads_a ? wave : 0);
+  const TileWork tw = tile_work<Q6K_GEMM01_XCD_ORDER != 0>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
+  const int64_t c0 = 8 * tw.s0, c1 = 8 * tw.s1;        // this workgroup's chunks
+  const int64_t T = (int64_t)tw.bx * kWgTokTiles + tt;
+  const int64_t R0 = (int64_t)tw.by * 4;                // the workgroup's first row tile
+  const int64_t Ta = (int64_t)tw.bx * kWgTokTiles + (loads_a ? wave : 0);
 
-  const uint8_t* a_src = xq + Ta * nchunk * 1024;
-  const uint8_t* d_src = reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128;
-  const uint8_t* b_src;
-  const uint8_t* s_src;
+  GemmSrc src;
+  src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
+  src.d = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
   if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
-    b_src = wcodes + (R0 + wave) * nchunk * 1024;
-    s_src = wscales + (R0 + wave) * nchunk * 256;
+    src.b = make_rsrc(wcodes + (R0 + wave) * nchunk * 1024, nchunk * 1024);
+    src.s = make_rsrc(wscales + (R0 + wave) * nchunk * 256, nchunk * 256);
   } else {
-    b_src = wcodes + (R0 + wave) * nchunk * 768;
-    s_src = wscales + (R0 + wave) * nchunk * 128;
+    src.b = make_rsrc(wcodes + (R0 + wave) * nchunk * 768, nchunk * 768);
+    src.s = make_rsrc(wscales + (R0 + wave) * nchunk * 128, nchunk * 128);
   }
 
   v16i bias;
@@ -490,11 +576,10 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-  // Prologue: chunks 0 .. kRing-2 in flight; chunk 0 ready in its slot.
+  // Prologue: chunks c0 .. c0+kRing-2 in flight; chunk c0 ready in its slot.
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j)
-    issue_chunk<LAYOUT>(smem + j * kSlot, a_src, b_src, s_src, d_src,
-                        j < nchunk ? j : nchunk - 1, wave, lane);
+    issue_chunk<LAYOUT>(smem + j * kSlot, src, c0 + j < c1 ? c0 + j : c1 - 1, wave, lane);
   wait_chunks<kRing - 2>(loads_a);
   if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot(smem, wave, lane);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -503,15 +588,14 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   int slot_c = 0;                 // slot of chunk c
   int slot_next = 1;              // slot of chunk c+1
   int slot_issue = kRing - 1;     // slot of chunk c+kRing-1
-  for (int64_t c = 0; c < nchunk; ++c) {
+  for (int64_t c = c0; c < c1; ++c) {
     // this wave's loads of chunk c+1 have landed (kRing-3 newer chunks may still be in flight)
     wait_chunks<kRing - 3>(loads_a);
     if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot(smem + slot_next * kSlot, wave, lane);
     // chunk c+1 complete in LDS for every wave; every wave is done with chunk c-1's slot
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int64_t ci = c + kRing - 1;
-    issue_chunk<LAYOUT>(smem + slot_issue * kSlot, a_src, b_src, s_src, d_src,
-                        ci < nchunk ? ci : nchunk - 1, wave, lane);
+    issue_chunk<LAYOUT>(smem + slot_issue * kSlot, src, ci < c1 ? ci : c1 - 1, wave, lane);
     // LDS reads of this chunk: row tile 2rp's B and d*sc, A and da, then row tile 2rp+1's
     const uint8_t* slot = smem + slot_c * kSlot;
     const uint32_t aa = lds_addr(slot + kSlotA + tt * 1024 + lane * 16);
@@ -560,7 +644,14 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < n) y[tok * ldy + mcol] = acc[u][r];
+      if (tok < n) {
+        // a lane's 16 values are one row of 16 tokens; an instruction covers 32 consecutive
+        // rows of 2 tokens
+        if (tw.split)
+          unsafeAtomicAdd(y + tok * ldy + mcol, acc[u][r]);
+        else
+          y[tok * ldy + mcol] = acc[u][r];
+      }
     }
   }
 }
@@ -588,19 +679,6 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 // ---------------------------------------------------------------------------------------------
 constexpr float kFoldK = -65.0f * kBiasF;  // exact: 195 * 2^22
 
-// Direct-to-LDS load of 16 bytes per lane through a buffer resource: the wave's LDS base goes in
-// M0, the lane offset is a constant register and the chunk offset a scalar, so no per-load
-// address arithmetic runs on the vector ALU.  Lanes past the resource's size read zeros.
-__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                       uint8_t* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_wave_base), 16, voff, soff, 0, 0);
-}
-
-// Buffer resource over `bytes` bytes at p (raw, no stride; 32-bit range, checked on the host).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 // e = 64*E_hi + E_lo from the two biased digit products (exact, see above), in two phases of 16
 // independent operations (no VALU instruction depends on the one before it).
@@ -621,11 +699,8 @@ __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, cons
 //     super-block instead of once per chunk;
 //   - the rescale of tile 1 runs one step late, while the MFMAs of the next chunk's tile 0 run;
 //   - 2 workgroups per CU (up to 256 VGPRs per wave).
-// Work split: the output tiles (64 tokens x 128 rows) are dealt out in rounds of one tile per
-// workgroup slot of the GPU.  When the last round would leave slots idle, its tiles are split
-// along k into `pieces` pieces of whole super-blocks that run side by side and add their partial
-// sums into y, which a small kernel has zeroed first (float atomics: the summation order of the
-// pieces, and so the last bits of those outputs, may differ from run to run).
+// Work split: tile_work (rounds of one tile per workgroup slot, a partial last round split along
+// k into pieces that add into y).
 // ---------------------------------------------------------------------------------------------
 #ifndef Q6K_FOLDED_WG_PER_CU
 #define Q6K_FOLDED_WG_PER_CU 2
@@ -658,20 +733,6 @@ struct FoldState {
   float d[16];       // d of this lane's 16 rows, for the super-block being finished
 };
 
-// XCD-aware tile order: workgroup t of the dispatch order runs on XCD t % 8, and each XCD has its
-// own L2; when the grid splits evenly, XCD j takes one (gx/2) x (gy/4) rectangle of the output
-// tiles, so each activation tile is fetched into 4 of the 8 L2s and each weight tile into 2.
-__device__ __forceinline__ void fold_tile(uint32_t t, uint32_t gx, uint32_t gy, uint32_t* bx,
-                                        uint32_t* by) {
-  if (gx % 2 == 0 && gy % 4 == 0) {
-    const uint32_t xcd = t % 8, local = t / 8, rw = gx / 2, rh = gy / 4;
-    *bx = (xcd % 2) * rw + local % rw;
-    *by = (xcd / 2) * rh + local / rw;
-  } else {
-    *bx = t % gx;
-    *by = t / gx;
-  }
-}
 
 // Digit planes of chunk c (clamped to the piece's last chunk, so every load stays in range).
 __device__ __forceinline__ void fold_load_planes(const FoldCtx& k, int64_t c, v4i& lo, v4i& hi) {
@@ -841,15 +902,11 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
     int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
     int32_t* __restrict__ dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot];
-  const uint32_t pid = blockIdx.x;
-  const bool split = pid >= n_full;
-  const uint32_t tile = split ? n_full + (pid - n_full) / pieces : pid;
-  const int64_t piece = split ? (pid - n_full) % pieces : 0;
-  const int64_t npieces = split ? pieces : 1;
-  uint32_t bx, by;
-  fold_tile(tile, gx, gy, &bx, &by);
+  const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
+  const bool split = tw.split;
+  const uint32_t bx = tw.bx, by = tw.by;
   const int64_t nsb = nchunk / 8;
-  const int64_t s0 = nsb * piece / npieces, s1 = nsb * (piece + 1) / npieces;
+  const int64_t s0 = tw.s0, s1 = tw.s1;
 
   FoldCtx k;
   k.smem = smem;
@@ -985,21 +1042,6 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   }
 }
 
-// Zero y over the tiles that folded_kernel splits along k (tiles n_full .. gx*gy-1 of its
-// order), one workgroup per tile.
-__global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, int64_t ldy,
-                                                      int64_t n, int64_t m, uint32_t gx,
-                                                      uint32_t gy, uint32_t n_full) {
-  uint32_t bx, by;
-  fold_tile(n_full + blockIdx.x, gx, gy, &bx, &by);
-  const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
-  if (r >= m) return;
-#pragma unroll 4
-  for (int t = threadIdx.x >> 7; t < 64; t += 2) {
-    const int64_t tok = (int64_t)bx * 64 + t;
-    if (tok < n) y[tok * ldy + r] = 0.0f;
-  }
-}
 
 // =============================================================================================
 // q4_K variant ("r18: Load-time B pre-expansion — staging becomes a bulk copy (W_exp's debut,
@@ -1136,9 +1178,9 @@ struct Q4Src {
 // they are issued at iteration 8s - 3.
 template <int CI8>
 __device__ __forceinline__ void q4_issue(uint8_t* slot, uint8_t* sbuf, const Q4Src& src,
-                                         int64_t ci, int64_t nchunk, int wave, int lane) {
-  const bool live = ci < nchunk;
-  const uint32_t cl = (uint32_t)(live ? ci : nchunk - 1);
+                                         int64_t ci, int64_t c_end, int wave, int lane) {
+  const bool live = ci < c_end;
+  const uint32_t cl = (uint32_t)(live ? ci : c_end - 1);
   const uint32_t l16 = lane * 16;
   bdma16(src.b, l16, cl * 1024, slot + kQ4SlotB + wave * 1024);
   if (wave < kWgTokTiles) bdma16(src.a, l16, cl * 1024, slot + kQ4SlotA + wave * 1024);
@@ -1166,7 +1208,7 @@ struct Q4Ctx {
   uint8_t* smem;
   uint8_t* sbuf;
   Q4Src src;
-  int64_t nchunk, n, m, tok_base, col;
+  int64_t nchunk, c_end, n, m, tok_base, col;
   int32_t* dots;
   uint32_t aa, bb, dd, ss;  // per-lane LDS addresses: A in slot 0, B in slot 0, da and SB (parity 0)
   int wave, lane;
@@ -1189,7 +1231,7 @@ __device__ __forceinline__ void q4_step(const Q4Ctx& k, int64_t s, uint32_t par,
   q4_wait<kQ4Ring - 3>(k.loads_a);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   q4_issue<(CC + kQ4Ring - 1) % 8>(k.smem + ((CC + kQ4Ring - 1) % kQ4Ring) * kQ4Slot, k.sbuf,
-                                   k.src, c + kQ4Ring - 1, k.nchunk, k.wave, k.lane);
+                                   k.src, c + kQ4Ring - 1, k.c_end, k.wave, k.lane);
   constexpr int kS = (CC % kQ4Ring) * kQ4Slot;
   v4i a, b0, b1;
   v4f d0, d1, d2, d3, s0, s1, s2, s3;
@@ -1254,7 +1296,8 @@ template <bool DOTS>
 __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da, const float* __restrict__ das,
     const uint8_t* __restrict__ wcodes, const float* __restrict__ wsb, int64_t n, int64_t m,
-    int64_t nchunk, float* __restrict__ y, int64_t ldy, int32_t* __restrict__ dots) {
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, int32_t* __restrict__ dots, uint32_t gx,
+    uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQ4Ring * kQ4Slot + 2 * kQ4SbBytes];
   Q4Ctx k;
   k.smem = smem;
@@ -1263,10 +1306,11 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
   k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   k.loads_a = k.wave < kWgTokTiles;
   const int tt = k.wave & 1, rp = k.wave >> 1;
-  const int64_t T = (int64_t)blockIdx.x * kWgTokTiles + tt;
-  const int64_t R0 = (int64_t)blockIdx.y * 4;
-  const int64_t Ta = (int64_t)blockIdx.x * kWgTokTiles + (k.loads_a ? k.wave : 0);
   const int64_t nsb = nchunk / 8;
+  const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nsb);
+  const int64_t T = (int64_t)tw.bx * kWgTokTiles + tt;
+  const int64_t R0 = (int64_t)tw.by * 4;
+  const int64_t Ta = (int64_t)tw.bx * kWgTokTiles + (k.loads_a ? k.wave : 0);
   k.src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
   k.src.da = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
   k.src.das = make_rsrc(reinterpret_cast<const uint8_t*>(das) + Ta * nchunk * 128, nchunk * 128);
@@ -1274,6 +1318,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
   k.src.sb = make_rsrc(reinterpret_cast<const uint8_t*>(wsb) + (R0 + k.wave) * nsb * 2048,
                        nsb * 2048);
   k.nchunk = nchunk;
+  k.c_end = 8 * tw.s1;
   k.n = n;
   k.m = m;
   k.dots = dots;
@@ -1294,13 +1339,14 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-  q4_issue<0>(smem + 0 * kQ4Slot, k.sbuf, k.src, 0, nchunk, k.wave, k.lane);
-  q4_issue<1>(smem + 1 * kQ4Slot, k.sbuf, k.src, 1, nchunk, k.wave, k.lane);
-  q4_issue<2>(smem + 2 * kQ4Slot, k.sbuf, k.src, 2, nchunk, k.wave, k.lane);
+  const int64_t c0 = 8 * tw.s0;
+  q4_issue<0>(smem + 0 * kQ4Slot, k.sbuf, k.src, c0 + 0, k.c_end, k.wave, k.lane);
+  q4_issue<1>(smem + 1 * kQ4Slot, k.sbuf, k.src, c0 + 1, k.c_end, k.wave, k.lane);
+  q4_issue<2>(smem + 2 * kQ4Slot, k.sbuf, k.src, c0 + 2, k.c_end, k.wave, k.lane);
   q4_wait<kQ4Ring - 2>(k.loads_a);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  for (int64_t s = 0; s < nsb; ++s) {
+  for (int64_t s = tw.s0; s < tw.s1; ++s) {
     const uint32_t par = (uint32_t)(s & 1) * kQ4SbBytes;
     q4_step<DOTS, 0>(k, s, par, bias, acc);
     q4_step<DOTS, 1>(k, s, par, bias, acc);
@@ -1321,7 +1367,12 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < n) y[tok * ldy + mcol] = acc[u][r];
+      if (tok < n) {
+        if (tw.split)
+          unsafeAtomicAdd(y + tok * ldy + mcol, acc[u][r]);
+        else
+          y[tok * ldy + mcol] = acc[u][r];
+      }
     }
   }
 }
@@ -1377,6 +1428,34 @@ int device_cus() {
   return v;
 }
 
+// Work split of a GEMM launch (see tile_work): n_full whole tiles, then the remaining tiles in
+// `pieces` pieces each; nblocks workgroups in all.
+struct SplitPlan {
+  int64_t n_full, pieces, nblocks;
+};
+
+q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitPlan* sp) {
+  const int cus = device_cus();
+  if (cus <= 0) return Q6K_EHIP;
+  const int64_t ntiles = gx * gy, slots = (int64_t)wg_per_cu * cus;
+  const int64_t rem = ntiles % slots;
+  int64_t pieces = rem ? std::min<int64_t>(slots / rem, nsb) : 1;
+  if (pieces < 2) pieces = 1;
+  sp->n_full = pieces > 1 ? ntiles - rem : ntiles;
+  sp->pieces = pieces;
+  sp->nblocks = sp->n_full + (ntiles - sp->n_full) * pieces;
+  return sp->nblocks > INT32_MAX ? Q6K_ESIZE : Q6K_OK;
+}
+
+// Zero y over the tiles that the plan splits (none if nothing is split).
+void zero_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, float* y, int64_t ldy,
+                      int64_t n, int64_t m, hipStream_t s) {
+  const int64_t nsplit = gx * gy - sp.n_full;
+  if (nsplit > 0)
+    hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)nsplit), dim3(256), 0, s, y, ldy, n, m,
+                       (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full);
+}
+
 q6k_status launch_status() {
   return hipGetLastError() == hipSuccess ? Q6K_OK : Q6K_EHIP;
 }
@@ -1395,6 +1474,8 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   // layout 2 addresses a row tile's digit planes (k/32 * 2048 bytes) through one 32-bit buffer
   // range
   if (layout == Q6K_LAYOUT_FOLDED && k / 32 * 2048 > INT32_MAX) return Q6K_ESIZE;
+  // layouts 0 and 1 address a tile's activations or codes (k/32 * 1024 bytes) likewise
+  if (layout != Q6K_LAYOUT_FOLDED && k / 32 * 1024 > INT32_MAX) return Q6K_ESIZE;
   if (n == 0 || m == 0) return Q6K_OK;
   if (!xq || !da || !w) return Q6K_EINVAL;
   if (!aligned16(xq) || !aligned16(da) || !aligned16(w)) return Q6K_EALIGN;
@@ -1416,33 +1497,25 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   const uint8_t* ws = wc + codes_bytes;
   const uint8_t* a = static_cast<const uint8_t*>(xq);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)gx, (unsigned)gy), block(256);
   constexpr bool kDots = OUT != kOutY;
+  SplitPlan sp;
+  const int wg_per_cu = layout == Q6K_LAYOUT_FOLDED ? Q6K_FOLDED_WG_PER_CU : Q6K_WG_PER_CU;
+  const q6k_status plan = plan_split(gx, gy, wg_per_cu, k / 256, &sp);
+  if (plan != Q6K_OK) return plan;
+  if (OUT == kOutY) zero_split_tiles(sp, gx, gy, y, ldy, n, m, s);
+  const dim3 grid((unsigned)sp.nblocks), block(256);
+  const uint32_t gx32 = (uint32_t)gx, gy32 = (uint32_t)gy, nf = (uint32_t)sp.n_full,
+                 pc = (uint32_t)sp.pieces;
   if (layout == Q6K_LAYOUT_FOLDED) {
     const int vec_store = OUT == kOutY && aligned16(y) && ldy % 4 == 0;
-    // deal the tiles out in rounds of one per workgroup slot; split the tiles of a partial last
-    // round along k so that its pieces fill the slots
-    const int cus = device_cus();
-    if (cus <= 0) return Q6K_EHIP;
-    const int64_t ntiles = gx * gy, slots = (int64_t)Q6K_FOLDED_WG_PER_CU * cus;
-    const int64_t rem = ntiles % slots;
-    int64_t pieces = rem ? std::min<int64_t>(slots / rem, k / 256) : 1;
-    if (pieces < 2) pieces = 1;
-    const int64_t n_full = pieces > 1 ? ntiles - rem : ntiles;
-    const int64_t nblocks = n_full + (ntiles - n_full) * pieces;
-    if (nblocks > INT32_MAX) return Q6K_ESIZE;
-    if (OUT == kOutY && n_full < ntiles)
-      hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)(ntiles - n_full)), dim3(256), 0, s, y,
-                         ldy, n, m, (uint32_t)gx, (uint32_t)gy, (uint32_t)n_full);
-    hipLaunchKernelGGL((folded_kernel<kDots>), dim3((unsigned)nblocks), block, 0, s, a, da, wc,
-                       ws, n, m, nchunk, y, ldy, vec_store, dots, (uint32_t)gx, (uint32_t)gy,
-                       (uint32_t)n_full, (uint32_t)pieces);
+    hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, ws, n, m, nchunk, y,
+                       ldy, vec_store, dots, gx32, gy32, nf, pc);
   } else if (layout == Q6K_LAYOUT_EXPANDED) {
     hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_EXPANDED, kDots>), grid, block, 0, s, a, da, wc,
-                       ws, n, m, nchunk, y, ldy, dots);
+                       ws, n, m, nchunk, y, ldy, dots, gx32, gy32, nf, pc);
   } else {
     hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_PACKED, kDots>), grid, block, 0, s, a, da, wc, ws,
-                       n, m, nchunk, y, ldy, dots);
+                       n, m, nchunk, y, ldy, dots, gx32, gy32, nf, pc);
   }
   const q6k_status st = launch_status();
   if (st == Q6K_OK) g_launches[layout].fetch_add(1, std::memory_order_relaxed);
@@ -1500,9 +1573,15 @@ q6k_status q4k_gemm_common(const void* xq, const float* da, const float* das, in
   // the test export reads no scales: point them at the codes, which are never dereferenced as such
   const float* dap = DOTS ? reinterpret_cast<const float*>(xq) : da;
   const float* dasp = DOTS ? reinterpret_cast<const float*>(xq) : das;
-  hipLaunchKernelGGL((q4k_gemm_kernel<DOTS>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(xq), dap, dasp,
-                     wc, ws, n, m, nchunk, y, ldy, dots);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SplitPlan sp;
+  const q6k_status plan = plan_split(gx, gy, Q4K_WG_PER_CU, k / 256, &sp);
+  if (plan != Q6K_OK) return plan;
+  if (!DOTS) zero_split_tiles(sp, gx, gy, y, ldy, n, m, s);
+  hipLaunchKernelGGL((q4k_gemm_kernel<DOTS>), dim3((unsigned)sp.nblocks), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(xq), dap, dasp, wc, ws, n, m, nchunk, y, ldy,
+                     dots, (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full,
+                     (uint32_t)sp.pieces);
   const q6k_status st = launch_status();
   if (st == Q6K_OK) g_q4k_launches.fetch_add(1, std::memory_order_relaxed);
   return st;
