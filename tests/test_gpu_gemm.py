@@ -283,3 +283,31 @@ def test_folded_split_k_pieces(n, m, k):
     ok, worst = gpu_util.within_tolerance(y[rows], y_ref, t_ref)
     assert ok, f"worst |err|/T = {worst}"
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("ldy", [4094, 4097, 4100])
+def test_gemm_whole_tiles_ragged_rows(layout, ldy):
+    """Enough tiles (1664) that most are computed whole, with m not a multiple of 4 and leading
+    dimensions that do (4100) and do not (4094, 4097) allow 16-byte stores: every store path of
+    the epilogues (vector, scalar, partial last row group, and the split pieces of layout 2), with
+    the columns past m untouched."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 3314, 4094, 512
+    print(f"whole tiles layout={layout} ldy={ldy}", flush=True)
+    raw = synthetic.weights(m, k, seed=ldy, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=ldy + 1, kind="outlier")
+    xq, da, w = prepare(x, raw, m, layout)
+    y = torch.full((n, ldy), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+    q6k.q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=ldy)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.isnan(y[:, m:]).all()
+    rows = sampled_tokens(n, 16, seed=ldy)
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y[rows, :m], y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
+    assert np.isfinite(y[:, :m]).all()
