@@ -5,12 +5,13 @@ One step = one pass of the hot path over one batch: the activation quantize-tran
 (q6k_expand_weights, outside the timed region).  Inputs are synthetic, seeded, and resident in HBM
 before timing starts.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1|2] [--workload NAME]
                     [--weights q6k|q4k] [--cold] [--swiglu] [--no-cpu-baseline]
                     [--copy-probe-mib MIB]
 
-Workloads: tiny, attn_v_n512, attn_v_n3314, ffn_down_n3314 (the default and headline case), and
-sweep32: 32 layers of (attn_v 4096x4096 + ffn_down 4096x11008) at 3314 tokens, 64 GEMMs back to
+Workloads: tiny, attn_v_n512, attn_v_n3314, ffn_down_n3314 (the default and headline case),
+ffn_down_shard8 (3314 x 512 x 11008: one GPU's share of ffn_down under an 8-way split of the
+output rows), and sweep32: 32 layers of (attn_v 4096x4096 + ffn_down 4096x11008) at 3314 tokens, 64 GEMMs back to
 back on one stream over 1.6 GB of raw weights, inputs drawn on the device.  --cold writes a
 512 MiB scrub buffer before every timed step, so weights and activations come from HBM rather
 than the 256 MB Infinity Cache.  --swiglu (single workloads) replaces the prepass by the fused
@@ -327,6 +328,8 @@ def main():
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
         "gemm": {"avg_us": round(float(gemm_us.mean()), 2),
                  "min_us": round(float(gemm_us.min()), 2),
+                 "p10_p50_p90_us_per_step": [round(float(v), 2) for v in
+                                             np.percentile(gemm_us.sum(axis=1), [10, 50, 90])],
                  "total_us_per_step": round(gemm_total_us, 2),
                  "tops": round(gemm_tops, 2), "us_per_gmac": round(gemm_total_us / gmac, 4),
                  "pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),

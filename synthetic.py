@@ -19,6 +19,8 @@ WORKLOADS = {
     "attn_v_n512": dict(n=512, m=4096, k=4096, seed=2, x="normal"),
     "attn_v_n3314": dict(n=3314, m=4096, k=4096, seed=3, x="outlier"),
     "ffn_down_n3314": dict(n=3314, m=4096, k=11008, seed=4, x="swiglu"),
+    # one GPU's share of ffn_down under an 8-way split of the output rows (M / 8 = 512)
+    "ffn_down_shard8": dict(n=3314, m=512, k=11008, seed=5, x="swiglu"),
 }
 
 

@@ -173,7 +173,7 @@ def sampled_tokens(n, count, seed):
     return np.array(sorted(idx))
 
 
-@pytest.mark.parametrize("name", ["attn_v_n512", "attn_v_n3314", "ffn_down_n3314"])
+@pytest.mark.parametrize("name", ["attn_v_n512", "attn_v_n3314", "ffn_down_n3314", "ffn_down_shard8"])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_gemm_full_size_sampled(name, layout):
     """Full workload shape, the benchmark's launch configuration; every row of W checked for a
