@@ -132,3 +132,31 @@ def test_gemm_full_size_sampled_and_liveness():
     err = np.abs(y[rows].astype(np.float64) - y_ref)
     assert (err <= 1e-3 * t_ref).all(), float((err / np.maximum(t_ref, 1e-300)).max())
     assert np.isfinite(y).all()
+
+
+def test_split_k_pieces():
+    """128 output tiles on a 768-slot device are all split along k, here 10 super-blocks over 6
+    pieces of unequal length: the integer dots stay bit-exact and the outputs within tolerance,
+    checked on a sample of tokens."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 1024, 1024, 2560
+    print(f"q4k split-k pieces n={n} m={m} k={k}", flush=True)
+    raw = synthetic.weights_q4k(m, k, seed=77)
+    x = synthetic.activations(n, k, seed=78, kind="outlier")
+    xq, da, das = prep_acts(x)
+    w = prep_weights(raw, m, k)
+    rows = np.array(sorted(set(np.random.default_rng(3).choice(n, 9, replace=False).tolist())
+                           | {0, n - 1, n // 2}))
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    dots = torch.full((n, m, k // 32), -7, dtype=torch.int32, device=gpu_util.DEV)
+    q6k.q4k_gemm_dots(xq, n, w, m, k, dots)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dots.cpu().numpy()[rows], oracle.q4_chunkdots(xq_ref, raw, m))
+    del dots
+    y = run_gemm(xq, da, das, n, w, m, k)
+    y_ref, t_ref = oracle.q4_gemm(xq_ref, da_ref, raw, m)
+    err = np.abs(y[rows].astype(np.float64) - y_ref)
+    assert (err <= 1e-3 * t_ref).all(), float((err / np.maximum(t_ref, 1e-300)).max())
+    assert np.isfinite(y).all()
