@@ -73,10 +73,13 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
                                                            const float* __restrict__ up,
                                                            int64_t n, int64_t ldx, int64_t nchunk,
                                                            uint8_t* __restrict__ xq,
-                                                           float* __restrict__ da) {
+                                                           float* __restrict__ da, int64_t t0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t T = blockIdx.x;
-  const int64_t c = (int64_t)blockIdx.y * 8 + (lane >> 3);  // this lane's chunk
+  // workgroup order: the 8-chunk block of k varies fastest, so workgroups running together read
+  // consecutive kilobytes of the same rows (sequential DRAM streams) rather than 1 KiB pieces of
+  // rows 44 KB apart
+  const int64_t T = t0 + blockIdx.y, kb = blockIdx.x;
+  const int64_t c = kb * 8 + (lane >> 3);  // this lane's chunk
   const int kk = 4 * (lane & 7);                             // its first k inside the chunk
   const bool live_c = c < nchunk;
   // place of the lane's 4 codes in the chunk's 1 KiB block: slot p + 32*g, byte 8*h + kk % 8
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
   // coalesced stores: thread t writes 32 bytes of chunk t / 32's 1 KiB block; threads 0..63 the
   // 8 x 32 scales
   const int t = threadIdx.x;
-  const int64_t ct = (int64_t)blockIdx.y * 8 + (t >> 5);
+  const int64_t ct = kb * 8 + (t >> 5);
   if (ct < nchunk) {
     const uint4* srcq = reinterpret_cast<const uint4*>(codes + t * 32);
     uint4* dstq = reinterpret_cast<uint4*>(xq + (T * nchunk + ct) * 64 * kFragBytes + (t & 31) * 32);
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
     dstq[1] = srcq[1];
   }
   if (t < 64) {
-    const int64_t cd = (int64_t)blockIdx.y * 8 + (t >> 3);
+    const int64_t cd = kb * 8 + (t >> 3);
     if (cd < nchunk)
       reinterpret_cast<float4*>(da + (T * nchunk + cd) * 32)[t & 7] =
           reinterpret_cast<const float4*>(scales)[t];
@@ -1536,11 +1539,14 @@ q6k_status quantize_common(const float* x, const float* up, int64_t n, int64_t k
   if (xq_bytes < need_x || da_bytes < need_d) return Q6K_ESIZE;
   const int64_t np = round_up(n, kWgTok);
   const int64_t nchunk = k / 32;
-  const int64_t gx = np / kTile, gy = (nchunk + 7) / 8;
-  if (gx > INT32_MAX || gy > 65535) return Q6K_ESIZE;
-  hipLaunchKernelGGL(quantize_act_kernel<SWIGLU>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), x, up, n, ldx, nchunk,
-                     static_cast<uint8_t*>(xq), da);
+  const int64_t ntt = np / kTile, nkb = (nchunk + 7) / 8;
+  if (nkb > INT32_MAX) return Q6K_ESIZE;
+  // grid x = 8-chunk blocks of k, y = token tiles (at most 65535 per launch)
+  for (int64_t t0 = 0; t0 < ntt; t0 += 65535)
+    hipLaunchKernelGGL(quantize_act_kernel<SWIGLU>,
+                       dim3((unsigned)nkb, (unsigned)std::min<int64_t>(65535, ntt - t0)),
+                       dim3(256), 0, static_cast<hipStream_t>(stream), x, up, n, ldx, nchunk,
+                       static_cast<uint8_t*>(xq), da, t0);
   return launch_status();
 }
 
