@@ -55,7 +55,8 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // tokens 8w .. 8w+7 of the tile; per token its 64 lanes read the 1 KiB of those 256 values with
 // one coalesced 16-byte load each (lane l holds k 4l .. 4l+3 of the window, chunk l / 8).  The 8
 // lanes of a chunk exchange their maxima (da = amax / 127, IEEE f32), each quantizes its four
-// values (q = roundf(x / da), correctly rounded f32 division, clamped to +-127) and puts them, as
+// values (q = roundf(x / da) on the correctly rounded f32 quotient, clamped to +-127; see
+// quant_code for how the division is avoided without changing any result) and puts them, as
 // one 4-byte word, at their place of the tiled layout in LDS; the block then writes its eight
 // 1 KiB code blocks and 1 KiB of scales with coalesced 16-byte stores.
 // With SWIGLU the input value is produced on the fly from two rows, h = up * silu(gate), so that
@@ -67,6 +68,24 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // infinity for very negative g and gives a signed zero).  The test export computes h with this
 // same function.
 __device__ __forceinline__ float swiglu_f32(float g, float u) { return u * (g / (1.0f + expf(-g))); }
+
+// q = roundf(x / s) with the correctly rounded f32 quotient (ties away from zero), clamped to
+// [-127, 127], without a full division in the common case.  r = rcp(s) is within 1 ulp of 1/s,
+// so y = x * r is within 2 ulps of the quotient (< 2^-15 absolute for |x / s| <= 127.5); when y
+// is farther than 2^-12 from a half-integer, the rounded quotient and y round to the same
+// integer and neither is a tie, so rint(y) is the result.  Near a half-integer, or when s lies
+// outside [2^-100, 2^100] (subnormal or huge scales, whose reciprocal may lose precision), the
+// exact division decides.  A NaN x gives a NaN q on both paths.
+__device__ __forceinline__ int quant_code(float x, float s, float r, bool fast) {
+  const float y = x * r;
+  const float yr = __builtin_rintf(y);
+  float q;
+  if (fast && !(fabsf(y - yr) > 0.5f - 0x1p-12f))
+    q = yr;
+  else
+    q = roundf(x / s);
+  return (int)fminf(fmaxf(q, -127.0f), 127.0f);
+}
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x,
@@ -117,10 +136,12 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
     const float scale = amax / 127.0f;
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
     if (scale != 0.0f) {
-      q0 = (int)fminf(fmaxf(roundf(v[j].x / scale), -127.0f), 127.0f);
-      q1 = (int)fminf(fmaxf(roundf(v[j].y / scale), -127.0f), 127.0f);
-      q2 = (int)fminf(fmaxf(roundf(v[j].z / scale), -127.0f), 127.0f);
-      q3 = (int)fminf(fmaxf(roundf(v[j].w / scale), -127.0f), 127.0f);
+      const float r = __builtin_amdgcn_rcpf(scale);
+      const bool fast = scale >= 0x1p-100f && scale <= 0x1p100f;
+      q0 = quant_code(v[j].x, scale, r, fast);
+      q1 = quant_code(v[j].y, scale, r, fast);
+      q2 = quant_code(v[j].z, scale, r, fast);
+      q3 = quant_code(v[j].w, scale, r, fast);
     }
     // stage the tile's codes and scales in LDS in their global order
     *reinterpret_cast<uint32_t*>(codes + (lane >> 3) * 1024 + (p + 32 * g) * kFragBytes + 8 * h +

@@ -56,3 +56,29 @@ def test_prepass_special_values():
 def test_prepass_full_size(name):
     import gpu_util
     check(gpu_util.cached_workload(name)[1])
+
+
+def test_prepass_near_ties():
+    """Values whose quotient x / da lies within a few ulps of a half-integer, on either side and
+    exactly on it, for scales that are not powers of two: the codes must still be those of
+    roundf on the correctly rounded quotient (the kernel's fast reciprocal path must hand every
+    such value to the exact division)."""
+    rng = np.random.default_rng(11)
+    n, k = 64, 2048
+    x = np.zeros((n, k), np.float32)
+    for t in range(n):
+        for c in range(k // 32):
+            amax = np.float32(rng.uniform(0.5, 4.0) * 10.0 ** rng.integers(-20, 20))
+            da = np.float32(amax / np.float32(127.0))
+            row = np.empty(32, np.float32)
+            row[0] = amax
+            for i in range(1, 32):
+                j = rng.integers(0, 127)
+                target = np.float32((j + 0.5) * np.float64(da))
+                steps = int(rng.integers(-3, 4))
+                v = target
+                for _ in range(abs(steps)):
+                    v = np.nextafter(v, np.float32(np.inf if steps > 0 else -np.inf), dtype=np.float32)
+                row[i] = v if rng.integers(0, 2) else -v
+            x[t, 32 * c: 32 * c + 32] = row
+    check(x)
