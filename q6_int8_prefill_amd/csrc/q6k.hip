@@ -54,7 +54,7 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // Prepass.  Block = 4 waves = one token tile (32 tokens) x 8 chunks (256 k values).  Wave w walks
 // tokens 8w .. 8w+7 of the tile; per token its 64 lanes read the 1 KiB of those 256 values with
 // one coalesced 16-byte load each (lane l holds k 4l .. 4l+3 of the window, chunk l / 8).  The 8
-// lanes of a chunk exchange their maxima (da = amax / 127, IEEE f32), each quantizes its four
+// lanes of a chunk exchange their maxima through DPP moves (da = amax / 127, IEEE f32), each quantizes its four
 // values (q = roundf(x / da) on the correctly rounded f32 quotient, clamped to +-127; see
 // quant_code for how the division is avoided without changing any result) and puts them, as
 // one 4-byte word, at their place of the tiled layout in LDS; the block then writes its eight
@@ -68,6 +68,13 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // infinity for very negative g and gives a signed zero).  The test export computes h with this
 // same function.
 __device__ __forceinline__ float swiglu_f32(float g, float u) { return u * (g / (1.0f + expf(-g))); }
+
+// A lane's neighbour value through a DPP move (no LDS traffic); CTRL is the DPP control code.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, true));
+}
 
 // q = roundf(x / s) with the correctly rounded f32 quotient (ties away from zero), clamped to
 // [-127, 127], without a full division in the common case.  r = rcp(s) is within 1 ulp of 1/s,
@@ -130,9 +137,9 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
   for (int j = 0; j < 8; ++j) {
     const int p = 8 * wave + j;
     float amax = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    amax = fmaxf(amax, dpp_f32<0xB1>(amax));   // lane ^ 1 (quad_perm 1,0,3,2)
+    amax = fmaxf(amax, dpp_f32<0x4E>(amax));   // lane ^ 2 (quad_perm 2,3,0,1)
+    amax = fmaxf(amax, dpp_f32<0x141>(amax));  // the other quad of the 8 (row_half_mirror)
     const float scale = amax / 127.0f;
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
     if (scale != 0.0f) {
