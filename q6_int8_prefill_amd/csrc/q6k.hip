@@ -437,8 +437,6 @@ struct RingSize {
   static constexpr int value = fit > 6 ? 6 : fit;
   static_assert(value >= 3, "the ring needs at least 3 slots");
 };
-// direct-to-LDS load instructions per chunk: waves 0, 1 load A, da, B, d*sc; waves 2, 3 B, d*sc
-__device__ __forceinline__ constexpr int loads_per_chunk(bool loads_a) { return loads_a ? 4 : 2; }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
