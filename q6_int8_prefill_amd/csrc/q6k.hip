@@ -369,18 +369,24 @@ __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_
   return w;
 }
 
-// Zero y over the tiles that a GEMM splits along k (tiles n_full .. gx*gy-1 of the tile order),
-// one workgroup per tile.
+// Zero y over the tiles that a GEMM splits along k (tiles n_full .. gx*gy-1 of the GEMM's tile
+// order, XCD-aware or plain), one workgroup per tile of tile_tok tokens x 128 rows.
 __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, int64_t ldy,
                                                       int64_t n, int64_t m, uint32_t gx,
-                                                      uint32_t gy, uint32_t n_full) {
+                                                      uint32_t gy, uint32_t n_full,
+                                                      uint32_t tile_tok, int xcd_order) {
   uint32_t bx, by;
-  tile_of(n_full + blockIdx.x, gx, gy, &bx, &by);
+  const uint32_t t = n_full + blockIdx.x;
+  if (xcd_order) {
+    tile_of(t, gx, gy, &bx, &by);
+  } else {
+    bx = t % gx;
+    by = t / gx;
+  }
   const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
   if (r >= m) return;
-#pragma unroll 4
-  for (int t = threadIdx.x >> 7; t < 64; t += 2) {
-    const int64_t tok = (int64_t)bx * 64 + t;
+  for (uint32_t i = threadIdx.x >> 7; i < tile_tok; i += 2) {
+    const int64_t tok = (int64_t)bx * tile_tok + i;
     if (tok < n) y[tok * ldy + r] = 0.0f;
   }
 }
@@ -731,14 +737,18 @@ __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, cons
 // Work split: tile_work (rounds of one tile per workgroup slot, a partial last round split along
 // k into pieces that add into y).
 // ---------------------------------------------------------------------------------------------
-#ifndef Q6K_FOLDED_WG_PER_CU
-#define Q6K_FOLDED_WG_PER_CU 2
-#endif
-constexpr int kFSlotDa = 16384;  // after 2 tiles x 8 chunks x 1 KiB of activations
-constexpr int kFSlot = 18432;
+// Waves per workgroup.  The kernel is written for 4 (64 tokens x 128 rows, 2 workgroups per CU)
+// or 8 (128 x 128, 1 per CU, two waves reading each row tile's planes); 8 measured 1 % faster on
+// ffn_down and 12 % slower on attn_v N=512, so 4 it is.
+constexpr int kFWaves = 4;
+static_assert(kFWaves == 4 || kFWaves == 8, "4 or 8 waves");
+constexpr int kFoldedWgPerCu = 8 / kFWaves;
+constexpr int kFTok = kFWaves / 2;         // token tiles per workgroup (2 per wave row)
+constexpr int kFSlotDa = kFTok * 8192;     // after kFTok tiles x 8 chunks x 1 KiB of activations
+constexpr int kFSlot = kFTok * 9216;
 constexpr int kFRing = 4;
 constexpr int kFAhead = 3;  // super-blocks whose activations are in flight
-static_assert(Q6K_FOLDED_WG_PER_CU * kFRing * kFSlot <= 160 * 1024, "LDS budget");
+static_assert(kFoldedWgPerCu * kFRing * kFSlot <= 160 * 1024, "LDS budget");
 static_assert(kFAhead < kFRing, "ring slot reuse");
 
 struct FoldCtx {
@@ -799,12 +809,12 @@ __device__ __forceinline__ void fold_load_d(const FoldCtx& k, int64_t s, float (
 }
 
 // This wave's share of super-block s's activations and da, direct to LDS slot s % 4: four 1 KiB
-// chunk tiles of token tile wave/2 and the da of token tile wave%2 (waves 2 and 3 write the same
-// da bytes as waves 0 and 1).  Nothing is loaded past the piece's last super-block.
+// chunk tiles of token tile wave/2 and the da of token tile wave % kFTok (the other waves write
+// the same da bytes again).  Nothing is loaded past the piece's last super-block.
 __device__ __forceinline__ void fold_dma(const FoldCtx& k, int64_t s) {
   if ((uint32_t)s >= k.s_end) return;
   uint8_t* slot = k.smem + (s % kFRing) * kFSlot;
-  const int u = k.wave >> 1, j0 = 4 * (k.wave & 1), ud = k.wave & 1;
+  const int u = k.wave >> 1, j0 = 4 * (k.wave & 1), ud = k.wave % kFTok;
   const uint32_t abase = (uint32_t)((u * k.nchunk + 8 * s + j0) * 1024);
 #pragma unroll
   for (int i = 0; i < 4; ++i) bdma16(k.a, k.l16, abase + i * 1024, slot + u * 8192 + (j0 + i) * 1024);
@@ -925,7 +935,7 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
 }
 
 template <bool DOTS>
-__global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
+__global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
     int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
@@ -942,9 +952,11 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   k.lane = threadIdx.x & 63;
   k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p = k.lane & 31, g = k.lane >> 5;
-  const int64_t T0 = (int64_t)bx * kWgTokTiles, R = (int64_t)by * 4 + k.wave;
-  k.a = make_rsrc(xq + T0 * nchunk * 1024, 2 * nchunk * 1024);
-  k.da = make_rsrc(reinterpret_cast<const uint8_t*>(da) + T0 * nchunk * 128, 2 * nchunk * 128);
+  const int rw = k.wave & 3, tp = k.wave >> 2;  // the wave's row tile and token-tile pair
+  const int64_t T0 = (int64_t)bx * kFTok, R = (int64_t)by * 4 + rw;
+  k.a = make_rsrc(xq + T0 * nchunk * 1024, kFTok * nchunk * 1024);
+  k.da = make_rsrc(reinterpret_cast<const uint8_t*>(da) + T0 * nchunk * 128,
+                   kFTok * nchunk * 128);
   k.b = make_rsrc(wcodes + R * nchunk * 2048, nchunk * 2048);
   k.w = make_rsrc(wd + R * nsb * 128, nsb * 128);
   k.l16 = k.lane * 16;
@@ -955,14 +967,14 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
   k.s_end = (uint32_t)s1;
   k.n = n;
   k.m = m;
-  k.tok0 = T0 * kTile + p;
+  k.tok0 = (T0 + 2 * tp) * kTile + p;
   k.row0 = R * kTile;
   k.dots = dots;
   // this lane's LDS addresses in slot 0: its 16 activation bytes, its token's da
   // (da of token p sits at position 16*((p/4)%2) + 4*(p/8) + p%4 of a chunk's 32 floats)
-  const uint32_t xb0 = lds_addr(smem) + k.l16;
-  const uint32_t db0 =
-      lds_addr(smem) + kFSlotDa + 4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
+  const uint32_t xb0 = lds_addr(smem) + 2 * tp * 8192 + k.l16;
+  const uint32_t db0 = lds_addr(smem) + kFSlotDa + 2 * tp * 1024 +
+                       4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
 
   v16i bias;
 #pragma unroll
@@ -1016,18 +1028,18 @@ __global__ __launch_bounds__(256, Q6K_FOLDED_WG_PER_CU) void folded_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[u][r] = __builtin_fmaf(st.sb[u][r], st.d[r], st.acc[u][r]);
 
-  // The workgroup's 64-token x 128-row output tile goes through LDS (the ring is free once every
-  // wave has passed the first barrier), so that each store or atomic instruction below covers
-  // consecutive rows of one token instead of 64 scattered 4-row pieces.
+  // The workgroup's (32 kFTok)-token x 128-row output tile goes through LDS (the ring is free once
+  // every wave has passed the first barrier), so that each store or atomic instruction below
+  // covers consecutive rows of one token instead of 64 scattered 4-row pieces.
   constexpr int kOutLd = 132;  // floats per token in LDS: 128 rows + 4 of padding
-  static_assert(64 * kOutLd * 4 <= kFRing * kFSlot, "output tile fits the ring");
+  static_assert(kTile * kFTok * kOutLd * 4 <= kFRing * kFSlot, "output tile fits the ring");
   float* out = reinterpret_cast<float*>(smem);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(out + (kTile * u + p) * kOutLd + kTile * k.wave + 8 * q + 4 * g) =
+      *reinterpret_cast<float4*>(out + (kTile * (2 * tp + u) + p) * kOutLd + kTile * rw + 8 * q + 4 * g) =
           make_float4(st.acc[u][4 * q], st.acc[u][4 * q + 1], st.acc[u][4 * q + 2],
                       st.acc[u][4 * q + 3]);
   __syncthreads();
@@ -1476,13 +1488,16 @@ q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitP
   return sp->nblocks > INT32_MAX ? Q6K_ESIZE : Q6K_OK;
 }
 
-// Zero y over the tiles that the plan splits (none if nothing is split).
-void zero_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, float* y, int64_t ldy,
-                      int64_t n, int64_t m, hipStream_t s) {
+// Zero y over the tiles that the plan splits (none if nothing is split), in the same tile order
+// and tile height (tokens) as the GEMM that follows.
+void zero_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, int64_t tile_tok,
+                      bool xcd_order, float* y, int64_t ldy, int64_t n, int64_t m,
+                      hipStream_t s) {
   const int64_t nsplit = gx * gy - sp.n_full;
   if (nsplit > 0)
     hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)nsplit), dim3(256), 0, s, y, ldy, n, m,
-                       (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full);
+                       (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full, (uint32_t)tile_tok,
+                       xcd_order ? 1 : 0);
 }
 
 q6k_status launch_status() {
@@ -1517,8 +1532,10 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
     if (((uintptr_t)y & 3) != 0) return Q6K_EALIGN;
   }
   const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
-  const int64_t gx = np / (kTile * 2), gy = mp / kWgRow;
-  if (gy > 65535 || gx > INT32_MAX) return Q6K_ESIZE;
+  // output tiles of tile_tok tokens x 128 rows
+  const int64_t tile_tok = layout == Q6K_LAYOUT_FOLDED ? kTile * kFTok : kTile * kWgTokTiles;
+  const int64_t gx = np / tile_tok, gy = mp / kWgRow;
+  if (gy > INT32_MAX || gx > INT32_MAX) return Q6K_ESIZE;
   const int64_t nchunk = k / 32;
   size_t codes_bytes, scales_bytes;
   weight_sizes(m, k, layout, &codes_bytes, &scales_bytes);
@@ -1528,11 +1545,14 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   hipStream_t s = static_cast<hipStream_t>(stream);
   constexpr bool kDots = OUT != kOutY;
   SplitPlan sp;
-  const int wg_per_cu = layout == Q6K_LAYOUT_FOLDED ? Q6K_FOLDED_WG_PER_CU : Q6K_WG_PER_CU;
+  const int wg_per_cu = layout == Q6K_LAYOUT_FOLDED ? kFoldedWgPerCu : Q6K_WG_PER_CU;
   const q6k_status plan = plan_split(gx, gy, wg_per_cu, k / 256, &sp);
   if (plan != Q6K_OK) return plan;
-  if (OUT == kOutY) zero_split_tiles(sp, gx, gy, y, ldy, n, m, s);
-  const dim3 grid((unsigned)sp.nblocks), block(256);
+  if (OUT == kOutY)
+    zero_split_tiles(sp, gx, gy, tile_tok, layout == Q6K_LAYOUT_FOLDED || Q6K_GEMM01_XCD_ORDER, y,
+                     ldy, n, m, s);
+  const dim3 grid((unsigned)sp.nblocks),
+      block(layout == Q6K_LAYOUT_FOLDED ? 64 * kFWaves : 256);
   const uint32_t gx32 = (uint32_t)gx, gy32 = (uint32_t)gy, nf = (uint32_t)sp.n_full,
                  pc = (uint32_t)sp.pieces;
   if (layout == Q6K_LAYOUT_FOLDED) {
@@ -1609,7 +1629,7 @@ q6k_status q4k_gemm_common(const void* xq, const float* da, const float* das, in
   SplitPlan sp;
   const q6k_status plan = plan_split(gx, gy, Q4K_WG_PER_CU, k / 256, &sp);
   if (plan != Q6K_OK) return plan;
-  if (!DOTS) zero_split_tiles(sp, gx, gy, y, ldy, n, m, s);
+  if (!DOTS) zero_split_tiles(sp, gx, gy, kTile * kWgTokTiles, true, y, ldy, n, m, s);
   hipLaunchKernelGGL((q4k_gemm_kernel<DOTS>), dim3((unsigned)sp.nblocks), dim3(256), 0, s,
                      static_cast<const uint8_t*>(xq), dap, dasp, wc, ws, n, m, nchunk, y, ldy,
                      dots, (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full,

@@ -311,3 +311,25 @@ def test_gemm_whole_tiles_ragged_rows(layout, ldy):
     ok, worst = gpu_util.within_tolerance(y[rows, :m], y_ref, t_ref)
     assert ok, f"worst |err|/T = {worst}"
     assert np.isfinite(y[:, :m]).all()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_partly_split_grid(layout):
+    """2176 x 4096 outputs: 1088 tiles of 64 x 128 (544 of 128 x 128), more than one round of
+    workgroup slots with a short last round, so some tiles are computed whole and the rest are
+    split along k, zeroed first and added into; the zeroing must hit exactly the split tiles of
+    the GEMM's own tile order (every output is checked finite, sampled tokens against the
+    oracle)."""
+    import gpu_util
+    n, m, k = 2176, 4096, 512
+    print(f"partly split grid layout={layout}", flush=True)
+    raw = synthetic.weights(m, k, seed=55, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=56, kind="outlier")
+    xq, da, w = prepare(x, raw, m, layout)
+    y = gpu_util.gemm(xq, da, n, w, layout, m, k)
+    assert np.isfinite(y).all()
+    rows = sampled_tokens(n, 24, seed=57)
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+    ok, worst = gpu_util.within_tolerance(y[rows], y_ref, t_ref)
+    assert ok, f"worst |err|/T = {worst}"
