@@ -392,13 +392,15 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
 }
 
 // ---------------------------------------------------------------------------------------------
-// GEMM.  Workgroup = 4 waves = 64 tokens (token tiles 2*bx, 2*bx+1) x 128 weight rows (row tiles
-// 4*by .. 4*by+3).  Wave w computes token tile w%2 against row tiles 2*(w/2) and 2*(w/2)+1: two
-// 32x32 output tiles, 32 f32 accumulators per lane.
+// GEMM on layouts 0 and 1.  Workgroup = 4 waves = one output tile of 64 tokens (token tiles 2*bx,
+// 2*bx+1) x 128 weight rows (row tiles 4*by .. 4*by+3), over the k-range tile_work gives it.
+// Wave w computes token tile w%2 against row tiles 2*(w/2) and 2*(w/2)+1: two 32x32 output
+// tiles, 32 f32 accumulators per lane.
 //
 // Staging: a ring of kRing LDS slots, one 32-k chunk of the workgroup's operands per slot.  Each
-// wave fills its share of a slot with gfx950 direct global->LDS loads (global_load_lds_dwordx4,
-// 16 bytes per lane, no registers): row tile w's weight codes and d*sc, and, for waves 0 and 1,
+// wave fills its share of a slot with gfx950 direct-to-LDS loads through buffer resources
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane, no registers): row tile w's weight codes and
+// d*sc, and, for waves 0 and 1,
 // token tile w's activations and da.  Loads run kRing-1 chunks ahead of the compute.  Per chunk c
 // a wave waits for its own loads of chunk c+1 (s_waitcnt vmcnt), layout 0 expands its row tile's
 // 6-bit codes of chunk c+1 into centered int8 and forms d*sc in the slot, one workgroup barrier
