@@ -57,7 +57,10 @@ q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, f
 
 /* The GEMM: y[t][j] = sum over chunks c of da*(d*sc)*D - (dmin*m)*das, D the exact int32 dot of
  * the int8 activations with the 4-bit codes over the chunk.  y f32 [n][ldy], ldy >= m, 4-byte
- * aligned; xq, da, das, w 16-byte aligned and of the sizes above; k <= 2^25. */
+ * aligned; xq, da, das, w 16-byte aligned and of the sizes above; k < 2^26 (Q6K_ESIZE
+ * otherwise).  As for q6k_gemm, output tiles of a partial last round of workgroups are split
+ * along k, zeroed in y and added into with float atomics, so the last bits of those outputs may
+ * vary from run to run. */
 q6k_status q4k_gemm(const void* xq, const float* da, const float* das, int64_t n, const void* w,
                     int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
 

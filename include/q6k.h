@@ -140,8 +140,8 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
  *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned; only y[0..n)[0..m) is
  *             written
  *   xq, da and w must hold at least the sizes q6k_act_bytes / q6k_weight_bytes return (the
- *   kernels read whole padded tiles).  Layout 2 also needs k <= 2^25, layouts 0 and 1
- *   k <= 2^26 (Q6K_ESIZE otherwise). */
+ *   kernels read whole padded tiles).  Layout 2 also needs k < 2^25, layouts 0 and 1
+ *   k < 2^26 (Q6K_ESIZE otherwise). */
 q6k_status q6k_gemm(const void* xq, const float* da, int64_t n, const void* w, int layout,
                     int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
 

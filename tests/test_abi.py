@@ -96,6 +96,18 @@ def test_gemm_errors(args, status):
     assert lib().q6k_gemm(*args) == status
 
 
+def test_gemm_size_limits():
+    # one 32-bit buffer range per operand tile: layout 2 needs k < 2^25 (k/32 x 2 KiB of digit
+    # planes per row tile), layouts 0/1 k < 2^26; dimensions beyond 2^40 are rejected outright
+    L = lib()
+    for layout, kmax in ((2, 1 << 25), (1, 1 << 26), (0, 1 << 26)):
+        assert L.q6k_gemm(FAKE, FAKE, 4, FAKE, layout, 8, kmax, FAKE, 8, None) == -4
+        assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 1 << 25, FAKE, None) == -4
+    assert L.q6k_gemm(FAKE, FAKE, (1 << 40) + 1, FAKE, 2, 8, 256, FAKE, 8, None) == -4
+    assert L.q6k_gemm(FAKE, FAKE, 4, FAKE, 2, (1 << 40) + 1, 256, FAKE, (1 << 40) + 1, None) == -4
+    assert L.q4k_gemm(FAKE, FAKE, FAKE, 4, FAKE, 8, 1 << 26, FAKE, 8, None) == -4
+
+
 def test_subdots_errors():
     L = lib()
     assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, None, None) == -1
