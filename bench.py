@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+# f32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, x 2 with dual
+# issue (the published 157.3 TFLOP/s fp32 vector figure counts one FMA as 2 flops)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
 METRIC = "q6_K GEMM effective int8 TOPS + µs/GMAC, % of MFMA peak (ffn_down, N=3314)"
 
 
@@ -290,6 +293,19 @@ def main():
     prep_total_us = float(prep_us.sum(axis=1).mean())
 
     ops = sum(2.0 * p.n * p.m * p.k for p in problems)
+
+    def valu_lane_ops(p):
+        # rescale work the method needs per launch (f32 lane-operations)
+        if args.weights == "q4k" or layout != 2:
+            per_chunk = 3 if args.weights == "q4k" else 4
+            return float(p.n) * p.m * per_chunk * (p.k // 32)
+        return float(p.n) * p.m * (3 * (p.k // 32) + p.k // 256)
+
+    valu_ops = sum(valu_lane_ops(p) for p in problems)
+    valu_form = ("3 per 32-k chunk: t = fma(F, d*sc, bias term), two fma with da and da*S"
+                 if args.weights == "q4k" else
+                 "4 per 32-k chunk: two halves x (fma with d*sc, fma with da)" if layout != 2 else
+                 "3 per 32-k chunk (digit fold fma + add, fma with da) + 1 per super-block (d)")
     gmac = ops / 2e9
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_total_us * 1e-6) / 1e12
@@ -352,6 +368,12 @@ def main():
                                 f"gemm_kernel<layout {layout}>"),
                      "algorithmic_per_launch": {"int8_ops": 2.0 * p0.n * p0.m * p0.k,
                                                 "bytes": p0.alg_bytes()["gemm"]}},
+        # the unit that binds this method's GEMM: its f32 rescale on the vector ALU
+        "alu_roofline": {"bound": "alu", "achieved": round(valu_ops / (gemm_total_us * 1e-6) / 1e12, 2),
+                         "peak": round(VALU_PEAK_TOPS, 1), "unit": "T VALU lane-ops/s",
+                         "frac": round(valu_ops / (gemm_total_us * 1e-6) / 1e12 / VALU_PEAK_TOPS, 4),
+                         "per_output": valu_form,
+                         "algorithmic_per_launch": {"valu_lane_ops": valu_lane_ops(p0)}},
     }
     if args.swiglu:
         # the unfused pair for comparison: h written by q6k_swiglu_f32, then q6k_quantize_act
