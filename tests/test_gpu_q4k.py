@@ -160,3 +160,22 @@ def test_split_k_pieces():
     err = np.abs(y[rows].astype(np.float64) - y_ref)
     assert (err <= 1e-3 * t_ref).all(), float((err / np.maximum(t_ref, 1e-300)).max())
     assert np.isfinite(y).all()
+
+
+def test_partly_split_grid():
+    """1088 output tiles on a 768-slot device: 768 computed whole, the other 320 split along k,
+    zeroed first and added into; every output finite, sampled tokens against the oracle."""
+    n, m, k = 2176, 4096, 512
+    print("q4k partly split grid", flush=True)
+    raw = synthetic.weights_q4k(m, k, seed=61)
+    x = synthetic.activations(n, k, seed=62, kind="outlier")
+    xq, da, das = prep_acts(x)
+    w = prep_weights(raw, m, k)
+    y = run_gemm(xq, da, das, n, w, m, k)
+    assert np.isfinite(y).all()
+    rows = np.array(sorted(set(np.random.default_rng(5).choice(n, 13, replace=False).tolist())
+                           | {0, n - 1}))
+    xq_ref, da_ref = oracle.quantize(x[rows])
+    y_ref, t_ref = oracle.q4_gemm(xq_ref, da_ref, raw, m)
+    err = np.abs(y[rows].astype(np.float64) - y_ref)
+    assert (err <= 1e-3 * t_ref).all(), float((err / np.maximum(t_ref, 1e-300)).max())
