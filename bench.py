@@ -13,8 +13,10 @@ Workloads: tiny, attn_v_n512, attn_v_n3314, ffn_down_n3314 (the default and head
 ffn_down_shard8 (3314 x 512 x 11008: one GPU's share of ffn_down under an 8-way split of the
 output rows), and sweep32: 32 layers of (attn_v 4096x4096 + ffn_down 4096x11008) at 3314 tokens, 64 GEMMs back to
 back on one stream over 1.6 GB of raw weights, inputs drawn on the device.  --cold writes a
-512 MiB scrub buffer before every timed step, so weights and activations come from HBM rather
-than the 256 MB Infinity Cache.  --swiglu (single workloads) replaces the prepass by the fused
+512 MiB scrub buffer and then reads a 1 GiB one before every timed step, so weights and
+activations come from HBM rather than the 256 MB Infinity Cache (the read leaves the cache
+holding clean lines: evicting the write's dirty lines inside the timed step would time their
+write-back instead).  --swiglu (single workloads) replaces the prepass by the fused
 producer q6k_swiglu_quantize_act reading the two SwiGLU factors, and also times the unfused pair
 (q6k_swiglu_f32 writing h, then q6k_quantize_act) once for comparison.  --weights q4k runs the
 q4_K variant on the same shapes (synthetic q4_K weights): step = q6k_quantize_act +
@@ -237,8 +239,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # 512 MiB written between steps evicts the 256 MB Infinity Cache
+    # 512 MiB written, then 1 GiB read, between steps: evicts the 256 MB Infinity Cache and leaves
+    # it holding clean lines
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    scrub_rd = torch.ones(256 << 20, dtype=torch.float32, device=dev) if args.cold else None
 
     def step(evs=None):
         # evs[j] = events before the prepass, between prepass and GEMM, after the GEMM
@@ -275,6 +279,7 @@ def main():
         step_ms, wall = [], 0.0
         for i in range(args.steps):
             scrub.fill_(i & 255)
+            scrub_rd.sum()
             torch.cuda.synchronize()
             s_ev = torch.cuda.Event(enable_timing=True)
             e_ev = torch.cuda.Event(enable_timing=True)

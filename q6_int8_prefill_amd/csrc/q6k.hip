@@ -370,13 +370,16 @@ __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_
 }
 
 // Zero y over the tiles that a GEMM splits along k (tiles n_full .. gx*gy-1 of the GEMM's tile
-// order, XCD-aware or plain), one workgroup per tile of tile_tok tokens x 128 rows.
+// order, XCD-aware or plain).  Each tile of tile_tok tokens x 128 rows is spread over
+// tile_tok / 8 workgroups of 8 tokens, one row per thread and token (512-byte wave stores).
+constexpr int kZeroTok = 8;  // tokens per zeroing workgroup
 __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, int64_t ldy,
                                                       int64_t n, int64_t m, uint32_t gx,
                                                       uint32_t gy, uint32_t n_full,
                                                       uint32_t tile_tok, int xcd_order) {
+  const uint32_t parts = tile_tok / kZeroTok;
+  const uint32_t t = n_full + blockIdx.x / parts, part = blockIdx.x % parts;
   uint32_t bx, by;
-  const uint32_t t = n_full + blockIdx.x;
   if (xcd_order) {
     tile_of(t, gx, gy, &bx, &by);
   } else {
@@ -385,8 +388,9 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
   }
   const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
   if (r >= m) return;
-  for (uint32_t i = threadIdx.x >> 7; i < tile_tok; i += 2) {
-    const int64_t tok = (int64_t)bx * tile_tok + i;
+#pragma unroll
+  for (uint32_t i = threadIdx.x >> 7; i < kZeroTok; i += 2) {
+    const int64_t tok = (int64_t)bx * tile_tok + part * kZeroTok + i;
     if (tok < n) y[tok * ldy + r] = 0.0f;
   }
 }
@@ -697,16 +701,22 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 // GEMM on layout 2 (folded scales).  q6_K has one f16 d per 256-element super-block and one int8
 // sc per 16 elements, so a 32-k chunk contributes da * d * E to y with the exact integer
 //     E = sum_k xq[k] * v[k],   v = sc[k/16] * (q[k] - 32)  in [-4064, 4096].
-// v does not fit an int8 MFMA operand; it is stored as two int8 digit planes v = 64*hi + lo.  Per
-// chunk and 32x32 tile: two v_mfma_i32_32x32x32_i8 (low and high digits, full 32-k chunk each),
-// both started from the bit pattern of 1.5*2^23 (|E_lo| <= 32*127*32, |E_hi| <= 32*127*64, both
-// < 2^22, so each result reads exactly as the float 1.5*2^23 + E_part).  Then
-//     u  = fma(F_hi, 64, -65 * 1.5*2^23)  = 64*E_hi - 1.5*2^23   (a multiple of 64 below 2^30:
+// v does not fit an int8 MFMA operand; it is stored as two int8 digit planes v = 64*hi + lo
+// (lo in [-32, 31], hi in [-63, 64]).  Per chunk and 32x32 tile: two v_mfma_i32_32x32x32_i8 (low
+// and high digits, full 32-k chunk each) whose int32 accumulators start from float bit patterns,
+// so that each result reads exactly as a float without a conversion (|E_lo| <= 32*127*32 and
+// |E_hi| <= 32*127*64 are both below 2^22, so the sum never leaves the starting binade):
+//     low digits from 1.5*2^23 (ulp 1):   F_lo = 1.5*2^23 + E_lo
+//     high digits from 1.5*2^29 (ulp 64): F_hi = 1.5*2^29 + 64*E_hi
+// Then
+//     u  = F_hi - (1.5*2^29 + 1.5*2^23)   = 64*E_hi - 1.5*2^23   (a multiple of 64 below 2^25:
 //                                                               exact)
 //     e  = u + F_lo                       = E                    (|E| < 2^24: exact)
 //     sb = fma(e, da, sb)
-// three VALU operations per output per chunk, all exact up to the single rounding of the last.
-// After the 8th chunk of a super-block, acc = fma(sb, d, acc) and sb restarts at 0.
+// three VALU operations per output per chunk, all exact up to the single rounding of the last,
+// and all three short (two-operand) encodings with register operands only, which issue faster
+// than a multiply-add with a literal 64.  After the 8th chunk of a super-block,
+// acc = fma(sb, d, acc) and sb restarts at 0.
 //
 // Orientation: the weights are the MFMA's A operand and the activations its B operand, so lane l,
 // register r of a tile holds weight row 8*(r/4) + 4*(l/32) + r%4 and token l%32: each lane needs a
@@ -714,14 +724,17 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 // x 128 weight rows (row tiles 4*by .. 4*by+3); wave w computes row tile 4*by + w against both
 // token tiles.
 // ---------------------------------------------------------------------------------------------
-constexpr float kFoldK = -65.0f * kBiasF;  // exact: 195 * 2^22
+constexpr int kBiasHiI = 0x4E400000;       // bit pattern of 1.5 * 2^29 (ulp 64)
+constexpr float kFoldK = -65.0f * kBiasF;  // -(1.5*2^29 + 1.5*2^23), exact: 195 * 2^22
 
 
 // e = 64*E_hi + E_lo from the two biased digit products (exact, see above), in two phases of 16
 // independent operations (no VALU instruction depends on the one before it).
 __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, const v16i& fl) {
+  float kk = kFoldK;
+  asm("" : "+v"(kk));  // a register operand: VOP2 adds without a literal
 #pragma unroll
-  for (int r = 0; r < 16; ++r) e[r] = __builtin_fmaf(__int_as_float(fh[r]), 64.0f, kFoldK);
+  for (int r = 0; r < 16; ++r) e[r] = __int_as_float(fh[r]) + kk;
 #pragma unroll
   for (int r = 0; r < 16; ++r) e[r] += __int_as_float(fl[r]);
 }
@@ -734,7 +747,8 @@ __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, cons
 //     holds a whole super-block (2 token tiles x 8 chunks x 1 KiB + 2 x 1 KiB of da), the ring
 //     has 4 slots and runs 3 super-blocks ahead, so the workgroup meets at a barrier once per
 //     super-block instead of once per chunk;
-//   - the rescale of tile 1 runs one step late, while the MFMAs of the next chunk's tile 0 run;
+//   - per chunk, tile 0's MFMAs and rescale, then tile 1's: one tile's MFMA results are live at a
+//     time (the other wave on the SIMD issues VALU work while this one waits for its MFMAs);
 //   - 2 workgroups per CU (up to 256 VGPRs per wave).
 // Work split: tile_work (rounds of one tile per workgroup slot, a partial last round split along
 // k into pieces that add into y).
@@ -766,8 +780,6 @@ struct FoldCtx {
 
 struct FoldState {
   float acc[2][16], sb[2][16];
-  v16i fh1, fl1;     // MFMA results of tile 1, rescaled one step late
-  float da1p;        // da of tile 1 for those results
   v4i x0, x1;        // activations of the current chunk, token tiles 0 and 1
   float da0, da1;    // their da (this lane's token)
   v4i blo[4], bhi[4];  // digit planes of chunk c in entry c % 4
@@ -845,13 +857,11 @@ __device__ __forceinline__ void fold_read(uint32_t xb, uint32_t dab, FoldState& 
   st.da1 = d1;
 }
 
-// sb (+)= e * da, or the store of e for the test export (chunks before the piece's first are the
-// placeholder of the first step and are not stored).
+// sb (+)= e * da, or the store of e for the test export.
 template <bool DOTS, bool FIRST>
 __device__ __forceinline__ void fold_rescale(float (&sb)[16], const float (&e)[16], float dav,
                                            const FoldCtx& k, int64_t c, int u) {
   if (DOTS) {
-    if (c < k.c_begin) return;
     const int g = k.lane >> 5;
     const int64_t tok = k.tok0 + kTile * u;
 #pragma unroll
@@ -868,33 +878,15 @@ __device__ __forceinline__ void fold_rescale(float (&sb)[16], const float (&e)[1
   }
 }
 
-__device__ __forceinline__ void fold_order(v4i& x, const float (&v)[16]) {
-  // v are inputs only: tied in/out operands would make the register allocator copy them
-  asm volatile(""
-               : "+v"(x)
-               : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]),
-                 "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]),
-                 "v"(v[13]), "v"(v[14]), "v"(v[15]));
-}
-
 // Chunk c = 8s + J.  xb/dab: this lane's LDS addresses in super-block s's slot; xn/dn: in slot
-// s + 1 (read by the last step).
+// s + 1 (read by the last step).  Tile 0's MFMAs, its rescale, then tile 1's MFMAs and rescale:
+// one tile's MFMA results are live at a time, and the other wave on the SIMD keeps the VALU busy
+// while this one waits for its MFMAs.
 template <bool DOTS, int J>
 __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t xb, uint32_t dab,
                                         uint32_t xn, uint32_t dn, FoldState& st,
-                                        const v16i& bias) {
+                                        const v16i& bias_lo, const v16i& bias_hi) {
   const int64_t c = 8 * s + J;
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(st.x0), "+v"(st.x1), "+v"(st.da0), "+v"(st.da1));
-  const v4i lo = st.blo[J % 4], hi = st.bhi[J % 4];
-  v16i fh0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x0, bias, 0, 0, 0);
-  v16i fl0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, st.x0, bias, 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // tile 1 of chunk c - 1, while tile 0's MFMAs run
-  {
-    float e1[16];
-    fold_digits(e1, st.fh1, st.fl1);
-    fold_rescale<DOTS, J == 1>(st.sb[1], e1, st.da1p, k, c - 1, 1);
-  }
   if (J == 0) {
     // both tiles have finished super-block s - 1: apply its d, then fetch super-block s's
     if (!DOTS) {
@@ -905,11 +897,12 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
     }
     fold_load_d(k, s, st.d, st.acc[0], st.acc[1]);
   }
-  fold_order(st.x1, st.sb[1]);
-  const v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x1, bias, 0, 0, 0);
-  const v16i fl1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, st.x1, bias, 0, 0, 0);
-  const float da0 = st.da0;
-  st.da1p = st.da1;
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(st.x0), "+v"(st.x1), "+v"(st.da0), "+v"(st.da1));
+  const v4i lo = st.blo[J % 4], hi = st.bhi[J % 4];
+  const v4i x1 = st.x1;
+  const float da0 = st.da0, da1 = st.da1;
+  v16i fh = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, st.x0, bias_hi, 0, 0, 0);
+  v16i fl = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, st.x0, bias_lo, 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
   fold_load_planes(k, c + 3, st.blo[(J + 3) % 4], st.bhi[(J + 3) % 4]);
   if (J == 0) fold_dma(k, s + kFAhead);
@@ -926,14 +919,21 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
   } else {
     fold_read<(J + 1) * 1024, (J + 1) * 128>(xb, dab, st);
   }
-  asm volatile("" : "+v"(fh0), "+v"(fl0));
+  asm volatile("" : "+v"(fh), "+v"(fl));
   {
-    float e0[16];
-    fold_digits(e0, fh0, fl0);
-    fold_rescale<DOTS, J == 0>(st.sb[0], e0, da0, k, c, 0);
+    float e[16];
+    fold_digits(e, fh, fl);
+    fold_rescale<DOTS, J == 0>(st.sb[0], e, da0, k, c, 0);
   }
-  st.fh1 = fh1;
-  st.fl1 = fl1;
+  __builtin_amdgcn_sched_barrier(0);
+  fh = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, x1, bias_hi, 0, 0, 0);
+  fl = __builtin_amdgcn_mfma_i32_32x32x32_i8(lo, x1, bias_lo, 0, 0, 0);
+  asm volatile("" : "+v"(fh), "+v"(fl));
+  {
+    float e[16];
+    fold_digits(e, fh, fl);
+    fold_rescale<DOTS, J == 0>(st.sb[1], e, da1, k, c, 1);
+  }
 }
 
 template <bool DOTS>
@@ -978,9 +978,12 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
   const uint32_t db0 = lds_addr(smem) + kFSlotDa + 2 * tp * 1024 +
                        4 * (16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3));
 
-  v16i bias;
+  v16i bias_lo, bias_hi;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) bias[r] = kBiasI;
+  for (int r = 0; r < 16; ++r) {
+    bias_lo[r] = kBiasI;
+    bias_hi[r] = kBiasHiI;
+  }
   FoldState st;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -988,9 +991,6 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     for (int r = 0; r < 16; ++r) st.acc[u][r] = st.sb[u][r] = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) st.d[r] = 0.0f;
-  st.fh1 = bias;  // the first step's late rescale of tile 1 then adds 0 * 0
-  st.fl1 = bias;
-  st.da1p = 0.0f;
 
   // prologue: super-blocks s0 .. s0+2 of activations, chunks c0 .. c0+2 of digit planes; wait
   // for all of them, meet, read chunk c0's operands
@@ -1008,21 +1008,16 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     const uint32_t cur = (uint32_t)(s % kFRing) * kFSlot;
     const uint32_t nxt = (uint32_t)((s + 1) % kFRing) * kFSlot;
     const uint32_t xb = xb0 + cur, dab = db0 + cur, xn = xb0 + nxt, dn = db0 + nxt;
-    fold_step<DOTS, 0>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 1>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 2>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 3>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 4>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 5>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 6>(k, s, xb, dab, xn, dn, st, bias);
-    fold_step<DOTS, 7>(k, s, xb, dab, xn, dn, st, bias);
+    fold_step<DOTS, 0>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 1>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 2>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 3>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 4>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 5>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 6>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
+    fold_step<DOTS, 7>(k, s, xb, dab, xn, dn, st, bias_lo, bias_hi);
   }
-  // tile 1 of the last chunk, then the last super-block's d
-  {
-    float e1[16];
-    fold_digits(e1, st.fh1, st.fl1);
-    fold_rescale<DOTS, false>(st.sb[1], e1, st.da1p, k, k.c_end - 1, 1);
-  }
+  // the last super-block's d
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // drain the trailing loads
   if (DOTS) return;
 #pragma unroll
@@ -1492,12 +1487,15 @@ q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitP
 
 // Zero y over the tiles that the plan splits (none if nothing is split), in the same tile order
 // and tile height (tokens) as the GEMM that follows.
+static_assert((kTile * kFTok) % kZeroTok == 0 && (kTile * kWgTokTiles) % kZeroTok == 0,
+              "zeroing workgroups cover whole tiles");
 void zero_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, int64_t tile_tok,
                       bool xcd_order, float* y, int64_t ldy, int64_t n, int64_t m,
                       hipStream_t s) {
   const int64_t nsplit = gx * gy - sp.n_full;
   if (nsplit > 0)
-    hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)nsplit), dim3(256), 0, s, y, ldy, n, m,
+    hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)(nsplit * (tile_tok / kZeroTok))),
+                       dim3(256), 0, s, y, ldy, n, m,
                        (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full, (uint32_t)tile_tok,
                        xcd_order ? 1 : 0);
 }
