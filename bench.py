@@ -310,7 +310,7 @@ def main():
     valu_form = ("3 per 32-k chunk: t = fma(F, d*sc, bias term), two fma with da and da*S"
                  if args.weights == "q4k" else
                  "4 per 32-k chunk: two halves x (fma with d*sc, fma with da)" if layout != 2 else
-                 "3 per 32-k chunk (digit fold fma + add, fma with da) + 1 per super-block (d)")
+                 "3 per 32-k chunk (digit fold: two adds; fma with da) + 1 per super-block (d)")
     gmac = ops / 2e9
     value = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_total_us * 1e-6) / 1e12
