@@ -84,6 +84,23 @@ def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
+def _flat(**bufs):
+    """Buffers the kernels address as plain byte ranges from their first element must be
+    contiguous (an expanded or strided view would let them run past the tensor's storage)."""
+    for name, t in bufs.items():
+        if t is not None and t.numel() and not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous buffer")
+
+
+def _rows_fit(name, t, rows, cols, ld):
+    """A row-major [rows][ld] operand: its last row must end inside the tensor's storage."""
+    if rows <= 0 or cols <= 0 or t is None or not t.numel():
+        return
+    span = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    if ((rows - 1) * ld + cols) * t.element_size() > span:
+        raise ValueError(f"{name}: {rows} rows of stride {ld} run past its storage")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -118,6 +135,8 @@ def q6k_quantize_act(x, xq, da, n=None, k=None, ldx=None, stream=None):
         raise ValueError("x must be row-major")
     if x.numel() and (n > x.shape[0] or k > x.shape[1]):
         raise ValueError("n, k exceed the shape of x")
+    _rows_fit("x", x, n, k, ldx)
+    _flat(xq=xq, da=da)
     _check(_lib.q6k_quantize_act(_ptr(x), n, k, ldx, _ptr(xq), _nbytes(xq), _ptr(da),
                                  _nbytes(da), _stream(stream)), "q6k_quantize_act")
 
@@ -131,6 +150,7 @@ def _rows_f32(name, t, n, k):
         raise ValueError(f"{name} must be row-major")
     if t.numel() and (n > t.shape[0] or k > t.shape[1]):
         raise ValueError(f"n, k exceed the shape of {name}")
+    _rows_fit(name, t, n, k, t.stride(0))
 
 
 def q6k_swiglu_quantize_act(gate, up, xq, da, n=None, k=None, stream=None):
@@ -141,6 +161,7 @@ def q6k_swiglu_quantize_act(gate, up, xq, da, n=None, k=None, stream=None):
     _rows_f32("up", up, n, k)
     if gate.stride(0) != up.stride(0):
         raise ValueError("gate and up must share their row stride")
+    _flat(xq=xq, da=da)
     _check(_lib.q6k_swiglu_quantize_act(_ptr(gate), _ptr(up), n, k, gate.stride(0), _ptr(xq),
                                         _nbytes(xq), _ptr(da), _nbytes(da), _stream(stream)),
            "q6k_swiglu_quantize_act")
@@ -160,6 +181,7 @@ def q6k_swiglu_f32(gate, up, h, stream=None):
 
 def q6k_expand_weights(w_raw, m, k, layout, w_out, stream=None):
     """raw q6_K bytes (device uint8, m*(k/256)*210 B) -> prepared weights in `layout`."""
+    _flat(w_raw=w_raw, w_out=w_out)
     if w_raw is not None and w_raw.numel() and _nbytes(w_raw) < m * (k // 256) * 210:
         raise ValueError("raw weight buffer too small")
     _check(_lib.q6k_expand_weights(_ptr(w_raw), m, k, layout, _ptr(w_out), _nbytes(w_out),
@@ -168,6 +190,7 @@ def q6k_expand_weights(w_raw, m, k, layout, w_out, stream=None):
 
 def _check_operands(xq, da, n, w, layout, m, k):
     """The C GEMM entry points take no buffer sizes: check them here before passing pointers."""
+    _flat(xq=xq, da=da, w=w)
     if n <= 0 or m <= 0:
         return
     xb, db = q6k_act_bytes(n, k)
@@ -189,6 +212,9 @@ def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None):
     _check_operands(xq, da, n, w, layout, m, k)
     if y is not None and n > 0 and m > 0 and y.numel() < (n - 1) * ldy + m:
         raise ValueError("y too small for n x ldy")
+    if y is not None and y.dim() == 2 and y.numel() and y.stride(1) != 1:
+        raise ValueError("y must be row-major")
+    _rows_fit("y", y, n, m, ldy)
     _check(_lib.q6k_gemm(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(y), ldy,
                          _stream(stream)), "q6k_gemm")
 
@@ -197,6 +223,7 @@ def q6k_gemm_subdots(xq, da, n, w, layout, m, k, dots, stream=None):
     """Test-only: int32 sub-block dots [n][m][k/16] from the GEMM kernel source."""
     if dots is not None and dots.dtype != torch.int32:
         raise TypeError("dots must be int32")
+    _flat(dots=dots)
     _check_operands(xq, da, n, w, layout, m, k)
     if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 16):
         raise ValueError("dots too small for n x m x k/16")
@@ -208,6 +235,7 @@ def q6k_gemm_chunkdots(xq, da, n, w, layout, m, k, dots, stream=None):
     """Test-only: int32 per-chunk numerators [n][m][k/32] from the layout-2 kernel source."""
     if dots is not None and dots.dtype != torch.int32:
         raise TypeError("dots must be int32")
+    _flat(dots=dots)
     _check_operands(xq, da, n, w, layout, m, k)
     if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 32):
         raise ValueError("dots too small for n x m x k/32")
@@ -231,6 +259,7 @@ def q4k_weight_bytes(m, k):
 
 def q4k_expand_weights(w_raw, m, k, w_out, stream=None):
     """raw q4_K bytes (device uint8, m*(k/256)*144 B) -> prepared codes + (d*sc, -dmin*m) pairs."""
+    _flat(w_raw=w_raw, w_out=w_out)
     if w_raw is not None and w_raw.numel() and _nbytes(w_raw) < m * (k // 256) * 144:
         raise ValueError("raw weight buffer too small")
     _check(_lib.q4k_expand_weights(_ptr(w_raw), m, k, _ptr(w_out), _nbytes(w_out),
@@ -239,6 +268,7 @@ def q4k_expand_weights(w_raw, m, k, w_out, stream=None):
 
 def q4k_act_sums(xq, da, n, k, das, stream=None):
     """das = da * (sum of each chunk's codes), tiled like da."""
+    _flat(xq=xq, da=da, das=das)
     xb, db = q6k_act_bytes(n, k)
     if n > 0 and xb and (_nbytes(xq) < xb or _nbytes(da) < db):
         raise ValueError("activation buffers too small")
@@ -247,6 +277,7 @@ def q4k_act_sums(xq, da, n, k, das, stream=None):
 
 
 def _check_q4_operands(xq, da, das, n, w, m, k):
+    _flat(xq=xq, da=da, das=das, w=w)
     if n <= 0 or m <= 0:
         return
     xb, db = q6k_act_bytes(n, k)
@@ -268,6 +299,9 @@ def q4k_gemm(xq, da, das, n, w, m, k, y, ldy=None, stream=None):
     _check_q4_operands(xq, da, das, n, w, m, k)
     if y is not None and n > 0 and m > 0 and y.numel() < (n - 1) * ldy + m:
         raise ValueError("y too small for n x ldy")
+    if y is not None and y.dim() == 2 and y.numel() and y.stride(1) != 1:
+        raise ValueError("y must be row-major")
+    _rows_fit("y", y, n, m, ldy)
     _check(_lib.q4k_gemm(_ptr(xq), _ptr(da), _ptr(das), n, _ptr(w), m, k, _ptr(y), ldy,
                          _stream(stream)), "q4k_gemm")
 
@@ -276,6 +310,7 @@ def q4k_gemm_dots(xq, n, w, m, k, dots, stream=None):
     """Test-only: int32 chunk dots [n][m][k/32] from the q4_K GEMM kernel source."""
     if dots is not None and dots.dtype != torch.int32:
         raise TypeError("dots must be int32")
+    _flat(dots=dots)
     _check_q4_operands(xq, None, None, n, w, m, k)
     if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 32):
         raise ValueError("dots too small for n x m x k/32")

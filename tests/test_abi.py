@@ -165,3 +165,36 @@ def test_q4k_sizes_and_errors():
     assert L.q4k_gemm(FAKE, FAKE, FAKE, 0, FAKE, 8, 256, FAKE, 8, None) == 0
     assert L.q4k_gemm_dots(FAKE, 4, FAKE, 8, 256, None, None) == -1
     assert q6k.q4k_launches() >= 0
+
+
+def test_binding_rejects_views_that_outrun_their_storage():
+    # checked in Python before any pointer reaches the library (CPU tensors suffice: the shape
+    # checks come before the device check)
+    import torch
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 64, 128, 256
+    xb, db = q6k.q6k_act_bytes(n, k)
+    wb = q6k.q6k_weight_bytes(m, k, 2)
+    one = torch.zeros(1, dtype=torch.uint8)
+    xq_exp = one.expand(xb)                     # numel large enough, storage one byte
+    da = torch.zeros(db // 4, dtype=torch.float32)
+    w = torch.zeros(wb, dtype=torch.uint8)
+    y = torch.zeros((n, m), dtype=torch.float32)
+    with pytest.raises(ValueError, match="contiguous"):
+        q6k.q6k_gemm(xq_exp, da, n, w, 2, m, k, y)
+    with pytest.raises(ValueError, match="contiguous"):
+        q6k.q6k_gemm(torch.zeros(xb, dtype=torch.uint8), da, n, one.expand(wb), 2, m, k, y)
+    with pytest.raises(ValueError, match="contiguous"):
+        q6k.q6k_quantize_act(torch.zeros((n, k)), xq_exp, da)
+    with pytest.raises(ValueError, match="contiguous"):
+        q6k.q4k_act_sums(xq_exp, da, n, k, da.clone())
+    with pytest.raises(ValueError, match="row-major"):
+        q6k.q6k_gemm(torch.zeros(xb, dtype=torch.uint8), da, n, w, 2, m, k,
+                     torch.zeros((m, n), dtype=torch.float32).t())
+    # an explicit row stride that runs the activation rows past the tensor's storage
+    with pytest.raises(ValueError, match="past its storage"):
+        q6k.q6k_quantize_act(torch.zeros((n, k)), torch.zeros(xb, dtype=torch.uint8), da,
+                             ldx=2 * k)
+    with pytest.raises(ValueError, match="past its storage"):
+        q6k.q6k_gemm(torch.zeros(xb, dtype=torch.uint8), da, n, w, 2, m, k,
+                     torch.zeros(1, dtype=torch.float32).expand(n * m))
