@@ -70,7 +70,23 @@ def cpu_baseline(raw, x, m, k, tokens, weights="q6k"):
     dt = time.perf_counter() - t0
     return {"value": 2.0 * tokens * m * k / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"first {tokens} tokens x all {m} rows x k={k} (quantize + reference GEMM), "
-                      f"{dt:.1f} s single-threaded"}
+                      f"{dt:.1f} s single-threaded",
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """The host CPU's model name and the hardware threads this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"model": model, "threads_available": threads}
 
 
 def kernel_source_digest():
