@@ -1,0 +1,75 @@
+"""The hot path recorded in a HIP graph (torch.cuda.graph) and replayed: the prepass and the layout-2
+GEMM with its split-k last round (a zeroing kernel, then float atomics) launch only kernels on
+the caller's stream (no memset nodes), so a captured step replays to the eager results.  Each
+replay follows eager work of the program's own that clobbers every output, and is checked: codes
+and scales byte for byte against the eager run and the oracle, outputs against the eager run up
+to the order of the split tiles' additions, and against the oracle within the output tolerance."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from layouts import untile_da, untile_xq
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n,m,k", [(2176, 4096, 512), (200, 384, 2048)])
+def test_captured_step_replays(n, m, k):
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    print(f"graph replay n={n} m={m} k={k}", flush=True)
+    dev = gpu_util.DEV
+    raw = synthetic.weights(m, k, seed=n + 5, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=n + 6, kind="outlier")
+    w = gpu_util.expand(raw, m, k, 2)
+    xg = torch.from_numpy(x).to(dev)
+    xb, db = q6k.q6k_act_bytes(n, k)
+    xq = torch.zeros(xb, dtype=torch.uint8, device=dev)
+    da = torch.zeros(db // 4, dtype=torch.float32, device=dev)
+    y = torch.zeros((n, m), dtype=torch.float32, device=dev)
+
+    def step():
+        q6k.q6k_quantize_act(xg, xq, da)
+        q6k.q6k_gemm(xq, da, n, w, 2, m, k, y)
+
+    # eager reference of the same calls
+    step()
+    torch.cuda.synchronize()
+    xq_e, da_e, y_e = xq.clone(), da.clone(), y.clone()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    xq_ref, da_ref = oracle.quantize(x)
+    rows = np.array(sorted(set(np.random.default_rng(n).choice(n, min(n, 12), replace=False).tolist())
+                           | {0, n - 1}))
+    y_ref, t_ref = oracle.gemm(xq_ref[rows], da_ref[rows], raw, m)
+    for rep in range(3):
+        # the program's own eager work between replays: clobber every output buffer
+        xq.fill_(0xA5)
+        da.fill_(float("nan"))
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xq, xq_e), rep
+        assert torch.equal(da.view(torch.int32), da_e.view(torch.int32)), rep
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all(), rep
+        # against the eager run: equal up to the order of the split tiles' additions
+        diff = np.abs(got.astype(np.float64) - y_e.cpu().numpy())
+        assert (diff[rows] <= 1e-6 * t_ref + 1e-30).all(), rep
+        ok, worst = gpu_util.within_tolerance(got[rows], y_ref, t_ref)
+        assert ok, f"replay {rep}: worst |err|/T = {worst}"
+    np.testing.assert_array_equal(untile_xq(xq.cpu().numpy(), n, k)[:n], xq_ref)
+    np.testing.assert_array_equal(untile_da(da.cpu().numpy(), n, k)[:n].view(np.uint32),
+                                  da_ref.view(np.uint32))
