@@ -43,7 +43,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # ~50 steps (~30 ms on ffn_down) bring the GPU's clock to its loaded steady state; with 5, the
+    # first timed steps still run several percent slow
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--layout", type=int, default=2, choices=[0, 1, 2])
     ap.add_argument("--workload", default="ffn_down_n3314")
     ap.add_argument("--weights", default="q6k", choices=["q6k", "q4k"],
@@ -279,17 +281,22 @@ def main():
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in problems]
            for _ in range(args.steps)]
     if scrub is None:
+        # the timed steps carry no instrumentation: the per-kernel breakdown (and the GEMM time the
+        # roofline uses) comes from the same number of steps run again with events between kernels
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         start.record(stream)
         for i in range(args.steps):
-            step(evs[i])
+            step()
         end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         ms_per_step = start.elapsed_time(end) / args.steps
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
     else:
         # cold: the scrub runs between steps, outside the timed span of each step
         step_ms, wall = [], 0.0
