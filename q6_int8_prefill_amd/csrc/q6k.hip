@@ -755,7 +755,7 @@ __device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, cons
 // ---------------------------------------------------------------------------------------------
 // Waves per workgroup.  The kernel is written for 4 (64 tokens x 128 rows, 2 workgroups per CU)
 // or 8 (128 x 128, 1 per CU, two waves reading each row tile's planes); 8 measured 1 % faster on
-// ffn_down and 5-12 % slower on attn_v N=512, so 4 it is.
+// ffn_down and 2-4 % slower on attn_v N=512, so 4 it is.
 constexpr int kFWaves = 4;
 static_assert(kFWaves == 4 || kFWaves == 8, "4 or 8 waves");
 constexpr int kFoldedWgPerCu = 8 / kFWaves;
