@@ -86,3 +86,19 @@ def untile_q4k(buf, m, k):
     pr = b[mp * k: mp * k + mp * nchunk * 8].view(np.float32).reshape(mp // 32, nsb, 8, 32, 2)
     pairs = pr.transpose(0, 3, 1, 2, 4).reshape(mp, nchunk, 2)
     return codes, pairs
+
+
+def untile_xq_tile(buf, tile, k):
+    """The 32 tokens of token tile `tile` from tiled xq bytes -> int8 [32][k]."""
+    nchunk = k // 32
+    b = np.asarray(buf, np.uint8)[tile * nchunk * 1024: (tile + 1) * nchunk * 1024]
+    # axes: c, g, p, h, e  ->  token p, k = 32c + 16h + 8g + e
+    return b.view(np.int8).reshape(nchunk, 2, 32, 2, 8).transpose(2, 0, 3, 1, 4).reshape(32, k)
+
+
+def untile_da_tile(buf, tile, k):
+    """The 32 tokens of token tile `tile` from tiled da floats -> f32 [32][k/32]."""
+    nchunk = k // 32
+    t = np.asarray(buf, np.float32)[tile * nchunk * 32: (tile + 1) * nchunk * 32]
+    # axes: c, g, q, r  ->  token 8q + 4g + r
+    return t.reshape(nchunk, 2, 4, 4).transpose(2, 1, 3, 0).reshape(32, nchunk)

@@ -82,3 +82,41 @@ def test_prepass_near_ties():
                 row[i] = v if rng.integers(0, 2) else -v
             x[t, 32 * c: 32 * c + 32] = row
     check(x)
+
+
+def test_prepass_more_token_tiles_than_one_launch_holds():
+    """Over 65535 token tiles (2,097,120 tokens) the prepass is issued as several launches with a
+    token-tile offset: tiles on both sides of the seam, the last real tile and the zero padding
+    tiles are checked bit for bit against the oracle (k = 256: 2.1 GB of activations)."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    from layouts import untile_da_tile, untile_xq_tile
+    n, k = 65535 * 32 + 45, 256
+    print(f"prepass multi-launch n={n} k={k}", flush=True)
+    x = synthetic.activations_torch(n, k, 31, gpu_util.DEV, "outlier")
+    xb, db = q6k.q6k_act_bytes(n, k)
+    xq = torch.full((xb,), 0xA5, dtype=torch.uint8, device=gpu_util.DEV)
+    da = torch.full((db // 4,), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+    q6k.q6k_quantize_act(x, xq, da)
+    torch.cuda.synchronize()
+    ntiles = round_up(n, 128) // 32
+    last = (n - 1) // 32
+    tiles = sorted({0, 1, 65533, 65534, 65535, 65536, last} |
+                   set(np.random.default_rng(3).integers(0, last, 4).tolist()))
+    nchunk = k // 32
+    for t in tiles:
+        lo, hi = 32 * t, min(32 * t + 32, n)
+        xs = x[lo:hi].cpu().numpy()
+        q_ref, d_ref = oracle.quantize(xs)
+        qb = xq[t * nchunk * 1024:(t + 1) * nchunk * 1024].cpu().numpy()
+        dbuf = da[t * nchunk * 32:(t + 1) * nchunk * 32].cpu().numpy()
+        got_q = untile_xq_tile(qb, 0, k)
+        got_d = untile_da_tile(dbuf, 0, k)
+        np.testing.assert_array_equal(got_q[:hi - lo], q_ref, err_msg=f"tile {t}")
+        np.testing.assert_array_equal(got_d[:hi - lo].view(np.uint32), d_ref.view(np.uint32),
+                                      err_msg=f"tile {t}")
+        assert (got_q[hi - lo:] == 0).all() and (got_d[hi - lo:] == 0).all()
+    for t in range(last + 1, ntiles):  # padding tiles
+        assert (xq[t * nchunk * 1024:(t + 1) * nchunk * 1024] == 0).all()
+        assert (da[t * nchunk * 32:(t + 1) * nchunk * 32] == 0).all()

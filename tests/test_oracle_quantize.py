@@ -74,3 +74,17 @@ def test_roundtrip_exact_grid(oracle_mod):
     xq, da = oracle_mod.quantize(x)
     assert (da == 1).all()
     np.testing.assert_array_equal(xq, x.astype(np.int8))
+
+
+def test_tile_views_agree_with_whole_buffer_views():
+    # test-side helpers only: the per-tile views read the same bytes as the whole-buffer ones
+    from layouts import untile_da, untile_da_tile, untile_xq, untile_xq_tile
+    rng = np.random.default_rng(7)
+    n, k = 200, 512
+    np_ = 256
+    xq = rng.integers(0, 256, np_ * k, dtype=np.uint8)
+    da = rng.standard_normal(np_ * (k // 32)).astype(np.float32)
+    whole_q, whole_d = untile_xq(xq, n, k), untile_da(da, n, k)
+    for t in (0, 3, 7):
+        np.testing.assert_array_equal(untile_xq_tile(xq, t, k), whole_q[32 * t: 32 * t + 32])
+        np.testing.assert_array_equal(untile_da_tile(da, t, k), whole_d[32 * t: 32 * t + 32])
