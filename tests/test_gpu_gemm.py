@@ -333,3 +333,28 @@ def test_gemm_partly_split_grid(layout):
     y_ref, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
     ok, worst = gpu_util.within_tolerance(y[rows], y_ref, t_ref)
     assert ok, f"worst |err|/T = {worst}"
+
+
+def test_repeatability_whole_and_split_tiles():
+    """Tiles computed whole are bit-for-bit repeatable; tiles split along k add their pieces with
+    float atomics in run-dependent order, so their last bits may vary by a few roundings of the
+    partial sums, each at most sum|terms| in magnitude."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    for n, m, k, split in ((2048, 4096, 512, False), (200, 384, 2048, True)):
+        print(f"repeatability n={n} m={m} k={k}", flush=True)
+        raw = synthetic.weights(m, k, seed=n + 9, sc_lo=-128, sc_hi=127)
+        x = synthetic.activations(n, k, seed=n + 10, kind="outlier")
+        xq, da = gpu_util.quantize(x)
+        w = gpu_util.expand(raw, m, k, 2)
+        runs = [gpu_util.gemm(xq, da, n, w, 2, m, k) for _ in range(3)]
+        if not split:
+            for r in runs[1:]:
+                np.testing.assert_array_equal(r.view(np.uint32), runs[0].view(np.uint32))
+        else:
+            xq_ref, da_ref = oracle.quantize(x)
+            _, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
+            for r in runs[1:]:
+                diff = np.abs(r.astype(np.float64) - runs[0])
+                assert (diff <= 1e-6 * t_ref).all(), float((diff / np.maximum(t_ref, 1e-300)).max())
