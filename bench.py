@@ -202,10 +202,8 @@ def main():
     if sweep:
         for layer in range(synthetic.SWEEP_LAYERS):
             for kind in ("attn_v", "ffn_down"):
-                s = synthetic.sweep_layer(layer, kind)
-                raw_d = synthetic.weights_torch(s["m"], s["k"], s["seed"], dev)
-                x_d = synthetic.activations_torch(s["n"], s["k"], s["seed"], dev, s["x"])
-                problems.append(Problem(q6k, torch, x_d, raw_d, s["n"], s["m"], s["k"], layout, dev))
+                raw_d, x_d, sn, sm, sk = synthetic.sweep_inputs_torch(layer, kind, dev)
+                problems.append(Problem(q6k, torch, x_d, raw_d, sn, sm, sk, layout, dev))
                 del raw_d
     elif args.swiglu:
         spec = synthetic.WORKLOADS[args.workload]

@@ -57,16 +57,21 @@ q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, f
 
 /* The GEMM: y[t][j] = sum over chunks c of da*(d*sc)*D - (dmin*m)*das, D the exact int32 dot of
  * the int8 activations with the 4-bit codes over the chunk.  y f32 [n][ldy], ldy >= m, 4-byte
- * aligned; xq, da, das, w 16-byte aligned and of the sizes above; k < 2^26 (Q6K_ESIZE
- * otherwise).  As for q6k_gemm, output tiles of a partial last round of workgroups are split
- * along k, zeroed in y and added into with float atomics, so the last bits of those outputs may
- * vary from run to run. */
-q6k_status q4k_gemm(const void* xq, const float* da, const float* das, int64_t n, const void* w,
-                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
+ * aligned, y_bytes >= 4*((n-1)*ldy + m); xq, da, das, w 16-byte aligned and at least the sizes
+ * above (Q6K_ESIZE otherwise); k < 2^26.  The work split is q6k_gemm's: output tiles of a
+ * partial last round of workgroups are split along k, zeroed in y and added into with float
+ * atomics, so the last bits of those outputs may vary from run to run. */
+q6k_status q4k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                    const float* das, size_t das_bytes, int64_t n, const void* w, size_t w_bytes,
+                    int64_t m, int64_t k, float* y, size_t y_bytes, int64_t ldy, void* stream);
 
-/* Test-only export of the same kernel source: the int32 chunk dots D to dots [n][m][k/32]. */
-q6k_status q4k_gemm_dots(const void* xq, int64_t n, const void* w, int64_t m, int64_t k,
-                         int32_t* dots, void* stream);
+/* Test-only export of the same kernel source, with the grid and work split of q4k_gemm: the int32
+ * chunk dots D of tokens [tok0, tok0 + ntok) x rows [row0, row0 + nrow) to dots
+ * int32 [ntok][nrow][k/32] (window and size rules of q6k_gemm_subdots). */
+q6k_status q4k_gemm_dots(const void* xq, size_t xq_bytes, int64_t n, const void* w,
+                         size_t w_bytes, int64_t m, int64_t k, int64_t tok0, int64_t ntok,
+                         int64_t row0, int64_t nrow, int32_t* dots, size_t dots_bytes,
+                         void* stream);
 
 /* Liveness counter: q4k_gemm and q4k_gemm_dots launches since load. */
 uint64_t q4k_launches(void);

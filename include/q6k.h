@@ -29,7 +29,12 @@
  *   - n == 0 or m == 0 is an empty problem: the call returns Q6K_OK and launches nothing.
  *   - k must be a positive multiple of 256 (whole super-blocks).
  *   - Buffers read with 16-byte accesses (x, xq, da, w) must be 16-byte aligned; y and dots
- *     need 4-byte alignment.
+ *     need 4-byte alignment; raw q6_K weights need 2-byte alignment (a 210-byte block is only
+ *     2-byte aligned, so a row of blocks cannot promise more).
+ *   - The tiled activations, the prepared weights and every output buffer come with their size
+ *     in bytes, checked against what the call reads or writes (Q6K_ESIZE if too small); a caller
+ *     that passes a size larger than the allocation defeats the check.  Row-major inputs (x,
+ *     gate, up, raw weights) are sized by n, k and their leading dimension alone.
  *
  * Tiled layouts (produced and consumed only by this library; the byte order is documented so
  * callers and tests can rebuild the plain [row][k] views):
@@ -75,7 +80,7 @@ typedef enum {
   Q6K_EINVAL = -1, /* null pointer, negative size, unknown layout, ld too small */
   Q6K_ESHAPE = -2, /* k not a positive multiple of 256 */
   Q6K_EALIGN = -3, /* a pointer or leading dimension breaks the 16-byte alignment rule */
-  Q6K_ESIZE = -4,  /* an output buffer is smaller than the size query returns, or sizes overflow */
+  Q6K_ESIZE = -4,  /* a buffer is smaller than the call reads or writes, or sizes overflow */
   Q6K_EHIP = -5    /* the HIP runtime rejected a launch */
 } q6k_status;
 
@@ -116,7 +121,7 @@ q6k_status q6k_swiglu_f32(const float* gate, const float* up, int64_t n, int64_t
 size_t q6k_weight_bytes(int64_t m, int64_t k, int layout);
 
 /* Load-time weight preparation.  Input: raw q6_K blocks, row j's super-block b at byte
- * (j*(k/256) + b)*210 (byte map of "r38 ..." sec. 2.1; any alignment).  Output: layout 0 (6-bit
+ * (j*(k/256) + b)*210 (byte map of "r38 ..." sec. 2.1; 2-byte aligned: Q6K_EALIGN otherwise).  Output: layout 0 (6-bit
  * codes regrouped for wide loads plus the raw scale bytes; expanded to centered int8 inside the
  * GEMM, "r41 ..." sec. 2), layout 1 (centered int8 plane plus f32 d*sc plane, "r53 ..." sec.
  * 2.3 and the W_dsc plane of "r42 ..." sec. 3.2) or layout 2 (two int8 digit planes of
@@ -129,34 +134,45 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
  * ("r38 ..." sec. 2.2, 2.4).  Layouts 0 and 1 accumulate each 32-k chunk as two independent f32
  * additions, one per 16-k half.  Layout 2 forms the chunk's exact integer
  * E = sc[2c]*D[2c] + sc[2c+1]*D[2c+1] and adds da * E once per chunk, then applies d once per
- * super-block; the result differs from layouts 0/1 only in f32 rounding.  When its output tiles
- * (64 tokens x 128 rows) do not fill whole rounds of the GPU's workgroup slots, layout 2 splits
- * the tiles of the last round along k: it first zeroes them in y, then adds the pieces' partial
- * sums with float atomics in no fixed order, so the last bits of those outputs may vary from run
- * to run (always within the rounding of one f32 addition per piece).  Two calls that write the
- * same y concurrently on different streams race.
- *   xq, da  : outputs of q6k_quantize_act for the same n, k
- *   w       : output of q6k_expand_weights for the same m, k and `layout`
- *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned; only y[0..n)[0..m) is
- *             written
- *   xq, da and w must hold at least the sizes q6k_act_bytes / q6k_weight_bytes return (the
- *   kernels read whole padded tiles).  Layout 2 also needs k < 2^25, layouts 0 and 1
- *   k < 2^26 (Q6K_ESIZE otherwise). */
-q6k_status q6k_gemm(const void* xq, const float* da, int64_t n, const void* w, int layout,
-                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream);
+ * super-block; the result differs from layouts 0/1 only in f32 rounding.
+ * Work split (every layout): output tiles of 64 tokens x 128 rows are dealt out in rounds of one
+ * per workgroup slot of the GPU; when the last round would leave slots idle, its tiles are split
+ * along k into pieces of whole super-blocks.  The call then first zeroes those tiles in y and the
+ * pieces add their partial sums with float atomics in no fixed order, so the last bits of those
+ * outputs may vary from run to run (within the rounding of one f32 addition per piece); tiles
+ * computed whole are bit-for-bit repeatable.  Two calls that write the same y concurrently on
+ * different streams race.
+ *   xq, da  : outputs of q6k_quantize_act for the same n, k; xq_bytes, da_bytes at least what
+ *             q6k_act_bytes returns (the kernels read whole padded tiles)
+ *   w       : output of q6k_expand_weights for the same m, k and `layout`; w_bytes at least
+ *             q6k_weight_bytes(m, k, layout)
+ *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned, y_bytes >= 4*((n-1)*ldy + m);
+ *             only y[0..n)[0..m) is written
+ * Layout 2 also needs k < 2^25, layouts 0 and 1 k < 2^26 (Q6K_ESIZE otherwise). */
+q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                    int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
+                    float* y, size_t y_bytes, int64_t ldy, void* stream);
 
-/* Test-only export of the same kernel source: instead of y, stores the int32 sub-block dots
- * D[t][j][s] (the two KSPLIT halves of every chunk) to dots [n][m][k/16].  Layouts 0 and 1 only
- * (layout 2 never forms them: Q6K_EINVAL). */
-q6k_status q6k_gemm_subdots(const void* xq, const float* da, int64_t n, const void* w, int layout,
-                            int64_t m, int64_t k, int32_t* dots, void* stream);
+/* Test-only export of the same kernel source, launched with the same grid and work split as
+ * q6k_gemm for this n, m, k and layout: instead of y, stores the int32 sub-block dots D[t][j][s]
+ * (the two KSPLIT halves of every chunk) of the window of tokens t in [tok0, tok0 + ntok) and
+ * rows j in [row0, row0 + nrow) to dots, int32 [ntok][nrow][k/16] (dots_bytes at least
+ * 4 * ntok * nrow * k/16).  The window must lie inside the n x m problem (Q6K_EINVAL otherwise);
+ * an empty window launches nothing.  Layouts 0 and 1 only (layout 2 never forms them:
+ * Q6K_EINVAL). */
+q6k_status q6k_gemm_subdots(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                            int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
+                            int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
+                            int32_t* dots, size_t dots_bytes, void* stream);
 
-/* Test-only export of the layout-2 kernel: instead of y, stores the per-chunk integer numerators
- * E[t][j][c] = sc[j][2c]*D[t][j][2c] + sc[j][2c+1]*D[t][j][2c+1] (|E| < 2^24), as the kernel
- * reconstructs them from its two digit products, to dots [n][m][k/32].  Layout 2 only
- * (Q6K_EINVAL otherwise). */
-q6k_status q6k_gemm_chunkdots(const void* xq, const float* da, int64_t n, const void* w,
-                              int layout, int64_t m, int64_t k, int32_t* dots, void* stream);
+/* Test-only export of the layout-2 kernel, with the window rules of q6k_gemm_subdots: stores the
+ * per-chunk integer numerators E[t][j][c] = sc[j][2c]*D[t][j][2c] + sc[j][2c+1]*D[t][j][2c+1]
+ * (|E| < 2^24), as the kernel reconstructs them from its two digit products, to dots
+ * int32 [ntok][nrow][k/32].  Layout 2 only (Q6K_EINVAL otherwise). */
+q6k_status q6k_gemm_chunkdots(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                              int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
+                              int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
+                              int32_t* dots, size_t dots_bytes, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* q6k_strerror(int status);

@@ -3,9 +3,11 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
 import this package.  The product package never imports it and shares no code with it.
 
-The arithmetic lives in ``q6k_oracle.c`` (plain single-threaded C loops, f64 where floating point
-is not fixed by the pages); this module only marshals numpy arrays through ctypes.  Each wrapper
-names the C function and, through it, the passage it follows.
+The arithmetic lives in ``q6k_oracle.c`` and ``q4k_oracle.c`` (plain C loops, f64 where floating
+point is not fixed by the pages); this module only marshals numpy arrays through ctypes.  Each
+wrapper names the C function and, through it, the passage it follows.  The functions over many
+output rows (or tokens) split them into contiguous ranges over ``threads`` host threads (default
+``default_threads()``); the result is the same bit for bit for every thread count.
 """
 import ctypes
 import os
@@ -26,8 +28,8 @@ def build():
     """Compile the C oracle (gcc, IEEE f32 semantics: no fast-math)."""
     os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
     tmp = _LIB_PATH + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
-                           *_SRC, "-o", tmp, "-lm"])
+    subprocess.check_call(["gcc", "-O3", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+                           "-ffp-contract=off", *_SRC, "-o", tmp, "-lm"])
     os.replace(tmp, _LIB_PATH)
 
 
@@ -45,21 +47,36 @@ def _load():
         lib.q6o_code.argtypes = [p, ctypes.c_int]
         lib.q6o_decode.argtypes = [p, i64, i64, p, p, p]
         lib.q6o_dequant.argtypes = [p, i64, i64, p]
-        lib.q6o_quantize.argtypes = [p, i64, i64, p, p]
-        lib.q6o_subdots.argtypes = [p, p, i64, i64, i64, p]
-        lib.q6o_chunkdots.argtypes = [p, p, i64, i64, i64, p]
+        ci = ctypes.c_int
+        lib.q6o_quantize.argtypes = [p, i64, i64, p, p, ci]
+        lib.q6o_subdots.argtypes = [p, p, i64, i64, i64, p, ci]
+        lib.q6o_chunkdots.argtypes = [p, p, i64, i64, i64, p, ci]
         lib.q6o_swiglu.argtypes = [p, p, i64, p]
         lib.q4o_scale_min.argtypes = [p, ctypes.c_int, p, p]
         lib.q4o_code.restype = ctypes.c_int
         lib.q4o_code.argtypes = [p, ctypes.c_int]
         lib.q4o_decode.argtypes = [p, i64, i64, p, p, p, p, p]
         lib.q4o_dequant.argtypes = [p, i64, i64, p]
-        lib.q4o_chunkdots.argtypes = [p, p, i64, i64, i64, p]
+        lib.q4o_chunkdots.argtypes = [p, p, i64, i64, i64, p, ci]
         lib.q4o_chunksums.argtypes = [p, i64, i64, p]
-        lib.q4o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p]
-        lib.q6o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p]
+        lib.q4o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p, ci]
+        lib.q6o_gemm.argtypes = [p, p, i64, p, i64, i64, p, p, ci]
         _lib = lib
     return _lib
+
+
+def default_threads():
+    """Host threads the oracle uses by default: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when that is set (a shared host's share of its cores)."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        avail = min(avail, int(cap))
+    return max(1, avail)
+
+
+def _threads(threads):
+    return default_threads() if threads is None else max(1, int(threads))
 
 
 def _ptr(a):
@@ -103,7 +120,7 @@ def dequant(raw, m, k):
     return w
 
 
-def quantize(x):
+def quantize(x, threads=None):
     """f32 [n][k] -> (xq int8 [n][k], da f32 [n][k/32])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     n, k = x.shape
@@ -111,17 +128,17 @@ def quantize(x):
         raise ValueError("k must be a multiple of 32")
     xq = np.empty((n, k), np.int8)
     da = np.empty((n, k // 32), np.float32)
-    _load().q6o_quantize(_ptr(x), n, k, _ptr(xq), _ptr(da))
+    _load().q6o_quantize(_ptr(x), n, k, _ptr(xq), _ptr(da), _threads(threads))
     return xq, da
 
 
-def subdots(xq, raw, m):
+def subdots(xq, raw, m, threads=None):
     """-> int32 [n][m][k/16] per-sub-block integer dots."""
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     n, k = xq.shape
     raw = _raw(raw, m, k)
     out = np.empty((n, m, k // 16), np.int32)
-    _load().q6o_subdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
+    _load().q6o_subdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out), _threads(threads))
     return out
 
 
@@ -135,17 +152,17 @@ def swiglu(gate, up):
     return out
 
 
-def chunkdots(xq, raw, m):
+def chunkdots(xq, raw, m, threads=None):
     """-> int32 [n][m][k/32] per-chunk integer numerators with the sub-block scales applied."""
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     n, k = xq.shape
     raw = _raw(raw, m, k)
     out = np.empty((n, m, k // 32), np.int32)
-    _load().q6o_chunkdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
+    _load().q6o_chunkdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out), _threads(threads))
     return out
 
 
-def gemm(xq, da, raw, m):
+def gemm(xq, da, raw, m, threads=None):
     """-> (y f64 [n][m], t f64 [n][m]): reference output and its tolerance scale sum |terms|."""
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     da = np.ascontiguousarray(da, dtype=np.float32)
@@ -154,7 +171,7 @@ def gemm(xq, da, raw, m):
     raw = _raw(raw, m, k)
     y = np.empty((n, m), np.float64)
     t = np.empty((n, m), np.float64)
-    _load().q6o_gemm(_ptr(xq), _ptr(da), n, _ptr(raw), m, k, _ptr(y), _ptr(t))
+    _load().q6o_gemm(_ptr(xq), _ptr(da), n, _ptr(raw), m, k, _ptr(y), _ptr(t), _threads(threads))
     return y, t
 
 
@@ -205,13 +222,13 @@ def q4_dequant(raw, m, k):
     return w
 
 
-def q4_chunkdots(xq, raw, m):
+def q4_chunkdots(xq, raw, m, threads=None):
     """-> int32 [n][m][k/32] integer dots of the activation codes with the 4-bit weight codes."""
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     n, k = xq.shape
     raw = _raw4(raw, m, k)
     out = np.empty((n, m, k // 32), np.int32)
-    _load().q4o_chunkdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out))
+    _load().q4o_chunkdots(_ptr(xq), _ptr(raw), n, m, k, _ptr(out), _threads(threads))
     return out
 
 
@@ -224,7 +241,7 @@ def q4_chunksums(xq):
     return out
 
 
-def q4_gemm(xq, da, raw, m):
+def q4_gemm(xq, da, raw, m, threads=None):
     """-> (y f64 [n][m], t f64 [n][m]) for q4_K weights."""
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     da = np.ascontiguousarray(da, dtype=np.float32)
@@ -233,5 +250,5 @@ def q4_gemm(xq, da, raw, m):
     raw = _raw4(raw, m, k)
     y = np.empty((n, m), np.float64)
     t = np.empty((n, m), np.float64)
-    _load().q4o_gemm(_ptr(xq), _ptr(da), n, _ptr(raw), m, k, _ptr(y), _ptr(t))
+    _load().q4o_gemm(_ptr(xq), _ptr(da), n, _ptr(raw), m, k, _ptr(y), _ptr(t), _threads(threads))
     return y, t

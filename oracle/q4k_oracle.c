@@ -36,6 +36,9 @@
 #define Q4_OFF_QS 16
 
 double q6o_f16_to_f64(uint16_t h); /* exact binary16 decode, in q6k_oracle.c */
+/* rows [0, m) in contiguous ranges over `threads` threads, in q6k_oracle.c */
+typedef void (*q6o_rows_fn)(void* ctx, int64_t r0, int64_t r1);
+void q6o_parallel_rows(q6o_rows_fn fn, void* ctx, int64_t m, int threads);
 
 /* The 6-bit scale and min of sub-block j (0..7) from the 12 scale bytes s. */
 void q4o_scale_min(const uint8_t* s, int j, int* sc, int* m) {
@@ -92,11 +95,21 @@ void q4o_dequant(const uint8_t* raw, int64_t m, int64_t k, double* w) {
 }
 
 /* Per-chunk integer dots D[n][m][k/32] = sum over the chunk of xq * q (exact, |D| <= 32*127*15). */
-void q4o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
-                   int32_t* dots) {
+struct q4o_dots_args {
+  const int8_t* xq;
+  const uint8_t* raw;
+  int64_t n, m, k;
+  int32_t* dots;
+};
+static void q4o_chunkdots_rows(void* p, int64_t j0, int64_t j1) {
+  const struct q4o_dots_args* a = (const struct q4o_dots_args*)p;
+  const int8_t* xq = a->xq;
+  const uint8_t* raw = a->raw;
+  int64_t n = a->n, m = a->m, k = a->k;
+  int32_t* dots = a->dots;
   int64_t nc = k / 32, nsb = k / Q4_QK;
   uint8_t* q = (uint8_t*)malloc((size_t)k);
-  for (int64_t j = 0; j < m; ++j) {
+  for (int64_t j = j0; j < j1; ++j) {
     for (int64_t i = 0; i < k; ++i) q[i] = (uint8_t)q4o_code(raw + (j * nsb + i / Q4_QK) * Q4_BLOCK, (int)(i % Q4_QK));
     for (int64_t t = 0; t < n; ++t)
       for (int64_t c = 0; c < nc; ++c) {
@@ -106,6 +119,11 @@ void q4o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, i
       }
   }
   free(q);
+}
+void q4o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
+                   int32_t* dots, int threads) {
+  struct q4o_dots_args a = {xq, raw, n, m, k, dots};
+  q6o_parallel_rows(q4o_chunkdots_rows, &a, m, threads);
 }
 
 /* Per-chunk activation sums S[n][k/32] = sum of the chunk's 32 int8 codes. */
@@ -122,13 +140,26 @@ void q4o_chunksums(const int8_t* xq, int64_t n, int64_t k, int32_t* sums) {
 /* Reference output: y[n][m] = sum over chunks c of da*(d*sc)*D - da*(dmin*m)*S in f64, and
  * t[n][m] = the sum of the magnitudes of those two terms over all chunks (tolerance scale).
  * t may be NULL. */
-void q4o_gemm(const int8_t* xq, const float* da, int64_t n, const uint8_t* raw, int64_t m,
-              int64_t k, double* y, double* t) {
+struct q4o_gemm_args {
+  const int8_t* xq;
+  const float* da;
+  int64_t n;
+  const uint8_t* raw;
+  int64_t m, k;
+  double *y, *t;
+};
+static void q4o_gemm_rows(void* p, int64_t j0, int64_t j1) {
+  const struct q4o_gemm_args* g = (const struct q4o_gemm_args*)p;
+  const int8_t* xq = g->xq;
+  const float* da = g->da;
+  const uint8_t* raw = g->raw;
+  int64_t n = g->n, m = g->m, k = g->k;
+  double *y = g->y, *t = g->t;
   int64_t nc = k / 32, nsb = k / Q4_QK;
   uint8_t* q = (uint8_t*)malloc((size_t)k);
   double* dsc = (double*)malloc(sizeof(double) * (size_t)nc);
   double* dmm = (double*)malloc(sizeof(double) * (size_t)nc);
-  for (int64_t j = 0; j < m; ++j) {
+  for (int64_t j = j0; j < j1; ++j) {
     for (int64_t c = 0; c < nc; ++c) {
       const uint8_t* blk = raw + (j * nsb + c / 8) * Q4_BLOCK;
       int a, mm;
@@ -158,4 +189,9 @@ void q4o_gemm(const int8_t* xq, const float* da, int64_t n, const uint8_t* raw, 
   free(q);
   free(dsc);
   free(dmm);
+}
+void q4o_gemm(const int8_t* xq, const float* da, int64_t n, const uint8_t* raw, int64_t m,
+              int64_t k, double* y, double* t, int threads) {
+  struct q4o_gemm_args g = {xq, da, n, raw, m, k, y, t};
+  q6o_parallel_rows(q4o_gemm_rows, &g, m, threads);
 }

@@ -23,9 +23,14 @@
  *   - the output reference is the f64 sum of the per-sub-block terms da * (d * sc) * D, and the
  *     per-output tolerance scale T is the f64 sum of their magnitudes.
  *
- * Every function is single-threaded plain loops; integer dots are accumulated in int64.
- * Build: gcc -O2 -fPIC -shared (no -ffast-math: the f32 division and roundf must be IEEE).
+ * Every function is plain loops; integer dots are accumulated in int64.  The functions over
+ * many output rows (or tokens) take a thread count and hand each thread one contiguous range of
+ * rows: rows are independent and each row's loops and arithmetic are the same whatever the range,
+ * so the result is the same bit for bit for any thread count (threads <= 1: the calling thread
+ * does everything).
+ * Build: gcc -O2 -fPIC -shared -pthread (no -ffast-math: the f32 division and roundf must be IEEE).
  */
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <math.h>
@@ -35,6 +40,42 @@
 #define OFF_QH 128
 #define OFF_SC 192
 #define OFF_D 208
+
+/* Run fn(ctx, r0, r1) over rows [0, m) split into `threads` contiguous ranges, one per thread. */
+typedef void (*q6o_rows_fn)(void* ctx, int64_t r0, int64_t r1);
+struct q6o_rows_job {
+  q6o_rows_fn fn;
+  void* ctx;
+  int64_t r0, r1;
+};
+static void* q6o_rows_thread(void* p) {
+  struct q6o_rows_job* job = (struct q6o_rows_job*)p;
+  job->fn(job->ctx, job->r0, job->r1);
+  return NULL;
+}
+void q6o_parallel_rows(q6o_rows_fn fn, void* ctx, int64_t m, int threads) {
+  if ((int64_t)threads > m) threads = (int)m;
+  if (threads <= 1) {
+    fn(ctx, 0, m);
+    return;
+  }
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)threads);
+  int* started = (int*)calloc((size_t)threads, sizeof(int));
+  struct q6o_rows_job* job = (struct q6o_rows_job*)malloc(sizeof(*job) * (size_t)threads);
+  for (int i = 0; i < threads; ++i) {
+    job[i].fn = fn;
+    job[i].ctx = ctx;
+    job[i].r0 = m * i / threads;
+    job[i].r1 = m * (i + 1) / threads;
+    started[i] = pthread_create(&tid[i], NULL, q6o_rows_thread, &job[i]) == 0;
+    if (!started[i]) q6o_rows_thread(&job[i]); /* no thread available: run the range here */
+  }
+  for (int i = 0; i < threads; ++i)
+    if (started[i]) pthread_join(tid[i], NULL);
+  free(tid);
+  free(started);
+  free(job);
+}
 
 /* IEEE 754 binary16 -> double, exact for every finite value including subnormals. */
 double q6o_f16_to_f64(uint16_t h) {
@@ -99,9 +140,20 @@ void q6o_dequant(const uint8_t* raw, int64_t m, int64_t k, double* w) {
 
 /* Activation quantization per (token, 32-k chunk) with f32 scale da (reading above).
  *   xq[n][k] int8, da[n][k/32] f32. */
-void q6o_quantize(const float* x, int64_t n, int64_t k, int8_t* xq, float* da) {
+struct q6o_quantize_args {
+  const float* x;
+  int64_t k;
+  int8_t* xq;
+  float* da;
+};
+static void q6o_quantize_rows(void* p, int64_t t0, int64_t t1) {
+  const struct q6o_quantize_args* a = (const struct q6o_quantize_args*)p;
+  const float* x = a->x;
+  int64_t k = a->k;
+  int8_t* xq = a->xq;
+  float* da = a->da;
   int64_t nc = k / 32;
-  for (int64_t t = 0; t < n; ++t)
+  for (int64_t t = t0; t < t1; ++t)
     for (int64_t c = 0; c < nc; ++c) {
       const float* xc = x + t * k + c * 32;
       float amax = 0.0f;
@@ -124,6 +176,10 @@ void q6o_quantize(const float* x, int64_t n, int64_t k, int8_t* xq, float* da) {
       }
     }
 }
+void q6o_quantize(const float* x, int64_t n, int64_t k, int8_t* xq, float* da, int threads) {
+  struct q6o_quantize_args a = {x, k, xq, da};
+  q6o_parallel_rows(q6o_quantize_rows, &a, n, threads);
+}
 
 /* Decode one row of blocks into centered codes. */
 static void decode_row(const uint8_t* row, int64_t k, int8_t* wc) {
@@ -133,13 +189,22 @@ static void decode_row(const uint8_t* row, int64_t k, int8_t* wc) {
 
 /* Per-sub-block integer dots D[n][m][s] = sum_{k in sub-block s} xq[n][k] * wc[m][k]
  * (KSPLIT=2 halves, [r38 sec. 2.4]); exact, stored as int32 (|D| <= 16*127*32). */
-void q6o_subdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
-                 int32_t* dots) {
+struct q6o_dots_args {
+  const int8_t* xq;
+  const uint8_t* raw;
+  int64_t n, m, k;
+  int32_t* dots;
+};
+static void q6o_subdots_rows(void* p, int64_t j0, int64_t j1) {
+  const struct q6o_dots_args* a = (const struct q6o_dots_args*)p;
+  const int8_t* xq = a->xq;
+  int64_t n = a->n, m = a->m, k = a->k;
+  int32_t* dots = a->dots;
   int64_t ns = k / 16;
   int64_t row_bytes = (k / QK) * BLOCK_BYTES;
   int8_t* wc = (int8_t*)malloc((size_t)k);
-  for (int64_t j = 0; j < m; ++j) {
-    decode_row(raw + j * row_bytes, k, wc);
+  for (int64_t j = j0; j < j1; ++j) {
+    decode_row(a->raw + j * row_bytes, k, wc);
     for (int64_t t = 0; t < n; ++t)
       for (int64_t s = 0; s < ns; ++s) {
         int64_t acc = 0;
@@ -148,6 +213,11 @@ void q6o_subdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int
       }
   }
   free(wc);
+}
+void q6o_subdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
+                 int32_t* dots, int threads) {
+  struct q6o_dots_args a = {xq, raw, n, m, k, dots};
+  q6o_parallel_rows(q6o_subdots_rows, &a, m, threads);
 }
 
 /* SwiGLU product feeding ffn_down, in f64: h = up * silu(gate), silu(g) = g / (1 + exp(-g)), for
@@ -168,13 +238,16 @@ void q6o_swiglu(const float* gate, const float* up, int64_t count, double* h) {
  * y is da[n][c] * d[m][c/8] * E[n][m][c], which equals the two per-half terms of sec. 2.2 summed
  * in exact arithmetic.  Written from the definition: decode each element, multiply by its own
  * scale, sum over the chunk. */
-void q6o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
-                   int32_t* dots) {
+static void q6o_chunkdots_rows(void* p, int64_t j0, int64_t j1) {
+  const struct q6o_dots_args* a = (const struct q6o_dots_args*)p;
+  const int8_t* xq = a->xq;
+  int64_t n = a->n, m = a->m, k = a->k;
+  int32_t* dots = a->dots;
   int64_t nc = k / 32;
   int64_t row_bytes = (k / QK) * BLOCK_BYTES;
   int32_t* ws = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-  for (int64_t j = 0; j < m; ++j) {
-    const uint8_t* row = raw + j * row_bytes;
+  for (int64_t j = j0; j < j1; ++j) {
+    const uint8_t* row = a->raw + j * row_bytes;
     for (int64_t i = 0; i < k; ++i) {
       const uint8_t* blk = row + (i / QK) * BLOCK_BYTES;
       int sc = (int8_t)blk[OFF_SC + (i % QK) / 16];
@@ -189,18 +262,35 @@ void q6o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, i
   }
   free(ws);
 }
+void q6o_chunkdots(const int8_t* xq, const uint8_t* raw, int64_t n, int64_t m, int64_t k,
+                   int32_t* dots, int threads) {
+  struct q6o_dots_args a = {xq, raw, n, m, k, dots};
+  q6o_parallel_rows(q6o_chunkdots_rows, &a, m, threads);
+}
 
 /* Reference output: y[n][m] = sum_s da[n][s/2] * (d[m][s/16] * sc[m][s]) * D[n][m][s] in f64,
  * and t[n][m] = sum_s |that term|, the tolerance scale ([r38 sec. 2.2]: one rescale per
  * 16-element half, no dmin term).  t may be NULL. */
-void q6o_gemm(const int8_t* xq, const float* da, int64_t n, const uint8_t* raw, int64_t m,
-              int64_t k, double* y, double* t) {
+struct q6o_gemm_args {
+  const int8_t* xq;
+  const float* da;
+  int64_t n;
+  const uint8_t* raw;
+  int64_t m, k;
+  double *y, *t;
+};
+static void q6o_gemm_rows(void* p, int64_t j0, int64_t j1) {
+  const struct q6o_gemm_args* a = (const struct q6o_gemm_args*)p;
+  const int8_t* xq = a->xq;
+  const float* da = a->da;
+  int64_t n = a->n, m = a->m, k = a->k;
+  double *y = a->y, *t = a->t;
   int64_t nsb = k / QK, ns = k / 16, nc = k / 32;
   int64_t row_bytes = nsb * BLOCK_BYTES;
   int8_t* wc = (int8_t*)malloc((size_t)k);
   double* dsc = (double*)malloc(sizeof(double) * (size_t)ns);
-  for (int64_t j = 0; j < m; ++j) {
-    const uint8_t* row = raw + j * row_bytes;
+  for (int64_t j = j0; j < j1; ++j) {
+    const uint8_t* row = a->raw + j * row_bytes;
     decode_row(row, k, wc);
     for (int64_t s = 0; s < ns; ++s) {
       const uint8_t* blk = row + (s / 16) * BLOCK_BYTES;
@@ -222,4 +312,9 @@ void q6o_gemm(const int8_t* xq, const float* da, int64_t n, const uint8_t* raw, 
   }
   free(wc);
   free(dsc);
+}
+void q6o_gemm(const int8_t* xq, const float* da, int64_t n, const uint8_t* raw, int64_t m,
+              int64_t k, double* y, double* t, int threads) {
+  struct q6o_gemm_args a = {xq, da, n, raw, m, k, y, t};
+  q6o_parallel_rows(q6o_gemm_rows, &a, m, threads);
 }

@@ -29,11 +29,14 @@ _lib.q6k_weight_bytes.argtypes = [_i64, _i64, _int]
 _lib.q6k_expand_weights.restype = _int
 _lib.q6k_expand_weights.argtypes = [_p, _i64, _i64, _int, _p, _sz, _p]
 _lib.q6k_gemm.restype = _int
-_lib.q6k_gemm.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _i64, _p]
+_lib.q6k_gemm.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64, _p]
+_WIN = [_i64, _i64, _i64, _i64]
 _lib.q6k_gemm_subdots.restype = _int
-_lib.q6k_gemm_subdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
+_lib.q6k_gemm_subdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + _WIN + \
+    [_p, _sz, _p]
 _lib.q6k_gemm_chunkdots.restype = _int
-_lib.q6k_gemm_chunkdots.argtypes = [_p, _p, _i64, _p, _int, _i64, _i64, _p, _p]
+_lib.q6k_gemm_chunkdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + _WIN + \
+    [_p, _sz, _p]
 _lib.q4k_weight_bytes.restype = _sz
 _lib.q4k_weight_bytes.argtypes = [_i64, _i64]
 _lib.q4k_expand_weights.restype = _int
@@ -41,9 +44,10 @@ _lib.q4k_expand_weights.argtypes = [_p, _i64, _i64, _p, _sz, _p]
 _lib.q4k_act_sums.restype = _int
 _lib.q4k_act_sums.argtypes = [_p, _p, _i64, _i64, _p, _sz, _p]
 _lib.q4k_gemm.restype = _int
-_lib.q4k_gemm.argtypes = [_p, _p, _p, _i64, _p, _i64, _i64, _p, _i64, _p]
+_lib.q4k_gemm.argtypes = [_p, _sz, _p, _sz, _p, _sz, _i64, _p, _sz, _i64, _i64, _p, _sz, _i64,
+                          _p]
 _lib.q4k_gemm_dots.restype = _int
-_lib.q4k_gemm_dots.argtypes = [_p, _i64, _p, _i64, _i64, _p, _p]
+_lib.q4k_gemm_dots.argtypes = [_p, _sz, _i64, _p, _sz, _i64, _i64] + _WIN + [_p, _sz, _p]
 _lib.q4k_launches.restype = ctypes.c_uint64
 _lib.q4k_launches.argtypes = []
 _lib.q6k_strerror.restype = ctypes.c_char_p
@@ -82,6 +86,14 @@ def _ptr(t):
 
 def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
+
+
+def _span(t):
+    """Bytes addressable from a tensor's first element to the end of its storage (the size of a
+    row-major operand whose rows are strided views of a larger buffer)."""
+    if t is None or not t.numel():
+        return 0
+    return t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
 
 
 def _flat(**bufs):
@@ -188,59 +200,54 @@ def q6k_expand_weights(w_raw, m, k, layout, w_out, stream=None):
                                    _stream(stream)), "q6k_expand_weights")
 
 
-def _check_operands(xq, da, n, w, layout, m, k):
-    """The C GEMM entry points take no buffer sizes: check them here before passing pointers."""
-    _flat(xq=xq, da=da, w=w)
-    if n <= 0 or m <= 0:
-        return
-    xb, db = q6k_act_bytes(n, k)
-    wb = q6k_weight_bytes(m, k, layout)
-    if xb == 0 or wb == 0:
-        return  # the library reports the shape / layout error itself
-    if _nbytes(xq) < xb or _nbytes(da) < db:
-        raise ValueError(f"activation buffers too small: need {xb} + {db} bytes")
-    if _nbytes(w) < wb:
-        raise ValueError(f"weight buffer too small: need {wb} bytes for layout {layout}")
-
-
-def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None):
-    """y f32 [n][ldy] = GEMM of prepared activations and weights."""
+def _y_operand(y, n, m, ldy):
+    """y f32 row-major [n][ldy]; -> ldy."""
     if y is not None and y.dtype != torch.float32:
         raise TypeError("y must be float32")
     if ldy is None:
         ldy = y.stride(0) if y is not None and y.dim() == 2 else m
-    _check_operands(xq, da, n, w, layout, m, k)
-    if y is not None and n > 0 and m > 0 and y.numel() < (n - 1) * ldy + m:
-        raise ValueError("y too small for n x ldy")
     if y is not None and y.dim() == 2 and y.numel() and y.stride(1) != 1:
         raise ValueError("y must be row-major")
-    _rows_fit("y", y, n, m, ldy)
-    _check(_lib.q6k_gemm(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(y), ldy,
-                         _stream(stream)), "q6k_gemm")
+    return ldy
 
 
-def q6k_gemm_subdots(xq, da, n, w, layout, m, k, dots, stream=None):
-    """Test-only: int32 sub-block dots [n][m][k/16] from the GEMM kernel source."""
+def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None):
+    """y f32 [n][ldy] = GEMM of prepared activations and weights."""
+    ldy = _y_operand(y, n, m, ldy)
+    _flat(xq=xq, da=da, w=w)
+    _check(_lib.q6k_gemm(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), n, _ptr(w), _nbytes(w),
+                         layout, m, k, _ptr(y), _span(y), ldy, _stream(stream)), "q6k_gemm")
+
+
+def _window(n, m, tok0, ntok, row0, nrow):
+    ntok = n - tok0 if ntok is None else ntok
+    nrow = m - row0 if nrow is None else nrow
+    return [int(tok0), int(ntok), int(row0), int(nrow)]
+
+
+def q6k_gemm_subdots(xq, da, n, w, layout, m, k, dots, tok0=0, ntok=None, row0=0, nrow=None,
+                     stream=None):
+    """Test-only: int32 sub-block dots [ntok][nrow][k/16] of a window of the problem (default: all
+    of it), from the GEMM kernel source launched as q6k_gemm launches it."""
     if dots is not None and dots.dtype != torch.int32:
         raise TypeError("dots must be int32")
-    _flat(dots=dots)
-    _check_operands(xq, da, n, w, layout, m, k)
-    if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 16):
-        raise ValueError("dots too small for n x m x k/16")
-    _check(_lib.q6k_gemm_subdots(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(dots),
-                                 _stream(stream)), "q6k_gemm_subdots")
+    _flat(xq=xq, da=da, w=w, dots=dots)
+    _check(_lib.q6k_gemm_subdots(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), n, _ptr(w),
+                                 _nbytes(w), layout, m, k, *_window(n, m, tok0, ntok, row0, nrow),
+                                 _ptr(dots), _nbytes(dots), _stream(stream)), "q6k_gemm_subdots")
 
 
-def q6k_gemm_chunkdots(xq, da, n, w, layout, m, k, dots, stream=None):
-    """Test-only: int32 per-chunk numerators [n][m][k/32] from the layout-2 kernel source."""
+def q6k_gemm_chunkdots(xq, da, n, w, layout, m, k, dots, tok0=0, ntok=None, row0=0, nrow=None,
+                       stream=None):
+    """Test-only: int32 per-chunk numerators [ntok][nrow][k/32] of a window of the problem
+    (default: all of it), from the layout-2 kernel source launched as q6k_gemm launches it."""
     if dots is not None and dots.dtype != torch.int32:
         raise TypeError("dots must be int32")
-    _flat(dots=dots)
-    _check_operands(xq, da, n, w, layout, m, k)
-    if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 32):
-        raise ValueError("dots too small for n x m x k/32")
-    _check(_lib.q6k_gemm_chunkdots(_ptr(xq), _ptr(da), n, _ptr(w), layout, m, k, _ptr(dots),
-                                   _stream(stream)), "q6k_gemm_chunkdots")
+    _flat(xq=xq, da=da, w=w, dots=dots)
+    _check(_lib.q6k_gemm_chunkdots(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), n, _ptr(w),
+                                   _nbytes(w), layout, m, k,
+                                   *_window(n, m, tok0, ntok, row0, nrow), _ptr(dots),
+                                   _nbytes(dots), _stream(stream)), "q6k_gemm_chunkdots")
 
 
 def q6k_stats():
@@ -276,46 +283,24 @@ def q4k_act_sums(xq, da, n, k, das, stream=None):
            "q4k_act_sums")
 
 
-def _check_q4_operands(xq, da, das, n, w, m, k):
-    _flat(xq=xq, da=da, das=das, w=w)
-    if n <= 0 or m <= 0:
-        return
-    xb, db = q6k_act_bytes(n, k)
-    wb = q4k_weight_bytes(m, k)
-    if xb == 0 or wb == 0:
-        return
-    if _nbytes(xq) < xb or (da is not None and _nbytes(da) < db) or (das is not None and _nbytes(das) < db):
-        raise ValueError("activation buffers too small")
-    if _nbytes(w) < wb:
-        raise ValueError(f"weight buffer too small: need {wb} bytes")
-
-
 def q4k_gemm(xq, da, das, n, w, m, k, y, ldy=None, stream=None):
     """y f32 [n][ldy] = q4_K GEMM of prepared activations (xq, da, das) and weights."""
-    if y is not None and y.dtype != torch.float32:
-        raise TypeError("y must be float32")
-    if ldy is None:
-        ldy = y.stride(0) if y is not None and y.dim() == 2 else m
-    _check_q4_operands(xq, da, das, n, w, m, k)
-    if y is not None and n > 0 and m > 0 and y.numel() < (n - 1) * ldy + m:
-        raise ValueError("y too small for n x ldy")
-    if y is not None and y.dim() == 2 and y.numel() and y.stride(1) != 1:
-        raise ValueError("y must be row-major")
-    _rows_fit("y", y, n, m, ldy)
-    _check(_lib.q4k_gemm(_ptr(xq), _ptr(da), _ptr(das), n, _ptr(w), m, k, _ptr(y), ldy,
-                         _stream(stream)), "q4k_gemm")
+    ldy = _y_operand(y, n, m, ldy)
+    _flat(xq=xq, da=da, das=das, w=w)
+    _check(_lib.q4k_gemm(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), _ptr(das), _nbytes(das), n,
+                         _ptr(w), _nbytes(w), m, k, _ptr(y), _span(y), ldy, _stream(stream)),
+           "q4k_gemm")
 
 
-def q4k_gemm_dots(xq, n, w, m, k, dots, stream=None):
-    """Test-only: int32 chunk dots [n][m][k/32] from the q4_K GEMM kernel source."""
+def q4k_gemm_dots(xq, n, w, m, k, dots, tok0=0, ntok=None, row0=0, nrow=None, stream=None):
+    """Test-only: int32 chunk dots [ntok][nrow][k/32] of a window of the problem (default: all of
+    it) from the q4_K GEMM kernel source."""
     if dots is not None and dots.dtype != torch.int32:
         raise TypeError("dots must be int32")
-    _flat(dots=dots)
-    _check_q4_operands(xq, None, None, n, w, m, k)
-    if dots is not None and n > 0 and m > 0 and dots.numel() < n * m * (k // 32):
-        raise ValueError("dots too small for n x m x k/32")
-    _check(_lib.q4k_gemm_dots(_ptr(xq), n, _ptr(w), m, k, _ptr(dots), _stream(stream)),
-           "q4k_gemm_dots")
+    _flat(xq=xq, w=w, dots=dots)
+    _check(_lib.q4k_gemm_dots(_ptr(xq), _nbytes(xq), n, _ptr(w), _nbytes(w), m, k,
+                              *_window(n, m, tok0, ntok, row0, nrow), _ptr(dots), _nbytes(dots),
+                              _stream(stream)), "q4k_gemm_dots")
 
 
 def q4k_launches():

@@ -350,6 +350,22 @@ struct TileWork {
   bool split;       // a piece of a split tile: add into y atomically
 };
 
+// Where the test exports store their integer dots: tokens [tok0, tok0 + ntok) x rows
+// [row0, row0 + nrow) of the full problem, as int32 [ntok][nrow][per], per = dots per row and
+// token (k/16 or k/32).  The window lies inside the problem; the kernel still computes every tile.
+struct DotsOut {
+  int32_t* p;
+  int64_t tok0, ntok, row0, nrow;
+};
+
+// Slot of (tok, row)'s dots in the window, or nullptr outside it.
+__device__ __forceinline__ int32_t* dots_at(const DotsOut& w, int64_t tok, int64_t row,
+                                            int64_t per) {
+  const int64_t ti = tok - w.tok0, ri = row - w.row0;
+  if ((uint64_t)ti >= (uint64_t)w.ntok || (uint64_t)ri >= (uint64_t)w.nrow) return nullptr;
+  return w.p + (ti * w.nrow + ri) * per;
+}
+
 template <bool XCD_ORDER>
 __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_t gy,
                                               uint32_t n_full, uint32_t pieces, int64_t nsb) {
@@ -538,8 +554,8 @@ __device__ __forceinline__ void expand_slot(uint8_t* slot, int wave, int lane) {
 template <bool SUBDOTS>
 __device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, long alo, long ahi,
                                            v4u b, v2f s, const float (&dav)[16], int lane,
-                                           int64_t c, int64_t T, int64_t R, int64_t n, int64_t m,
-                                           int64_t nchunk, int32_t* __restrict__ dots) {
+                                           int64_t c, int64_t T, int64_t R, int64_t nchunk,
+                                           const DotsOut& dots) {
   const long blo = (long)(((uint64_t)b.y << 32) | b.x);
   const long bhi = (long)(((uint64_t)b.w << 32) | b.z);
   const v16i lo_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo, blo, bias, 0, 0, 0);
@@ -550,10 +566,10 @@ __device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, l
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < n && mcol < m) {
-        int32_t* o = dots + (tok * m + mcol) * (2 * nchunk) + 2 * c;
-        o[0] = lo_d[r] - kBiasI;
-        o[1] = hi_d[r] - kBiasI;
+      int32_t* o = dots_at(dots, tok, mcol, 2 * nchunk);
+      if (o) {
+        o[2 * c] = lo_d[r] - kBiasI;
+        o[2 * c + 1] = hi_d[r] - kBiasI;
       }
     }
   } else {
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
                                                       const uint8_t* __restrict__ wscales,
                                                       int64_t n, int64_t m, int64_t nchunk,
                                                       float* __restrict__ y, int64_t ldy,
-                                                      int32_t* __restrict__ dots, uint32_t gx,
+                                                      DotsOut dots, uint32_t gx,
                                                       uint32_t gy, uint32_t n_full,
                                                       uint32_t pieces) {
   constexpr int kSlot = SlotSize<LAYOUT>::value;
@@ -666,11 +682,11 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
                            d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
     const long alo = (long)(((uint64_t)a.y << 32) | a.x);
     const long ahi = (long)(((uint64_t)a.w << 32) | a.z);
-    tile_chunk<SUBDOTS>(acc[0], bias, alo, ahi, b0, s0, dav, lane, c, T, R0 + 2 * rp, n, m,
-                        nchunk, dots);
+    tile_chunk<SUBDOTS>(acc[0], bias, alo, ahi, b0, s0, dav, lane, c, T, R0 + 2 * rp, nchunk,
+                        dots);
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b1), "+v"(s1)::"memory");
-    tile_chunk<SUBDOTS>(acc[1], bias, alo, ahi, b1, s1, dav, lane, c, T, R0 + 2 * rp + 1, n, m,
-                        nchunk, dots);
+    tile_chunk<SUBDOTS>(acc[1], bias, alo, ahi, b1, s1, dav, lane, c, T, R0 + 2 * rp + 1, nchunk,
+                        dots);
     slot_c = slot_next;
     slot_next = slot_next + 1 == kRing ? 0 : slot_next + 1;
     slot_issue = slot_issue + 1 == kRing ? 0 : slot_issue + 1;
@@ -775,7 +791,7 @@ struct FoldCtx {
   int64_t nchunk, c_begin;  // this piece's first chunk
   uint32_t c_end, s_end;    // and its chunk and super-block ends
   int64_t n, m, tok0, row0;
-  int32_t* dots;
+  DotsOut dots;
 };
 
 struct FoldState {
@@ -867,7 +883,8 @@ __device__ __forceinline__ void fold_rescale(float (&sb)[16], const float (&e)[1
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t row = k.row0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < k.n && row < k.m) k.dots[(tok * k.m + row) * k.nchunk + c] = (int32_t)e[r];
+      int32_t* o = dots_at(k.dots, tok, row, k.nchunk);
+      if (o) o[c] = (int32_t)e[r];
     }
   } else if (FIRST) {
 #pragma unroll
@@ -941,7 +958,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
     int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
-    int32_t* __restrict__ dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
+    DotsOut dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot];
   const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
   const bool split = tw.split;
@@ -1247,7 +1264,7 @@ struct Q4Ctx {
   uint8_t* sbuf;
   Q4Src src;
   int64_t nchunk, c_end, n, m, tok_base, col;
-  int32_t* dots;
+  DotsOut dots;
   uint32_t aa, bb, dd, ss;  // per-lane LDS addresses: A in slot 0, B in slot 0, da and SB (parity 0)
   int wave, lane;
   bool loads_a;
@@ -1314,7 +1331,8 @@ __device__ __forceinline__ void q4_step(const Q4Ctx& k, int64_t s, uint32_t par,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t tok = k.tok_base + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (tok < k.n && col < k.m) k.dots[(tok * k.m + col) * k.nchunk + c] = f[r] - kBiasI;
+        int32_t* o = dots_at(k.dots, tok, col, k.nchunk);
+        if (o) o[c] = f[r] - kBiasI;
       }
     } else {
       const float nb = -kBiasF * pr.x;
@@ -1334,7 +1352,7 @@ template <bool DOTS>
 __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da, const float* __restrict__ das,
     const uint8_t* __restrict__ wcodes, const float* __restrict__ wsb, int64_t n, int64_t m,
-    int64_t nchunk, float* __restrict__ y, int64_t ldy, int32_t* __restrict__ dots, uint32_t gx,
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, DotsOut dots, uint32_t gx,
     uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQ4Ring * kQ4Slot + 2 * kQ4SbBytes];
   Q4Ctx k;
@@ -1506,9 +1524,36 @@ q6k_status launch_status() {
 
 enum { kOutY = 0, kOutSubdots = 1, kOutChunkdots = 2 };
 
+// The f32 output [n][ldy] (only [0, n) x [0, m) written): ldy >= m, and the buffer holds the
+// last row's first m values.
+q6k_status check_y(const float* y, size_t y_bytes, int64_t n, int64_t m, int64_t ldy) {
+  if (!y) return Q6K_EINVAL;
+  if (ldy < m) return Q6K_EINVAL;
+  if (ldy > kMaxDim) return Q6K_ESIZE;
+  if (((uintptr_t)y & 3) != 0) return Q6K_EALIGN;
+  if ((uint64_t)(n - 1) > (SIZE_MAX / 4 - (uint64_t)m) / (uint64_t)ldy) return Q6K_ESIZE;
+  if (y_bytes / 4 < (uint64_t)(n - 1) * (uint64_t)ldy + (uint64_t)m) return Q6K_ESIZE;
+  return Q6K_OK;
+}
+
+// A test export's window of tokens x rows inside the n x m problem, and its int32 buffer of
+// ntok * nrow * per values.
+q6k_status check_window(const DotsOut& w, size_t dots_bytes, int64_t n, int64_t m, int64_t per) {
+  if (w.tok0 < 0 || w.ntok < 0 || w.row0 < 0 || w.nrow < 0) return Q6K_EINVAL;
+  if (w.tok0 > n || w.ntok > n - w.tok0 || w.row0 > m || w.nrow > m - w.row0) return Q6K_EINVAL;
+  if (w.ntok == 0 || w.nrow == 0) return Q6K_OK;
+  if (!w.p) return Q6K_EINVAL;
+  if (((uintptr_t)w.p & 3) != 0) return Q6K_EALIGN;
+  if ((uint64_t)w.ntok > SIZE_MAX / 4 / (uint64_t)w.nrow / (uint64_t)per) return Q6K_ESIZE;
+  if (dots_bytes / 4 < (uint64_t)w.ntok * (uint64_t)w.nrow * (uint64_t)per) return Q6K_ESIZE;
+  return Q6K_OK;
+}
+
 template <int OUT>
-q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w, int layout,
-                       int64_t m, int64_t k, float* y, int64_t ldy, int32_t* dots, void* stream) {
+q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                       int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
+                       float* y, size_t y_bytes, int64_t ldy, DotsOut dots, size_t dots_bytes,
+                       void* stream) {
   if (n < 0 || m < 0) return Q6K_EINVAL;
   if (!valid_layout(layout)) return Q6K_EINVAL;
   if (OUT == kOutSubdots && layout == Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
@@ -1523,13 +1568,18 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   if (n == 0 || m == 0) return Q6K_OK;
   if (!xq || !da || !w) return Q6K_EINVAL;
   if (!aligned16(xq) || !aligned16(da) || !aligned16(w)) return Q6K_EALIGN;
+  size_t need_x, need_d, codes_bytes, scales_bytes;
+  if (!act_sizes(n, k, &need_x, &need_d)) return Q6K_ESIZE;
+  if (!weight_sizes(m, k, layout, &codes_bytes, &scales_bytes)) return Q6K_ESIZE;
+  if (xq_bytes < need_x || da_bytes < need_d || w_bytes < codes_bytes + scales_bytes)
+    return Q6K_ESIZE;
   if (OUT != kOutY) {
-    if (!dots) return Q6K_EINVAL;
-    if (((uintptr_t)dots & 3) != 0) return Q6K_EALIGN;
+    const q6k_status ws = check_window(dots, dots_bytes, n, m, OUT == kOutSubdots ? k / 16 : k / 32);
+    if (ws != Q6K_OK) return ws;
+    if (dots.ntok == 0 || dots.nrow == 0) return Q6K_OK;
   } else {
-    if (!y) return Q6K_EINVAL;
-    if (ldy < m) return Q6K_EINVAL;
-    if (((uintptr_t)y & 3) != 0) return Q6K_EALIGN;
+    const q6k_status ys = check_y(y, y_bytes, n, m, ldy);
+    if (ys != Q6K_OK) return ys;
   }
   const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
   // output tiles of tile_tok tokens x 128 rows
@@ -1537,8 +1587,6 @@ q6k_status gemm_common(const void* xq, const float* da, int64_t n, const void* w
   const int64_t gx = np / tile_tok, gy = mp / kWgRow;
   if (gy > INT32_MAX || gx > INT32_MAX) return Q6K_ESIZE;
   const int64_t nchunk = k / 32;
-  size_t codes_bytes, scales_bytes;
-  weight_sizes(m, k, layout, &codes_bytes, &scales_bytes);
   const uint8_t* wc = static_cast<const uint8_t*>(w);
   const uint8_t* ws = wc + codes_bytes;
   const uint8_t* a = static_cast<const uint8_t*>(xq);
@@ -1597,9 +1645,10 @@ q6k_status quantize_common(const float* x, const float* up, int64_t n, int64_t k
 }
 
 template <bool DOTS>
-q6k_status q4k_gemm_common(const void* xq, const float* da, const float* das, int64_t n,
-                           const void* w, int64_t m, int64_t k, float* y, int64_t ldy,
-                           int32_t* dots, void* stream) {
+q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                           const float* das, size_t das_bytes, int64_t n, const void* w,
+                           size_t w_bytes, int64_t m, int64_t k, float* y, size_t y_bytes,
+                           int64_t ldy, DotsOut dots, size_t dots_bytes, void* stream) {
   if (n < 0 || m < 0) return Q6K_EINVAL;
   if (k <= 0 || k % 256) return Q6K_ESHAPE;
   if (n > kMaxDim || m > kMaxDim || k > kMaxDim) return Q6K_ESIZE;
@@ -1608,13 +1657,19 @@ q6k_status q4k_gemm_common(const void* xq, const float* da, const float* das, in
   if (!xq || !w || (!DOTS && (!da || !das))) return Q6K_EINVAL;
   if (!aligned16(xq) || !aligned16(w) || (!DOTS && (!aligned16(da) || !aligned16(das))))
     return Q6K_EALIGN;
+  size_t need_x, need_d;
+  if (!act_sizes(n, k, &need_x, &need_d)) return Q6K_ESIZE;
+  const size_t need_w = q4k_weight_bytes(m, k);
+  if (need_w == 0) return Q6K_ESIZE;
+  if (xq_bytes < need_x || w_bytes < need_w) return Q6K_ESIZE;
+  if (!DOTS && (da_bytes < need_d || das_bytes < need_d)) return Q6K_ESIZE;
   if (DOTS) {
-    if (!dots) return Q6K_EINVAL;
-    if (((uintptr_t)dots & 3) != 0) return Q6K_EALIGN;
+    const q6k_status ws = check_window(dots, dots_bytes, n, m, k / 32);
+    if (ws != Q6K_OK) return ws;
+    if (dots.ntok == 0 || dots.nrow == 0) return Q6K_OK;
   } else {
-    if (!y) return Q6K_EINVAL;
-    if (ldy < m) return Q6K_EINVAL;
-    if (((uintptr_t)y & 3) != 0) return Q6K_EALIGN;
+    const q6k_status ys = check_y(y, y_bytes, n, m, ldy);
+    if (ys != Q6K_OK) return ys;
   }
   const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
   const int64_t gx = np / (kTile * 2), gy = mp / kWgRow;
@@ -1689,14 +1744,19 @@ q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, f
   return launch_status();
 }
 
-q6k_status q4k_gemm(const void* xq, const float* da, const float* das, int64_t n, const void* w,
-                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream) {
-  return q4k_gemm_common<false>(xq, da, das, n, w, m, k, y, ldy, nullptr, stream);
+q6k_status q4k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                    const float* das, size_t das_bytes, int64_t n, const void* w, size_t w_bytes,
+                    int64_t m, int64_t k, float* y, size_t y_bytes, int64_t ldy, void* stream) {
+  return q4k_gemm_common<false>(xq, xq_bytes, da, da_bytes, das, das_bytes, n, w, w_bytes, m, k,
+                                y, y_bytes, ldy, DotsOut{nullptr, 0, 0, 0, 0}, 0, stream);
 }
 
-q6k_status q4k_gemm_dots(const void* xq, int64_t n, const void* w, int64_t m, int64_t k,
-                         int32_t* dots, void* stream) {
-  return q4k_gemm_common<true>(xq, nullptr, nullptr, n, w, m, k, nullptr, 0, dots, stream);
+q6k_status q4k_gemm_dots(const void* xq, size_t xq_bytes, int64_t n, const void* w,
+                         size_t w_bytes, int64_t m, int64_t k, int64_t tok0, int64_t ntok,
+                         int64_t row0, int64_t nrow, int32_t* dots, size_t dots_bytes,
+                         void* stream) {
+  return q4k_gemm_common<true>(xq, xq_bytes, nullptr, 0, nullptr, 0, n, w, w_bytes, m, k, nullptr,
+                               0, 0, DotsOut{dots, tok0, ntok, row0, nrow}, dots_bytes, stream);
 }
 
 uint64_t q4k_launches(void) { return g_q4k_launches.load(std::memory_order_relaxed); }
@@ -1773,19 +1833,29 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
   return launch_status();
 }
 
-q6k_status q6k_gemm(const void* xq, const float* da, int64_t n, const void* w, int layout,
-                    int64_t m, int64_t k, float* y, int64_t ldy, void* stream) {
-  return gemm_common<kOutY>(xq, da, n, w, layout, m, k, y, ldy, nullptr, stream);
+q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                    int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
+                    float* y, size_t y_bytes, int64_t ldy, void* stream) {
+  return gemm_common<kOutY>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k, y, y_bytes,
+                            ldy, DotsOut{nullptr, 0, 0, 0, 0}, 0, stream);
 }
 
-q6k_status q6k_gemm_subdots(const void* xq, const float* da, int64_t n, const void* w, int layout,
-                            int64_t m, int64_t k, int32_t* dots, void* stream) {
-  return gemm_common<kOutSubdots>(xq, da, n, w, layout, m, k, nullptr, 0, dots, stream);
+q6k_status q6k_gemm_subdots(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                            int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
+                            int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
+                            int32_t* dots, size_t dots_bytes, void* stream) {
+  return gemm_common<kOutSubdots>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k,
+                                  nullptr, 0, 0, DotsOut{dots, tok0, ntok, row0, nrow},
+                                  dots_bytes, stream);
 }
 
-q6k_status q6k_gemm_chunkdots(const void* xq, const float* da, int64_t n, const void* w,
-                              int layout, int64_t m, int64_t k, int32_t* dots, void* stream) {
-  return gemm_common<kOutChunkdots>(xq, da, n, w, layout, m, k, nullptr, 0, dots, stream);
+q6k_status q6k_gemm_chunkdots(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                              int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
+                              int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
+                              int32_t* dots, size_t dots_bytes, void* stream) {
+  return gemm_common<kOutChunkdots>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k,
+                                    nullptr, 0, 0, DotsOut{dots, tok0, ntok, row0, nrow},
+                                    dots_bytes, stream);
 }
 
 const char* q6k_strerror(int status) {

@@ -111,7 +111,8 @@ def workload(name):
 # ------------------------------------------------------------------------------------------------
 # Device-side generators with the same distributions, for workloads too large to draw on the host
 # (the 32-layer sweep).  They draw from torch's seeded CUDA generator, so their values differ from
-# the numpy generators above; tests that compare against the oracle use the numpy ones.
+# the numpy generators above; the sweep's parity tests copy these device draws to the host and
+# hand them to the oracle.
 # ------------------------------------------------------------------------------------------------
 def weights_torch(m, k, seed, device, sc_lo=-32, sc_hi=31):
     """Raw q6_K blocks as a flat uint8 device tensor of m*(k/256)*210 bytes."""
@@ -157,3 +158,13 @@ def sweep_layer(layer, kind):
     if kind == "attn_v":
         return dict(n=3314, m=4096, k=4096, seed=1000 + layer, x="outlier")
     return dict(n=3314, m=4096, k=11008, seed=2000 + layer, x="swiglu")
+
+
+def sweep_inputs_torch(layer, kind, device):
+    """-> (raw weights flat uint8, activations f32 [n][k], n, m, k) of one sweep GEMM, drawn on the
+    device; each draw has its own seeded generator, so a layer's inputs are the same whatever was
+    drawn before them (the benchmark and the parity tests get identical values)."""
+    s = sweep_layer(layer, kind)
+    raw = weights_torch(s["m"], s["k"], s["seed"], device)
+    x = activations_torch(s["n"], s["k"], s["seed"], device, s["x"])
+    return raw, x, s["n"], s["m"], s["k"]

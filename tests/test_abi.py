@@ -79,21 +79,47 @@ def test_expand_errors(args, status):
     assert lib().q6k_expand_weights(*args) == status
 
 
-@pytest.mark.parametrize("args,status", [
-    ((FAKE, FAKE, 4, FAKE, 3, 8, 256, FAKE, 8, None), -1),      # layout
-    ((FAKE, FAKE, 4, FAKE, 1, 8, 0, FAKE, 8, None), -2),        # k = 0
-    ((FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE, 7, None), -1),      # ldy < m
-    ((FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE + 2, 8, None), -3),  # y not 4-byte aligned
-    ((FAKE, FAKE + 4, 4, FAKE, 1, 8, 256, FAKE, 10, None), -3),  # misaligned da
-    ((FAKE + 8, FAKE, 4, FAKE, 1, 8, 256, FAKE, 8, None), -3),
-    ((None, FAKE, 4, FAKE, 1, 8, 256, FAKE, 8, None), -1),
-    ((FAKE, FAKE, 4, FAKE, 1, 8, 256, None, 8, None), -1),
-    ((FAKE, FAKE, 0, FAKE, 1, 8, 256, FAKE, 8, None), 0),       # n = 0: no-op
-    ((FAKE, FAKE, 4, FAKE, 1, 0, 256, FAKE, 8, None), 0),       # m = 0: no-op
-    ((FAKE, FAKE, -4, FAKE, 1, 8, 256, FAKE, 8, None), -1),
+BIG = 1 << 40  # a buffer size that passes every size check
+
+
+def gemm_args(xq=FAKE, xqb=BIG, da=FAKE, dab=BIG, n=4, w=FAKE, wb=BIG, layout=1, m=8, k=256,
+              y=FAKE, yb=BIG, ldy=8):
+    return (xq, xqb, da, dab, n, w, wb, layout, m, k, y, yb, ldy, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=3), -1),
+    (dict(k=0), -2),
+    (dict(ldy=7), -1),                 # ldy < m
+    (dict(y=FAKE + 2), -3),            # y not 4-byte aligned
+    (dict(da=FAKE + 4, ldy=10), -3),   # misaligned da
+    (dict(xq=FAKE + 8), -3),
+    (dict(xq=None), -1),
+    (dict(y=None), -1),
+    (dict(n=0), 0),                    # n = 0: no-op
+    (dict(m=0), 0),                    # m = 0: no-op
+    (dict(n=-4), -1),
+    # buffer sizes (n = 4 tokens pad to 128: xq 128*256 B, da 128*8*4 B; m = 8 rows pad to 128)
+    (dict(xqb=128 * 256 - 1), -4),
+    (dict(dab=128 * 8 * 4 - 1), -4),
+    (dict(wb=128 * 256 * 5 // 4 - 1), -4),             # layout 1: 1.25 B per weight
+    (dict(layout=2, wb=128 * 256 * 2 + 128 * 4 - 1), -4),
+    (dict(layout=0, wb=128 * 256 * 7 // 8 - 1), -4),
+    (dict(yb=4 * (3 * 8 + 8) - 1), -4),                # y: (n-1)*ldy + m floats
+    (dict(yb=4 * (3 * 10 + 8) - 1, ldy=10), -4),
+    (dict(ldy=(1 << 40) + 1), -4),
 ])
-def test_gemm_errors(args, status):
-    assert lib().q6k_gemm(*args) == status
+def test_gemm_errors(kw, status):
+    assert lib().q6k_gemm(*gemm_args(**kw)) == status
+
+
+def test_gemm_one_byte_short_weights():
+    # every other buffer at its exact size, the weights one byte short (a passing call would
+    # launch on these fake pointers, so only the failing side is checked)
+    L = lib()
+    for layout, wb in ((0, 128 * 256 * 7 // 8), (1, 128 * 256 * 5 // 4), (2, 128 * 256 * 2 + 128 * 4)):
+        assert L.q6k_gemm(*gemm_args(layout=layout, wb=wb - 1, xqb=128 * 256, dab=4096,
+                                     yb=4 * 32)) == -4
 
 
 def test_gemm_size_limits():
@@ -101,28 +127,42 @@ def test_gemm_size_limits():
     # planes per row tile), layouts 0/1 k < 2^26; dimensions beyond 2^40 are rejected outright
     L = lib()
     for layout, kmax in ((2, 1 << 25), (1, 1 << 26), (0, 1 << 26)):
-        assert L.q6k_gemm(FAKE, FAKE, 4, FAKE, layout, 8, kmax, FAKE, 8, None) == -4
-        assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 1 << 25, FAKE, None) == -4
-    assert L.q6k_gemm(FAKE, FAKE, (1 << 40) + 1, FAKE, 2, 8, 256, FAKE, 8, None) == -4
-    assert L.q6k_gemm(FAKE, FAKE, 4, FAKE, 2, (1 << 40) + 1, 256, FAKE, (1 << 40) + 1, None) == -4
-    assert L.q4k_gemm(FAKE, FAKE, FAKE, 4, FAKE, 8, 1 << 26, FAKE, 8, None) == -4
+        assert L.q6k_gemm(*gemm_args(layout=layout, k=kmax)) == -4
+    assert L.q6k_gemm_chunkdots(FAKE, BIG, FAKE, BIG, 4, FAKE, BIG, 2, 8, 1 << 25, 0, 4, 0, 8,
+                                FAKE, BIG, None) == -4
+    assert L.q6k_gemm(*gemm_args(layout=2, n=(1 << 40) + 1)) == -4
+    assert L.q6k_gemm(*gemm_args(layout=2, m=(1 << 40) + 1, ldy=(1 << 40) + 1)) == -4
+    assert L.q4k_gemm(FAKE, BIG, FAKE, BIG, FAKE, BIG, 4, FAKE, BIG, 8, 1 << 26, FAKE, BIG, 8,
+                      None) == -4
+
+
+def dots_args(layout, win=(0, 4, 0, 8), dots=FAKE, dotsb=BIG, k=256, n=4, m=8):
+    return (FAKE, BIG, FAKE, BIG, n, FAKE, BIG, layout, m, k, *win, dots, dotsb, None)
 
 
 def test_subdots_errors():
     L = lib()
-    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, None, None) == -1
-    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 256, FAKE + 2, None) == -3
-    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 1, 8, 100, FAKE, None) == -2
-    assert L.q6k_gemm_subdots(FAKE, FAKE, 4, FAKE, 2, 8, 256, FAKE, None) == -1  # layout 2
+    assert L.q6k_gemm_subdots(*dots_args(1, dots=None)) == -1
+    assert L.q6k_gemm_subdots(*dots_args(1, dots=FAKE + 2)) == -3
+    assert L.q6k_gemm_subdots(*dots_args(1, k=100)) == -2
+    assert L.q6k_gemm_subdots(*dots_args(2)) == -1  # layout 2 never forms them
+    # the window must lie inside the problem, and the buffer hold ntok * nrow * k/16 int32
+    assert L.q6k_gemm_subdots(*dots_args(1, win=(1, 4, 0, 8))) == -1
+    assert L.q6k_gemm_subdots(*dots_args(1, win=(0, 4, 4, 5))) == -1
+    assert L.q6k_gemm_subdots(*dots_args(1, win=(-1, 2, 0, 8))) == -1
+    assert L.q6k_gemm_subdots(*dots_args(1, win=(2, 2, 3, 5), dotsb=4 * 2 * 5 * 16 - 1)) == -4
+    assert L.q6k_gemm_subdots(*dots_args(1, win=(2, 0, 3, 5), dots=None)) == 0  # empty window
 
 
 def test_chunkdots_errors():
     L = lib()
-    assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 256, None, None) == -1
-    assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 256, FAKE + 2, None) == -3
-    assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, 2, 8, 100, FAKE, None) == -2
+    assert L.q6k_gemm_chunkdots(*dots_args(2, dots=None)) == -1
+    assert L.q6k_gemm_chunkdots(*dots_args(2, dots=FAKE + 2)) == -3
+    assert L.q6k_gemm_chunkdots(*dots_args(2, k=100)) == -2
     for layout in (0, 1, 3):  # only layout 2 forms the per-chunk numerators
-        assert L.q6k_gemm_chunkdots(FAKE, FAKE, 4, FAKE, layout, 8, 256, FAKE, None) == -1
+        assert L.q6k_gemm_chunkdots(*dots_args(layout)) == -1
+    assert L.q6k_gemm_chunkdots(*dots_args(2, win=(0, 4, 0, 8), dotsb=4 * 4 * 8 * 8 - 1)) == -4
+    assert L.q6k_gemm_chunkdots(*dots_args(2, win=(0, 5, 0, 8))) == -1
 
 
 def test_strerror_and_stats():
@@ -159,11 +199,19 @@ def test_q4k_sizes_and_errors():
     assert L.q4k_expand_weights(None, 0, 256, None, 0, None) == 0
     assert L.q4k_act_sums(FAKE, FAKE, 4, 256, FAKE, 10, None) == -4
     assert L.q4k_act_sums(FAKE, FAKE + 4, 4, 256, FAKE, 1 << 30, None) == -3
-    assert L.q4k_gemm(FAKE, FAKE, None, 4, FAKE, 8, 256, FAKE, 8, None) == -1      # null das
-    assert L.q4k_gemm(FAKE, FAKE, FAKE, 4, FAKE, 8, 256, FAKE, 7, None) == -1      # ldy < m
-    assert L.q4k_gemm(FAKE, FAKE, FAKE, 4, FAKE, 8, 100, FAKE, 8, None) == -2
-    assert L.q4k_gemm(FAKE, FAKE, FAKE, 0, FAKE, 8, 256, FAKE, 8, None) == 0
-    assert L.q4k_gemm_dots(FAKE, 4, FAKE, 8, 256, None, None) == -1
+    def q4(xq=FAKE, da=FAKE, das=FAKE, n=4, k=256, ldy=8, wb=BIG, yb=BIG, dab=BIG):
+        return L.q4k_gemm(xq, BIG, da, dab, das, dab, n, FAKE, wb, 8, k, FAKE, yb, ldy, None)
+    assert q4(das=None) == -1                     # null das
+    assert q4(ldy=7) == -1                        # ldy < m
+    assert q4(k=100) == -2
+    assert q4(n=0) == 0
+    assert q4(wb=128 * 256 + 128 * 8 * 8 - 1) == -4
+    assert q4(dab=128 * 8 * 4 - 1) == -4
+    assert q4(yb=4 * (3 * 8 + 8) - 1) == -4
+    assert L.q4k_gemm_dots(FAKE, BIG, 4, FAKE, BIG, 8, 256, 0, 4, 0, 8, None, BIG, None) == -1
+    assert L.q4k_gemm_dots(FAKE, BIG, 4, FAKE, BIG, 8, 256, 0, 4, 0, 9, FAKE, BIG, None) == -1
+    assert L.q4k_gemm_dots(FAKE, BIG, 4, FAKE, BIG, 8, 256, 0, 4, 0, 8, FAKE, 4 * 4 * 8 * 8 - 1,
+                           None) == -4
     assert q6k.q4k_launches() >= 0
 
 
@@ -195,6 +243,3 @@ def test_binding_rejects_views_that_outrun_their_storage():
     with pytest.raises(ValueError, match="past its storage"):
         q6k.q6k_quantize_act(torch.zeros((n, k)), torch.zeros(xb, dtype=torch.uint8), da,
                              ldx=2 * k)
-    with pytest.raises(ValueError, match="past its storage"):
-        q6k.q6k_gemm(torch.zeros(xb, dtype=torch.uint8), da, n, w, 2, m, k,
-                     torch.zeros(1, dtype=torch.float32).expand(n * m))
