@@ -50,11 +50,13 @@
  *     scales f32 : at byte offset MP*k, float ((R*nchunk + c)*32 + p)*2 + h = d*sc[2c + h] of row
  *                  32R + p (sub-block index counted along the whole row)
  *   layout 0 (Q6K_LAYOUT_PACKED), 6 bits per weight plus 4 scale bytes per 32 weights:
- *     codes      : 12 bytes at ((R*nchunk + c)*64 + l)*12 for row 32R + p; with a_e (e = 0..7) the
- *                  6-bit codes at k = 32c + 8g + e and b_e those at k = 32c + 16 + 8g + e:
- *                  byte t (t = 0..3)   = (a_t & 15) | (a_{t+4} & 15) << 4
- *                  byte 4+t            = (b_t & 15) | (b_{t+4} & 15) << 4
- *                  byte 8+t            = a_t>>4 | (a_{t+4}>>4) << 2 | (b_t>>4) << 4 | (b_{t+4}>>4) << 6
+ *     codes      : 12 bytes at ((R*nchunk + c)*64 + l)*12 for row 32R + p, three little-endian
+ *                  words X, Y, Z; with a_e (e = 0..7) the 6-bit codes at k = 32c + 8g + e and
+ *                  b_e those at k = 32c + 16 + 8g + e, byte t (t = 0..3) of
+ *                    X = a_t << 2     | (b_{t+4} & 3)
+ *                    Y = a_{t+4} << 2 | ((b_{t+4} >> 2) & 3)
+ *                    Z = b_t << 2     | (b_{t+4} >> 4)
+ *                  (the GEMM turns a byte s into (s & 0xFC) ^ 0x80 = 4 * (q - 32))
  *     scales     : at byte offset MP*k*3/4, 4 bytes at ((R*nchunk + c)*32 + p)*4:
  *                  int8 sc[2c], int8 sc[2c+1], f16 d (little-endian) of row 32R + p
  *   layout 2 (Q6K_LAYOUT_FOLDED), the int8 sub-block scale applied to the codes ahead of time:

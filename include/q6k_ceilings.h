@@ -45,7 +45,9 @@ enum {
 };
 enum {
   Q6C_TILEOP_FOLDED = 0,     /* per tile and chunk: 2 x 32x32x32 int8 MFMA + 48 VALU (fold, rescale) */
-  Q6C_TILEOP_HALVES = 1      /* per tile and chunk: 2 x 32x32x16 int8 MFMA + 64 VALU (two halves) */
+  Q6C_TILEOP_HALVES = 1,     /* per tile and chunk: 2 x 32x32x16 int8 MFMA + 64 VALU (two halves) */
+  Q6C_TILEOP_FOLDED_PIPE = 2, /* FOLDED with each tile's MFMAs issued half a step ahead of its fold */
+  Q6C_TILEOP_ZERO_C = 3       /* FOLDED's instruction mix, MFMA accumulator input an inline zero */
 };
 enum { Q6C_STREAM_READ = 0, Q6C_STREAM_COPY = 1 };
 enum {

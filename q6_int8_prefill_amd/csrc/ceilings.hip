@@ -197,7 +197,72 @@ __global__ __launch_bounds__(256, 2) void tileop_kernel(int iters, uint64_t* out
   for (int u = 0; u < 2; ++u)
     for (int r = 0; r < 16; ++r) acc[u][r] = sb[u][r] = 0.0f;
   float da0 = 1.0f + lane * 1e-3f, da1 = 0.5f + lane * 1e-3f;
-  if (KIND == Q6C_TILEOP_FOLDED) {
+  if (KIND == Q6C_TILEOP_FOLDED_PIPE) {
+    // the folded tile operation with each tile's MFMAs issued one half-step ahead of its fold:
+    // while the wave folds one tile, the matrix core works on the other tile's products
+    v16i bias_lo, bias_hi;
+    for (int r = 0; r < 16; ++r) {
+      bias_lo[r] = kBiasI;
+      bias_hi[r] = kBiasHiI;
+    }
+    float kk = -65.0f * kBiasF;
+    asm("" : "+v"(kk));
+    v16i fh0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, bias_hi, 0, 0, 0);
+    v16i fl0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1, b0, bias_lo, 0, 0, 0);
+    for (int i = 0; i < iters; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      v16i fh1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, bias_hi, 0, 0, 0);
+      v16i fl1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1, b1, bias_lo, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = __int_as_float(fh0[r]) + kk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] += __int_as_float(fl0[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sb[0][r] = __builtin_fmaf(e[r], da0, sb[0][r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      fh0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, bias_hi, 0, 0, 0);
+      fl0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1, b0, bias_lo, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = __int_as_float(fh1[r]) + kk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] += __int_as_float(fl1[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sb[1][r] = __builtin_fmaf(e[r], da1, sb[1][r]);
+      }
+      asm volatile("" : "+v"(da0), "+v"(da1));
+    }
+    for (int r = 0; r < 16; ++r) sb[0][r] += __int_as_float(fh0[r] ^ fl0[r]);
+  } else if (KIND == Q6C_TILEOP_ZERO_C) {
+    // the folded tile operation's instruction mix with the MFMAs' accumulator input an inline
+    // zero instead of bias registers (results not meaningful: probes the cost of reading C)
+    float kk = -65.0f * kBiasF;
+    asm("" : "+v"(kk));
+    const v16i zero = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v4i x = u ? b1 : b0;
+        v16i fh = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, x, zero, 0, 0, 0);
+        v16i fl = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1, x, zero, 0, 0, 0);
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = __int_as_float(fh[r]) + kk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] += __int_as_float(fl[r]);
+        const float dav = u ? da1 : da0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sb[u][r] = __builtin_fmaf(e[r], dav, sb[u][r]);
+      }
+      asm volatile("" : "+v"(da0), "+v"(da1));
+    }
+  } else if (KIND == Q6C_TILEOP_FOLDED) {
     v16i bias_lo, bias_hi;
     for (int r = 0; r < 16; ++r) {
       bias_lo[r] = kBiasI;
@@ -452,6 +517,10 @@ int q6c_tileop(int kind, int iters, int waves_per_simd, uint64_t* out, size_t ou
       return launch_probe(tileop_kernel<Q6C_TILEOP_FOLDED>, iters, waves_per_simd, out, out_bytes, stream);
     case Q6C_TILEOP_HALVES:
       return launch_probe(tileop_kernel<Q6C_TILEOP_HALVES>, iters, waves_per_simd, out, out_bytes, stream);
+    case Q6C_TILEOP_ZERO_C:
+      return launch_probe(tileop_kernel<Q6C_TILEOP_ZERO_C>, iters, waves_per_simd, out, out_bytes, stream);
+    case Q6C_TILEOP_FOLDED_PIPE:
+      return launch_probe(tileop_kernel<Q6C_TILEOP_FOLDED_PIPE>, iters, waves_per_simd, out, out_bytes, stream);
     default:
       return Q6K_EINVAL;
   }

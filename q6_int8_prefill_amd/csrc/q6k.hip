@@ -287,7 +287,9 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint8_t* __restrict__
     if (R * kTile + p >= m) s.x = s.y = 0.0f;
     reinterpret_cast<float2*>(scales)[tc * 32 + p] = s;
   } else {
-    // lane p (g = 0) takes k 8g + e = e and 16 + e; lane p + 32 (g = 1) takes 8 + e and 24 + e
+    // lane p (g = 0) takes k 8g + e = e and 16 + e; lane p + 32 (g = 1) takes 8 + e and 24 + e.
+    // Three words X, Y, Z hold the codes a_0..3, a_4..7, b_0..3 as q << 2 (bits 2-7 of each
+    // byte); bits 0-1 of byte t of X, Y, Z hold bits 0-1, 2-3, 4-5 of b_{4+t}.
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int* a = code + 8 * g;       // half 0 codes a_0..a_7
@@ -295,11 +297,10 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint8_t* __restrict__
       uint32_t w0 = 0, w1 = 0, w2 = 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        w0 |= (uint32_t)((a[t] & 15) | ((a[t + 4] & 15) << 4)) << (8 * t);
-        w1 |= (uint32_t)((b[t] & 15) | ((b[t + 4] & 15) << 4)) << (8 * t);
-        w2 |= (uint32_t)((a[t] >> 4) | ((a[t + 4] >> 4) << 2) | ((b[t] >> 4) << 4) |
-                         ((b[t + 4] >> 4) << 6))
-              << (8 * t);
+        const int f = b[t + 4];
+        w0 |= (uint32_t)((a[t] << 2) | (f & 3)) << (8 * t);
+        w1 |= (uint32_t)((a[t + 4] << 2) | ((f >> 2) & 3)) << (8 * t);
+        w2 |= (uint32_t)((b[t] << 2) | (f >> 4)) << (8 * t);
       }
       uint32_t* dst = reinterpret_cast<uint32_t*>(codes + (tc * 64 + p + 32 * g) * kPackBytes);
       dst[0] = w0;
@@ -312,12 +313,18 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint8_t* __restrict__
   }
 }
 
-// Layout 0 in-register expand of one lane's 16 codes into the two 8-byte MFMA fragments of
-// centered int8.  Per byte: q = nibble | field << 4 (0..63); q - 32 = (q + 0x60) ^ 0x80, which
-// neither carries nor borrows across bytes for q <= 63.
-__device__ __forceinline__ uint32_t center4(uint32_t nib, uint32_t fld) {
-  const uint32_t q = (nib & 0x0F0F0F0Fu) | ((fld & 0x03030303u) << 4);
-  return (q + 0x60606060u) ^ 0x80808080u;
+// Layout 0 in-register expand of one lane's 16 codes into the two 8-byte MFMA fragments, as
+// centered int8 times 4: a byte s = (q << 2) | x (q the 6-bit code, x two bits stored for the
+// fourth word) becomes (s & 0xFC) ^ 0x80 = 4q - 128 = 4 (q - 32) in [-128, 124] -- two SWAR
+// operations per word, no carries -- and the fourth word's bytes are gathered from the x bits of
+// the other three and then treated alike.  The MFMA then yields 4 D exactly (|4 D| < 2^22, so the
+// float bias trick still holds), and the staged d*sc is d*sc/4 (exact: a power of two).
+__device__ __forceinline__ uint32_t center4x4(uint32_t s) { return (s & 0xFCFCFCFCu) ^ 0x80808080u; }
+
+__device__ __forceinline__ uint32_t fourth4x4(uint32_t x, uint32_t y, uint32_t z) {
+  const uint32_t lo = 0x03030303u;
+  const uint32_t q = (x & lo) | ((y & lo) << 2) | ((z & lo) << 4);  // b_4..7, 6 bits each
+  return ((q << 2) & 0xFCFCFCFCu) ^ 0x80808080u;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -366,6 +373,9 @@ __device__ __forceinline__ int32_t* dots_at(const DotsOut& w, int64_t tok, int64
   return w.p + (ti * w.nrow + ri) * per;
 }
 
+// The result is uniform across the workgroup; the divisions in it run on the vector ALU, so each
+// field goes through readfirstlane to tell the compiler (and keep everything derived from it in
+// scalar registers).
 template <bool XCD_ORDER>
 __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_t gy,
                                               uint32_t n_full, uint32_t pieces, int64_t nsb) {
@@ -382,6 +392,11 @@ __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_
   }
   w.s0 = nsb * piece / npieces;
   w.s1 = nsb * (piece + 1) / npieces;
+  w.bx = __builtin_amdgcn_readfirstlane(w.bx);
+  w.by = __builtin_amdgcn_readfirstlane(w.by);
+  w.s0 = __builtin_amdgcn_readfirstlane((int)w.s0);
+  w.s1 = __builtin_amdgcn_readfirstlane((int)w.s1);
+  w.split = __builtin_amdgcn_readfirstlane((int)w.split) != 0;
   return w;
 }
 
@@ -423,15 +438,17 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
 // d*sc, and, for waves 0 and 1,
 // token tile w's activations and da.  Loads run kRing-1 chunks ahead of the compute.  Per chunk c
 // a wave waits for its own loads of chunk c+1 (s_waitcnt vmcnt), layout 0 expands its row tile's
-// 6-bit codes of chunk c+1 into centered int8 and forms d*sc in the slot, one workgroup barrier
-// makes the slot visible and frees the slot of chunk c-1, the loads of chunk c+kRing-1 are issued,
-// and chunk c is computed.  LDS reads and writes are inline assembly with explicit waits: the
-// compiler would otherwise wait for every outstanding direct-to-LDS load before each LDS access,
-// which would serialize the ring.
+// 6-bit codes of chunk c+1 into int8 (4 x the centered codes) and forms d*sc/4 in the slot, one
+// workgroup barrier makes the slot visible and frees the slot of chunk c-1, the loads of chunk
+// c+kRing-1 are issued, and chunk c is computed.  The chunk loop is unrolled over the ring, so
+// every slot address is a per-lane base register plus an immediate offset (no address arithmetic
+// per chunk).  LDS reads and writes are inline assembly with explicit waits: the compiler would
+// otherwise wait for every outstanding direct-to-LDS load before each LDS access, which would
+// serialize the ring.
 //
 // Per chunk and output tile: two v_mfma_i32_32x32x16_i8 (halves 0 and 1), each started from the
-// bit pattern of 1.5*2^23 so that the int32 result D is read as the float 1.5*2^23 + D exactly
-// (|D| <= 16*127*32 < 2^22).  The rescale of each half is then
+// bit pattern of 1.5*2^23 so that the int32 result D (4 D on layout 0) is read as the float
+// 1.5*2^23 + D exactly (|4 D| <= 4*16*127*32 < 2^22).  The rescale of each half is then
 //     t = fma(F, dsc, -1.5*2^23*dsc)  (= D*dsc rounded once; the bias product is exact)
 //     acc = fma(t, da, acc)
 // i.e. the two independent += of the method, four VALU fma per output per chunk.
@@ -443,7 +460,7 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
 #define Q6K_GEMM01_XCD_ORDER 0
 #endif
 #ifndef Q6K_WG_PER_CU
-#define Q6K_WG_PER_CU 4
+#define Q6K_WG_PER_CU 3
 #endif
 constexpr int kWgTokTiles = 2;   // token tiles per workgroup
 constexpr int kSlotA = 0;        // 2 token tiles x 1 KiB of A fragments
@@ -519,39 +536,47 @@ __device__ __forceinline__ void wait_chunks(bool loads_a) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CHUNKS * 2) : "memory");
 }
 
-// Layout 0: expand row tile `wave` of a slot from packed 6-bit codes and raw scale bytes.
-__device__ __forceinline__ void expand_slot(uint8_t* slot, int wave, int lane) {
-  const uint32_t raw = lds_addr(slot + kSlotRawB + wave * 768 + lane * 12);
-  const uint32_t rsc = lds_addr(slot + kSlotRawS + wave * 128 + (lane & 31) * 4);
-  uint32_t n0, n1, h, s;
+// Per-lane LDS addresses of a workgroup's operands in ring slot 0; slot j adds j * slot size,
+// which the LDS instructions take as an immediate offset (no per-chunk address arithmetic).
+struct GemmLanes {
+  uint32_t aa, dd, bb, ss;         // reads: A fragment, da, B fragments, d*sc pairs
+  uint32_t raw, rsc, bdst, sdst;   // layout 0 expand: packed codes and scale words in, B and
+                                   // d*sc out (row tile `wave`)
+};
+
+// Layout 0: expand row tile `wave` of the slot at byte offset OFF from packed 6-bit codes and raw
+// scale bytes into B fragments of 4 x the centered int8 codes and the pair d*sc / 4.
+template <int OFF>
+__device__ __forceinline__ void expand_slot(const GemmLanes& L, int lane) {
+  uint32_t x, y, z, s;
   asm volatile(
-      "ds_read_b32 %0, %4\n\t"
-      "ds_read_b32 %1, %4 offset:4\n\t"
-      "ds_read_b32 %2, %4 offset:8\n\t"
-      "ds_read_b32 %3, %5\n\t"
+      "ds_read_b32 %0, %4 offset:%6\n\t"
+      "ds_read_b32 %1, %4 offset:%7\n\t"
+      "ds_read_b32 %2, %4 offset:%8\n\t"
+      "ds_read_b32 %3, %5 offset:%6\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(n0), "=&v"(n1), "=&v"(h), "=&v"(s)
-      : "v"(raw), "v"(rsc)
+      : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(s)
+      : "v"(L.raw), "v"(L.rsc), "n"(OFF), "n"(OFF + 4), "n"(OFF + 8)
       : "memory");
   v4u b;
-  b.x = center4(n0, h);
-  b.y = center4(n0 >> 4, h >> 2);
-  b.z = center4(n1, h >> 4);
-  b.w = center4(n1 >> 4, h >> 6);
-  const float d = __half2float(__ushort_as_half((unsigned short)(s >> 16)));
+  b.x = center4x4(x);
+  b.y = center4x4(y);
+  b.z = center4x4(z);
+  b.w = fourth4x4(x, y, z);
+  // d*sc / 4, exact: an 11-bit significand times an int8 times a power of two
+  const float d = 0.25f * __half2float(__ushort_as_half((unsigned short)(s >> 16)));
   v2f v;
-  v.x = d * (float)(int8_t)(s & 255);  // exact: an 11-bit significand times an int8
+  v.x = d * (float)(int8_t)(s & 255);
   v.y = d * (float)(int8_t)((s >> 8) & 255);
-  const uint32_t bdst = lds_addr(slot + kSlotB + wave * 1024 + lane * 16);
-  asm volatile("ds_write_b128 %0, %1" ::"v"(bdst), "v"(b) : "memory");
-  if (lane < 32) {
-    const uint32_t sdst = lds_addr(slot + kSlotS + wave * 256 + lane * 8);
-    asm volatile("ds_write_b64 %0, %1" ::"v"(sdst), "v"(v) : "memory");
-  }
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(L.bdst), "v"(b), "n"(OFF) : "memory");
+  if (lane < 32)
+    asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(L.sdst), "v"(v), "n"(OFF) : "memory");
 }
 
 // MFMAs and rescale of one 32x32 output tile for one chunk.
-template <bool SUBDOTS>
+// SHIFT: log2 of the factor the staged B operand carries (2 for layout 0, whose fragments hold
+// 4 x the centered codes; the sub-block dots come out as 4 D and are exported as D).
+template <bool SUBDOTS, int SHIFT>
 __device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, long alo, long ahi,
                                            v4u b, v2f s, const float (&dav)[16], int lane,
                                            int64_t c, int64_t T, int64_t R, int64_t nchunk,
@@ -568,8 +593,8 @@ __device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, l
       const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
       int32_t* o = dots_at(dots, tok, mcol, 2 * nchunk);
       if (o) {
-        o[2 * c] = lo_d[r] - kBiasI;
-        o[2 * c + 1] = hi_d[r] - kBiasI;
+        o[2 * c] = (lo_d[r] - kBiasI) >> SHIFT;
+        o[2 * c + 1] = (hi_d[r] - kBiasI) >> SHIFT;
       }
     }
   } else {
@@ -588,6 +613,88 @@ __device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, l
   }
 }
 
+// What one wave of gemm_kernel carries from chunk to chunk.
+struct GemmCtx {
+  uint8_t* smem;
+  GemmSrc src;
+  GemmLanes lanes;
+  int64_t c1, nchunk, T, R0;
+  DotsOut dots;
+  int wave, lane, tt, rp;
+  bool loads_a;
+};
+
+// One chunk c held in ring slot J (chunk c0 + i lives in slot i % KRING): wait for this wave's
+// loads of chunk c+1, (layout 0) expand its row tile of chunk c+1, meet, issue the loads of chunk
+// c+KRING-1 into the slot chunk c-1 left free, then read chunk c's operands and run both tiles.
+// Every slot offset is a compile-time constant.
+template <int LAYOUT, bool SUBDOTS, int KRING, int J>
+__device__ __forceinline__ void gemm_step(const GemmCtx& k, int64_t c, float (&acc)[2][16],
+                                          const v16i& bias) {
+  constexpr int kSlot = SlotSize<LAYOUT>::value;
+  constexpr int kCur = J * kSlot;
+  constexpr int kNext = ((J + 1) % KRING) * kSlot;
+  constexpr int kIssue = ((J + KRING - 1) % KRING) * kSlot;
+  // keep the steps apart: the scheduler would otherwise sink one step's rescale below the next
+  // step's reads and lengthen every live range
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's loads of chunk c+1 have landed (KRING-3 newer chunks may still be in flight)
+  wait_chunks<KRING - 3>(k.loads_a);
+  if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot<kNext>(k.lanes, k.lane);
+  // chunk c+1 complete in LDS for every wave; every wave is done with chunk c-1's slot
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int64_t ci = c + KRING - 1;
+  issue_chunk<LAYOUT>(k.smem + kIssue, k.src, ci < k.c1 ? ci : k.c1 - 1, k.wave, k.lane);
+  // LDS reads of this chunk: row tile 2rp's B and d*sc, A and da, then row tile 2rp+1's
+  v4u a, b0, b1;
+  v4f d0, d1, d2, d3;
+  v2f s0, s1;
+  asm volatile(
+      "ds_read_b128 %0, %9 offset:%13\n\t"
+      "ds_read_b64 %1, %10 offset:%14\n\t"
+      "ds_read_b128 %2, %11 offset:%15\n\t"
+      "ds_read_b128 %3, %12 offset:%16\n\t"
+      "ds_read_b128 %4, %12 offset:%17\n\t"
+      "ds_read_b128 %5, %12 offset:%18\n\t"
+      "ds_read_b128 %6, %12 offset:%19\n\t"
+      "ds_read_b128 %7, %9 offset:%20\n\t"
+      "ds_read_b64 %8, %10 offset:%21"
+      : "=&v"(b0), "=&v"(s0), "=&v"(a), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(b1),
+        "=&v"(s1)
+      : "v"(k.lanes.bb), "v"(k.lanes.ss), "v"(k.lanes.aa), "v"(k.lanes.dd), "n"(kCur),
+        "n"(kCur), "n"(kCur), "n"(kCur), "n"(kCur + 16), "n"(kCur + 32), "n"(kCur + 48),
+        "n"(kCur + 1024), "n"(kCur + 256)
+      : "memory");
+  asm volatile("s_waitcnt lgkmcnt(2)"
+               : "+v"(b0), "+v"(s0), "+v"(a), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)::"memory");
+  const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
+                         d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
+  const long alo = (long)(((uint64_t)a.y << 32) | a.x);
+  const long ahi = (long)(((uint64_t)a.w << 32) | a.z);
+  constexpr int kShift = LAYOUT == Q6K_LAYOUT_PACKED ? 2 : 0;
+  tile_chunk<SUBDOTS, kShift>(acc[0], bias, alo, ahi, b0, s0, dav, k.lane, c, k.T,
+                              k.R0 + 2 * k.rp, k.nchunk, k.dots);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b1), "+v"(s1)::"memory");
+  tile_chunk<SUBDOTS, kShift>(acc[1], bias, alo, ahi, b1, s1, dav, k.lane, c, k.T,
+                              k.R0 + 2 * k.rp + 1, k.nchunk, k.dots);
+}
+
+// Chunks cb .. cb+KRING-1 (slots 0 .. KRING-1), stopping at the piece's end.
+template <int LAYOUT, bool SUBDOTS, int KRING, int J>
+struct GemmSteps {
+  __device__ __forceinline__ static void run(const GemmCtx& k, int64_t cb, float (&acc)[2][16],
+                                             const v16i& bias) {
+    if (cb + J >= k.c1) return;
+    gemm_step<LAYOUT, SUBDOTS, KRING, J>(k, cb + J, acc, bias);
+    GemmSteps<LAYOUT, SUBDOTS, KRING, J + 1>::run(k, cb, acc, bias);
+  }
+};
+template <int LAYOUT, bool SUBDOTS, int KRING>
+struct GemmSteps<LAYOUT, SUBDOTS, KRING, KRING> {
+  __device__ __forceinline__ static void run(const GemmCtx&, int64_t, float (&)[2][16],
+                                             const v16i&) {}
+};
+
 template <int LAYOUT, bool SUBDOTS>
 __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t* __restrict__ xq,
                                                       const float* __restrict__ da,
@@ -601,28 +708,43 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   constexpr int kSlot = SlotSize<LAYOUT>::value;
   constexpr int kRing = RingSize<LAYOUT>::value;
   static_assert(Q6K_WG_PER_CU * kRing * kSlot <= 160 * 1024, "LDS budget");
+  static_assert(kRing * kSlot + 1024 < 65536, "slot offsets fit the LDS immediate offset");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kSlot];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool loads_a = wave < kWgTokTiles;
-  const int tt = wave & 1;                              // token tile of this wave in the workgroup
-  const int rp = wave >> 1;                             // row-tile pair of this wave
+  GemmCtx k;
+  k.smem = smem;
+  k.lane = threadIdx.x & 63;
+  k.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  k.loads_a = k.wave < kWgTokTiles;
+  k.tt = k.wave & 1;                                    // token tile of this wave in the workgroup
+  k.rp = k.wave >> 1;                                   // row-tile pair of this wave
   const TileWork tw = tile_work<Q6K_GEMM01_XCD_ORDER != 0>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
-  const int64_t c0 = 8 * tw.s0, c1 = 8 * tw.s1;        // this workgroup's chunks
-  const int64_t T = (int64_t)tw.bx * kWgTokTiles + tt;
-  const int64_t R0 = (int64_t)tw.by * 4;                // the workgroup's first row tile
-  const int64_t Ta = (int64_t)tw.bx * kWgTokTiles + (loads_a ? wave : 0);
+  const int64_t c0 = 8 * tw.s0;                         // this workgroup's chunks [c0, c1)
+  k.c1 = 8 * tw.s1;
+  k.nchunk = nchunk;
+  k.T = (int64_t)tw.bx * kWgTokTiles + k.tt;
+  k.R0 = (int64_t)tw.by * 4;                            // the workgroup's first row tile
+  k.dots = dots;
+  const int lane = k.lane, wave = k.wave;
+  const int64_t Ta = (int64_t)tw.bx * kWgTokTiles + (k.loads_a ? wave : 0);
 
-  GemmSrc src;
-  src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
-  src.d = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
+  k.src.a = make_rsrc(xq + Ta * nchunk * 1024, nchunk * 1024);
+  k.src.d = make_rsrc(reinterpret_cast<const uint8_t*>(da) + Ta * nchunk * 128, nchunk * 128);
   if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
-    src.b = make_rsrc(wcodes + (R0 + wave) * nchunk * 1024, nchunk * 1024);
-    src.s = make_rsrc(wscales + (R0 + wave) * nchunk * 256, nchunk * 256);
+    k.src.b = make_rsrc(wcodes + (k.R0 + wave) * nchunk * 1024, nchunk * 1024);
+    k.src.s = make_rsrc(wscales + (k.R0 + wave) * nchunk * 256, nchunk * 256);
   } else {
-    src.b = make_rsrc(wcodes + (R0 + wave) * nchunk * 768, nchunk * 768);
-    src.s = make_rsrc(wscales + (R0 + wave) * nchunk * 128, nchunk * 128);
+    k.src.b = make_rsrc(wcodes + (k.R0 + wave) * nchunk * 768, nchunk * 768);
+    k.src.s = make_rsrc(wscales + (k.R0 + wave) * nchunk * 128, nchunk * 128);
   }
+  const int p = lane & 31, g = lane >> 5;
+  k.lanes.aa = lds_addr(smem + kSlotA + k.tt * 1024 + lane * 16);
+  k.lanes.dd = lds_addr(smem + kSlotD + k.tt * 128 + g * 64);
+  k.lanes.bb = lds_addr(smem + kSlotB + k.rp * 2048 + lane * 16);
+  k.lanes.ss = lds_addr(smem + kSlotS + k.rp * 512 + p * 8);
+  k.lanes.raw = lds_addr(smem + kSlotRawB + wave * 768 + lane * 12);
+  k.lanes.rsc = lds_addr(smem + kSlotRawS + wave * 128 + p * 4);
+  k.lanes.bdst = lds_addr(smem + kSlotB + wave * 1024 + lane * 16);
+  k.lanes.sdst = lds_addr(smem + kSlotS + wave * 256 + lane * 8);
 
   v16i bias;
 #pragma unroll
@@ -633,70 +755,22 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-  // Prologue: chunks c0 .. c0+kRing-2 in flight; chunk c0 ready in its slot.
+  // Prologue: chunks c0 .. c0+kRing-2 in flight in slots 0 .. kRing-2; chunk c0 ready in slot 0.
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j)
-    issue_chunk<LAYOUT>(smem + j * kSlot, src, c0 + j < c1 ? c0 + j : c1 - 1, wave, lane);
-  wait_chunks<kRing - 2>(loads_a);
-  if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot(smem, wave, lane);
+    issue_chunk<LAYOUT>(smem + j * kSlot, k.src, c0 + j < k.c1 ? c0 + j : k.c1 - 1, wave, lane);
+  wait_chunks<kRing - 2>(k.loads_a);
+  if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot<0>(k.lanes, lane);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  const int p = lane & 31, g = lane >> 5;
-  int slot_c = 0;                 // slot of chunk c
-  int slot_next = 1;              // slot of chunk c+1
-  int slot_issue = kRing - 1;     // slot of chunk c+kRing-1
-  for (int64_t c = c0; c < c1; ++c) {
-    // this wave's loads of chunk c+1 have landed (kRing-3 newer chunks may still be in flight)
-    wait_chunks<kRing - 3>(loads_a);
-    if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot(smem + slot_next * kSlot, wave, lane);
-    // chunk c+1 complete in LDS for every wave; every wave is done with chunk c-1's slot
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int64_t ci = c + kRing - 1;
-    issue_chunk<LAYOUT>(smem + slot_issue * kSlot, src, ci < c1 ? ci : c1 - 1, wave, lane);
-    // LDS reads of this chunk: row tile 2rp's B and d*sc, A and da, then row tile 2rp+1's
-    const uint8_t* slot = smem + slot_c * kSlot;
-    const uint32_t aa = lds_addr(slot + kSlotA + tt * 1024 + lane * 16);
-    const uint32_t dd = lds_addr(slot + kSlotD + tt * 128 + g * 64);
-    const uint32_t bb = lds_addr(slot + kSlotB + rp * 2048 + lane * 16);
-    const uint32_t ss = lds_addr(slot + kSlotS + rp * 512 + p * 8);
-    v4u a, b0, b1;
-    v4f d0, d1, d2, d3;
-    v2f s0, s1;
-    asm volatile(
-        "ds_read_b128 %0, %9\n\t"
-        "ds_read_b64 %1, %10\n\t"
-        "ds_read_b128 %2, %11\n\t"
-        "ds_read_b128 %3, %12\n\t"
-        "ds_read_b128 %4, %12 offset:16\n\t"
-        "ds_read_b128 %5, %12 offset:32\n\t"
-        "ds_read_b128 %6, %12 offset:48\n\t"
-        "ds_read_b128 %7, %9 offset:1024\n\t"
-        "ds_read_b64 %8, %10 offset:256"
-        : "=&v"(b0), "=&v"(s0), "=&v"(a), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(b1),
-          "=&v"(s1)
-        : "v"(bb), "v"(ss), "v"(aa), "v"(dd)
-        : "memory");
-    asm volatile("s_waitcnt lgkmcnt(2)"
-                 : "+v"(b0), "+v"(s0), "+v"(a), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)::"memory");
-    const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
-                           d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
-    const long alo = (long)(((uint64_t)a.y << 32) | a.x);
-    const long ahi = (long)(((uint64_t)a.w << 32) | a.z);
-    tile_chunk<SUBDOTS>(acc[0], bias, alo, ahi, b0, s0, dav, lane, c, T, R0 + 2 * rp, nchunk,
-                        dots);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b1), "+v"(s1)::"memory");
-    tile_chunk<SUBDOTS>(acc[1], bias, alo, ahi, b1, s1, dav, lane, c, T, R0 + 2 * rp + 1, nchunk,
-                        dots);
-    slot_c = slot_next;
-    slot_next = slot_next + 1 == kRing ? 0 : slot_next + 1;
-    slot_issue = slot_issue + 1 == kRing ? 0 : slot_issue + 1;
-  }
+  for (int64_t cb = c0; cb < k.c1; cb += kRing) GemmSteps<LAYOUT, SUBDOTS, kRing, 0>::run(k, cb, acc, bias);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
 
   if (SUBDOTS) return;
+  const int64_t T = k.T;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int64_t mcol = (R0 + 2 * rp + u) * kTile + p;
+    const int64_t mcol = (k.R0 + 2 * k.rp + u) * kTile + p;
     if (mcol >= m) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -925,12 +999,16 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
   if (J == 0) fold_dma(k, s + kFAhead);
   if (J == 7) {
     // super-block s + 1's slot: this wave's share of it has landed, and after the barrier every
-    // wave's has.  Its loads were issued at least two iterations ago, before the planes of
-    // chunks 8s+3 .. 8s+6 (issued in steps 0-3 of this iteration, and feeding MFMAs whose
-    // results reach volatile statements ahead of this one, so the compiler cannot sink them
-    // below it): with at most those 8 loads outstanding, the slot's loads are complete.  (The
-    // compiler is free to move the plane loads relative to the direct-to-LDS ones otherwise, so
-    // no tighter count is safe.)
+    // wave's has.  vmcnt(N) waits until at most the N most recently issued vector memory loads
+    // of this wave are outstanding (loads complete in issue order for this count), so it
+    // suffices that at least 8 loads were issued after the last load of super-block s + 1's
+    // slot and before this wait.  That holds whatever order the compiler picks inside a step:
+    // the slot's loads were issued in step 0 of super-block s - 2, and this statement and the
+    // same one of super-blocks s - 2 and s - 1 are volatile and clobber memory, so no load can
+    // cross them; the 16 digit-plane loads of super-block s - 1 (two per step, every step,
+    // clamped to the piece but never skipped) therefore sit between the slot's loads and this
+    // wait.  (The slots of a piece's first three super-blocks were loaded in the prologue, which
+    // waits for all of its loads.)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     fold_read<0, 0>(xn, dn, st);
   } else {

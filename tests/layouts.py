@@ -40,19 +40,22 @@ def untile_expanded(buf, m, k):
 
 
 def untile_packed(buf, m, k):
-    """layout 0 bytes -> (6-bit codes uint8 [MP][k], sc int8 [MP][k/16], d-bits uint16 [MP][k/32])."""
+    """layout 0 bytes -> (6-bit codes uint8 [MP][k], sc int8 [MP][k/16], d-bits uint16 [MP][k/32]).
+
+    Per lane three words X, Y, Z: byte t of X / Y / Z holds a_t / a_{t+4} / b_t in bits 2-7 and
+    bits 0-1 / 2-3 / 4-5 of b_{t+4} in bits 0-1."""
     mp = round_up(m, 128)
     nchunk = k // 32
     b = np.asarray(buf, np.uint8)
     nb = mp * k * 3 // 4
     w = b[:nb].reshape(mp // 32, nchunk, 2, 32, 3, 4).astype(np.int32)  # T,c,g,p,word,byte
-    n0, n1, h = w[..., 0, :], w[..., 1, :], w[..., 2, :]
-    a = np.zeros(n0.shape[:-1] + (8,), np.int32)
+    x, y, z = w[..., 0, :], w[..., 1, :], w[..., 2, :]
+    a = np.zeros(x.shape[:-1] + (8,), np.int32)
     bb = np.zeros_like(a)
-    a[..., 0:4] = (n0 & 15) | (((h >> 0) & 3) << 4)
-    a[..., 4:8] = ((n0 >> 4) & 15) | (((h >> 2) & 3) << 4)
-    bb[..., 0:4] = (n1 & 15) | (((h >> 4) & 3) << 4)
-    bb[..., 4:8] = ((n1 >> 4) & 15) | (((h >> 6) & 3) << 4)
+    a[..., 0:4] = x >> 2
+    a[..., 4:8] = y >> 2
+    bb[..., 0:4] = z >> 2
+    bb[..., 4:8] = (x & 3) | ((y & 3) << 2) | ((z & 3) << 4)
     full = np.stack([a, bb], axis=4)  # T,c,g,p,h,e
     codes = full.transpose(0, 3, 1, 4, 2, 5).reshape(mp, k).astype(np.uint8)
     s = b[nb: nb + mp * nchunk * 4].reshape(mp // 32, nchunk, 32, 4).transpose(0, 2, 1, 3)

@@ -139,20 +139,21 @@ def _dense_expander(block):
 
 
 def _group_form(block):
-    """Third statement (r41 sec. 3.2): a staging window of two chunks starting at even chunk
-    cb is four 16-element groups g; group g reads a 16-byte ql run at 64*h0 + 16*g and a 16-byte
-    qh run at 128 + 32*h0 + 16*(g % 2), where h0 = (cb // 4) % 2; the nibble is selected by
-    shift 4*((cb // 2) % 2) and the 2-bit field by that shift + 2*((g // 2) % 2)."""
+    """Third statement ("r41 — q6_K B-expand widened to uint4 group loads (LANDED)", sec. 3.2):
+    the expand works on 16-element groups, and every group reads exactly one 16-byte run of ql
+    bytes (runs start at 0, 16, ..., 112) and one 16-byte run of qh bytes (runs start at 128,
+    144, 160, 176).  Restated per group: group gi (elements 16*gi .. 16*gi+15) lies in half
+    hf = gi // 8 of the block at position pos = gi % 8 of that half; it reads the ql run at
+    64*hf + 16*(pos % 4), taking the high nibble for pos >= 4, and the qh run at
+    128 + 32*hf + 16*(pos % 2), taking 2-bit field pos // 2 of each byte."""
     out = np.zeros(256, int)
-    for cb in range(0, 8, 2):
-        h0 = (cb >> 2) & 1
-        qsh = ((cb >> 1) & 1) * 4
-        for g in range(4):
-            ql = block[h0 * 64 + g * 16: h0 * 64 + g * 16 + 16].astype(int)
-            qh = block[128 + h0 * 32 + (g & 1) * 16: 128 + h0 * 32 + (g & 1) * 16 + 16].astype(int)
-            qhs = qsh + ((g >> 1) & 1) * 2
-            e0 = cb * 32 + g * 16
-            out[e0:e0 + 16] = ((ql >> qsh) & 15) | (((qh >> qhs) & 3) << 4)
+    for gi in range(16):
+        hf, pos = divmod(gi, 8)
+        ql_run = block[64 * hf + 16 * (pos % 4):][:16].astype(int)
+        qh_run = block[128 + 32 * hf + 16 * (pos % 2):][:16].astype(int)
+        low = (ql_run >> (4 * (pos // 4))) & 15
+        high = (qh_run >> (2 * (pos // 2))) & 3
+        out[16 * gi:16 * gi + 16] = low | (high << 4)
     return out
 
 
@@ -180,8 +181,13 @@ def test_decode_multi_row_multi_block_layout(oracle_mod):
 
 
 def test_f16_conversion_all_finite(oracle_mod):
-    bits = np.arange(0, 0x10000, 37, dtype=np.uint32).astype(np.uint16)
+    # every one of the 65536 binary16 bit patterns: finite values exactly as numpy converts them
+    # (subnormals included), infinities as infinities, NaNs as NaNs
+    bits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
     ref = bits.view(np.float16).astype(np.float64)
     got = np.array([oracle_mod.f16_to_f64(int(b)) for b in bits])
     fin = np.isfinite(ref)
+    assert fin.sum() == 0x10000 - 2 * 1024
     np.testing.assert_array_equal(got[fin], ref[fin])
+    np.testing.assert_array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+    assert np.isnan(got[np.isnan(ref)]).all()
