@@ -448,8 +448,12 @@ def main(argv=None):
     sweep = args.workload == "sweep32"
     q4 = args.weights == "q4k"
     head = "q4k" if q4 else args.layout
-    layouts = ["q4k"] if q4 or args.swiglu else \
-        sorted({int(v) for v in args.layouts.split(",") if v.strip()} | {args.layout})
+    if q4:
+        layouts = ["q4k"]
+    elif args.swiglu:
+        layouts = [args.layout]
+    else:
+        layouts = sorted({int(v) for v in args.layouts.split(",") if v.strip()} | {args.layout})
 
     # ------------------------------------------------------------ inputs resident in HBM
     t0 = time.perf_counter()
