@@ -231,35 +231,39 @@ class Probes:
         import numpy as np
         return float(np.median(cycles / secs) / 1e9)
 
+    # Cycle figures are per SIMD over the whole launch: the clock measured inside the waves times
+    # the event-timed launch, divided by the instructions (or tiles) one SIMD ran -- all SIMDs run
+    # the same share concurrently.  (A single wave's own span would overstate the rate when several
+    # waves share a SIMD and start or end at different times.)
     def mfma(self, kind, w, iters=20000):
-        import numpy as np
         name, ops = MFMA_KINDS[kind]
         el, cyc, secs, nw = self.run("q6c_mfma", kind, iters, w)
         n_instr = nw * iters * 4
+        ghz = self.clock_ghz(cyc, secs)
         return {"instr": name, "waves_per_simd": w, "tops": round(n_instr * ops / el / 1e12, 1),
-                "cycles_per_instr_per_simd": round(float(np.median(cyc)) / (iters * 4 * w), 2),
-                "clock_ghz": round(self.clock_ghz(cyc, secs), 3)}
+                "cycles_per_instr_per_simd": round(ghz * 1e9 * el / (n_instr / 1024), 2),
+                "clock_ghz": round(ghz, 3)}
 
     def valu(self, kind, w, iters=8000):
-        import numpy as np
         el, cyc, secs, nw = self.run("q6c_valu", kind, iters, w)
         n_instr = nw * iters * 64
+        ghz = self.clock_ghz(cyc, secs)
         return {"instr": VALU_KINDS[kind], "waves_per_simd": w,
                 "lane_ops_t_per_s": round(n_instr * 64 / el / 1e12, 2),
-                "cycles_per_instr_per_simd": round(float(np.median(cyc)) / (iters * 64 * w), 3),
-                "clock_ghz": round(self.clock_ghz(cyc, secs), 3)}
+                "cycles_per_instr_per_simd": round(ghz * 1e9 * el / (n_instr / 1024), 3),
+                "clock_ghz": round(ghz, 3)}
 
     def tileop(self, kind, w, iters=4000):
-        import numpy as np
         name, nvalu = TILEOP_KINDS[kind]
         el, cyc, secs, nw = self.run("q6c_tileop", kind, iters, w)
         tiles = nw * iters * 2  # two 32x32 tiles per wave and round, one 32-k chunk each
+        ghz = self.clock_ghz(cyc, secs)
         return {"op": name, "waves_per_simd": w,
                 "ns_per_tile_chunk_per_simd": round(el * 1e9 * 1024 / tiles, 2),
-                "cycles_per_tile_chunk_per_simd": round(float(np.median(cyc)) / (iters * 2), 1),
+                "cycles_per_tile_chunk_per_simd": round(ghz * 1e9 * el / (tiles / 1024), 1),
                 "valu_lane_ops_t_per_s": round(tiles * nvalu * 64 / el / 1e12, 2),
                 "equiv_gemm_tops": round(tiles * 2 * 32 * 32 * 32 / el / 1e12, 1),
-                "clock_ghz": round(self.clock_ghz(cyc, secs), 3)}
+                "clock_ghz": round(ghz, 3)}
 
     def overlap(self, iters=20000):
         """Whether the vector ALU issues while the matrix core runs (see q6k_ceilings.h): median

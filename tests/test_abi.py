@@ -33,6 +33,32 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(L, name), name
 
 
+def test_ceilings_library_exports_its_declared_symbols():
+    # the measurement library beside the product: every q6c_ call its header declares
+    text = open(os.path.join(ROOT, "include", "q6k_ceilings.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(q6c_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["q6c_mfma", "q6c_overlap", "q6c_probe_waves", "q6c_stream", "q6c_tileop",
+                     "q6c_valu", "q6c_wall_clock_khz"]
+    L = ctypes.CDLL(os.path.join(ROOT, "q6_int8_prefill_amd", "_build", "libq6k_ceilings.so"))
+    for name in names:
+        assert hasattr(L, name), name
+    # host-side argument checks (no device needed: they fail before any HIP call)
+    f = L.q6c_mfma
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    assert f(9, 10, 1, FAKE, 1 << 20, None) == -1      # unknown kind
+    assert f(0, 10, 9, FAKE, 1 << 20, None) == -1      # more than 8 waves per SIMD
+    assert f(0, 0, 1, FAKE, 1 << 20, None) == -1       # no rounds
+    s = L.q6c_stream
+    s.restype = ctypes.c_int
+    s.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    assert s(0, FAKE, FAKE, 100, 1 << 20, None) == -1   # not a multiple of 16
+    assert s(0, FAKE + 8, FAKE, 1 << 20, 1 << 20, None) == -3
+
+
 def test_size_queries():
     import q6_int8_prefill_amd as q6k
     assert q6k.q6k_act_bytes(1, 256) == (128 * 256, 128 * 8 * 4)
