@@ -315,16 +315,21 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint8_t* __restrict__
 
 // Layout 0 in-register expand of one lane's 16 codes into the two 8-byte MFMA fragments, as
 // centered int8 times 4: a byte s = (q << 2) | x (q the 6-bit code, x two bits stored for the
-// fourth word) becomes (s & 0xFC) ^ 0x80 = 4q - 128 = 4 (q - 32) in [-128, 124] -- two SWAR
-// operations per word, no carries -- and the fourth word's bytes are gathered from the x bits of
+// fourth word) becomes (s & 0xFC) ^ 0x80 = 4q - 128 = 4 (q - 32) in [-128, 124] -- one SWAR
+// operation per word, no carries -- and the fourth word's bytes are gathered from the x bits of
 // the other three and then treated alike.  The MFMA then yields 4 D exactly (|4 D| < 2^22, so the
-// float bias trick still holds), and the staged d*sc is d*sc/4 (exact: a power of two).
+// float bias trick still holds); the rescale uses d*sc itself, so the accumulators hold 4 y and
+// the store multiplies by 1/4 (exact: a power of two).
 __device__ __forceinline__ uint32_t center4x4(uint32_t s) { return (s & 0xFCFCFCFCu) ^ 0x80808080u; }
 
+// Bits 0-1 of byte t of x, y, z become bits 2-3, 4-5, 6-7 of byte t (4 b_{4+t}), centered like
+// the others.  Each shift drags a neighbouring byte's bits into the positions it does not keep;
+// the two bit-field inserts and the final mask take only the wanted ones.
 __device__ __forceinline__ uint32_t fourth4x4(uint32_t x, uint32_t y, uint32_t z) {
-  const uint32_t lo = 0x03030303u;
-  const uint32_t q = (x & lo) | ((y & lo) << 2) | ((z & lo) << 4);  // b_4..7, 6 bits each
-  return ((q << 2) & 0xFCFCFCFCu) ^ 0x80808080u;
+  const uint32_t a = x << 2, b = y << 4, c = z << 6;
+  const uint32_t ab = (a & 0x0C0C0C0Cu) | (b & ~0x0C0C0C0Cu);
+  const uint32_t abc = (ab & 0x3C3C3C3Cu) | (c & ~0x3C3C3C3Cu);
+  return (abc & 0xFCFCFCFCu) ^ 0x80808080u;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -438,16 +443,22 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
 // Staging: a ring of kRing LDS slots, one 32-k chunk of the workgroup's operands per slot.  Each
 // wave fills its share of a slot with gfx950 direct-to-LDS loads through buffer resources
 // (buffer_load_dwordx4 ... lds, 16 bytes per lane, no registers): row tile w's weight codes and
-// d*sc, and, for waves 0 and 1,
-// token tile w's activations and da.  Loads run kRing-1 chunks ahead of the compute.  Per chunk c
-// a wave waits for its own loads of chunk c+1 (s_waitcnt vmcnt), layout 0 expands its row tile's
-// 6-bit codes of chunk c+1 into int8 (4 x the centered codes) and forms d*sc/4 in the slot, one
-// workgroup barrier makes the slot visible and frees the slot of chunk c-1, the loads of chunk
-// c+kRing-1 are issued, and chunk c is computed.  The chunk loop is unrolled over the ring, so
-// every slot address is a per-lane base register plus an immediate offset (no address arithmetic
-// per chunk).  LDS reads and writes are inline assembly with explicit waits: the compiler would
-// otherwise wait for every outstanding direct-to-LDS load before each LDS access, which would
-// serialize the ring.
+// scales, and, for waves 0 and 1, token tile w's activations and da.  Loads run kRing-1 chunks
+// ahead of the compute.  Step c (chunk c, slot c % kRing) of a wave:
+//   1. meet: every wave's share of chunk c is in its slot (each wave waited for its own loads of
+//      chunk c during step c-1, and layout 0 expanded its row tile of chunk c there), and every
+//      wave is done with chunk c-1, so that slot is free;
+//   2. issue the loads of chunk c+kRing-1 into the freed slot;
+//   3. read chunk c's fragments and scales from LDS, start the four MFMAs;
+//   4. wait for this wave's own loads of chunk c+1 (kRing-2 newer chunks may stay in flight) and,
+//      on layout 0, start the LDS reads of its packed codes;
+//   5. rescale chunk c (the LDS reads of step 4 land meanwhile);
+//   6. layout 0: expand row tile w of chunk c+1 into B fragments of 4 x the centered int8 codes
+//      and the pair (d*sc0, d*sc1) in the slot.
+// The chunk loop is unrolled over the ring, so every slot address is a per-lane base register
+// plus an immediate offset (no address arithmetic per chunk).  LDS reads and writes are inline
+// assembly with explicit waits: the compiler would otherwise wait for every outstanding
+// direct-to-LDS load before each LDS access, which would serialize the ring.
 //
 // Per chunk and output tile: two v_mfma_i32_32x32x16_i8 (halves 0 and 1), each started from the
 // bit pattern of 1.5*2^23 so that the int32 result D (4 D on layout 0) is read as the float
@@ -507,26 +518,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
 }
 
 // Buffer resources of one workgroup's operands: this wave's row tile (codes and scales) and, for
-// waves 0 and 1, token tile `wave` (activations and da).
+// waves 0 and 1, token tile `wave` (activations and da).  (Spreading the activation loads over
+// all four waves, half a tile each, measured 2-3 % slower.)
 struct GemmSrc {
   __amdgpu_buffer_rsrc_t a, d, b, s;
 };
 
 // Issue this wave's loads of chunk c (already clamped to a valid chunk) into `slot`.
 template <int LAYOUT>
-__device__ __forceinline__ void issue_chunk(uint8_t* slot, const GemmSrc& src, int64_t c, int wave,
+__device__ __forceinline__ void issue_chunk(uint8_t* slot, const GemmSrc& src, uint32_t c, int wave,
                                             int lane) {
-  const uint32_t l16 = lane * 16, cc = (uint32_t)c;
+  const uint32_t l16 = lane * 16;
   if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
-    bdma16(src.b, l16, cc * 1024, slot + kSlotB + wave * 1024);
-    if (lane < 16) bdma16(src.s, l16, cc * 256, slot + kSlotS + wave * 256);
+    bdma16(src.b, l16, c * 1024, slot + kSlotB + wave * 1024);
+    if (lane < 16) bdma16(src.s, l16, c * 256, slot + kSlotS + wave * 256);
   } else {
-    if (lane < 48) bdma16(src.b, l16, cc * 768, slot + kSlotRawB + wave * 768);
-    if (lane < 8) bdma16(src.s, l16, cc * 128, slot + kSlotRawS + wave * 128);
+    if (lane < 48) bdma16(src.b, l16, c * 768, slot + kSlotRawB + wave * 768);
+    if (lane < 8) bdma16(src.s, l16, c * 128, slot + kSlotRawS + wave * 128);
   }
   if (wave < kWgTokTiles) {
-    bdma16(src.a, l16, cc * 1024, slot + kSlotA + wave * 1024);
-    if (lane < 8) bdma16(src.d, l16, cc * 128, slot + kSlotD + wave * 128);
+    bdma16(src.a, l16, c * 1024, slot + kSlotA + wave * 1024);
+    if (lane < 8) bdma16(src.d, l16, c * 128, slot + kSlotD + wave * 128);
   }
 }
 
@@ -542,52 +554,68 @@ __device__ __forceinline__ void wait_chunks(bool loads_a) {
 // Per-lane LDS addresses of a workgroup's operands in ring slot 0; slot j adds j * slot size,
 // which the LDS instructions take as an immediate offset (no per-chunk address arithmetic).
 struct GemmLanes {
-  uint32_t aa, dd, bb, ss;         // reads: A fragment, da, B fragments, d*sc pairs
+  uint32_t aa, dd, bb, ss;         // reads: A fragment, da, B fragments, scales
   uint32_t raw, rsc, bdst, sdst;   // layout 0 expand: packed codes and scale words in, B and
-                                   // d*sc out (row tile `wave`)
+                                   // scale quads out (row tile `wave`)
 };
 
-// Layout 0: expand row tile `wave` of the slot at byte offset OFF from packed 6-bit codes and raw
-// scale bytes into B fragments of 4 x the centered int8 codes and the pair d*sc / 4.
-template <int OFF>
-__device__ __forceinline__ void expand_slot(const GemmLanes& L, int lane) {
+// Layout 0: this lane's packed codes and its row's raw scale word of row tile `wave` in the slot at
+// byte offset OFF.  No wait: the caller waits (with the registers as operands) after other work.
+struct RawCodes {
   uint32_t x, y, z, s;
+};
+template <int OFF>
+__device__ __forceinline__ void expand_read(const GemmLanes& L, RawCodes& r) {
   asm volatile(
       "ds_read_b32 %0, %4 offset:%6\n\t"
       "ds_read_b32 %1, %4 offset:%7\n\t"
       "ds_read_b32 %2, %4 offset:%8\n\t"
-      "ds_read_b32 %3, %5 offset:%6\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(s)
+      "ds_read_b32 %3, %5 offset:%6"
+      : "=&v"(r.x), "=&v"(r.y), "=&v"(r.z), "=&v"(r.s)
       : "v"(L.raw), "v"(L.rsc), "n"(OFF), "n"(OFF + 4), "n"(OFF + 8)
       : "memory");
-  v4u b;
-  b.x = center4x4(x);
-  b.y = center4x4(y);
-  b.z = center4x4(z);
-  b.w = fourth4x4(x, y, z);
-  // d*sc / 4, exact: an 11-bit significand times an int8 times a power of two
-  const float d = 0.25f * __half2float(__ushort_as_half((unsigned short)(s >> 16)));
-  v2f v;
-  v.x = d * (float)(int8_t)(s & 255);
-  v.y = d * (float)(int8_t)((s >> 8) & 255);
-  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(L.bdst), "v"(b), "n"(OFF) : "memory");
-  if (lane < 32)
-    asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(L.sdst), "v"(v), "n"(OFF) : "memory");
 }
 
-// MFMAs and rescale of one 32x32 output tile for one chunk.
-// SHIFT: log2 of the factor the staged B operand carries (2 for layout 0, whose fragments hold
-// 4 x the centered codes; the sub-block dots come out as 4 D and are exported as D).
-template <bool SUBDOTS, int SHIFT>
-__device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, long alo, long ahi,
-                                           v4u b, v2f s, const float (&dav)[16], int lane,
-                                           int64_t c, int64_t T, int64_t R, int64_t nchunk,
-                                           const DotsOut& dots) {
+// Layout 0: write row tile `wave` of the slot at OFF as B fragments of 4 x the centered int8
+// codes and, from lanes 0-31 (one row each), the pair (d*sc0, d*sc1).  (Also staging the bias
+// products -1.5*2^23 d*sc, which saves the steps four multiplies, measured 1.5 % slower: more LDS
+// traffic.)
+template <int OFF>
+__device__ __forceinline__ void expand_write(const GemmLanes& L, const RawCodes& r, int lane) {
+  v4u b;
+  b.x = center4x4(r.x);
+  b.y = center4x4(r.y);
+  b.z = center4x4(r.z);
+  b.w = fourth4x4(r.x, r.y, r.z);
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(L.bdst), "v"(b), "n"(OFF) : "memory");
+  if (lane < 32) {
+    // d*sc, exact: an 11-bit significand times an int8
+    const float d = __half2float(__ushort_as_half((unsigned short)(r.s >> 16)));
+    v2f v;
+    v.x = d * (float)(int8_t)(r.s & 255);
+    v.y = d * (float)(int8_t)((r.s >> 8) & 255);
+    asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(L.sdst), "v"(v), "n"(OFF) : "memory");
+  }
+}
+
+// The MFMAs of one 32x32 output tile for one chunk (halves 0 and 1).
+__device__ __forceinline__ void tile_mfma(v16i& lo_d, v16i& hi_d, const v16i& bias, long alo,
+                                          long ahi, v4u b) {
   const long blo = (long)(((uint64_t)b.y << 32) | b.x);
   const long bhi = (long)(((uint64_t)b.w << 32) | b.z);
-  const v16i lo_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo, blo, bias, 0, 0, 0);
-  const v16i hi_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(ahi, bhi, bias, 0, 0, 0);
+  lo_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(alo, blo, bias, 0, 0, 0);
+  hi_d = __builtin_amdgcn_mfma_i32_32x32x16_i8(ahi, bhi, bias, 0, 0, 0);
+}
+
+// Rescale of one 32x32 output tile for one chunk, or (SUBDOTS) the store of its sub-block dots.
+// s = (dsc0, dsc1, nb0, nb1).  SHIFT: log2 of the factor the staged B operand carries (2 for
+// layout 0, whose fragments hold 4 x the centered codes; its dots come out as 4 D and are
+// exported as D).
+template <bool SUBDOTS, int SHIFT>
+__device__ __forceinline__ void tile_rescale(float (&acc)[16], const v16i& lo_d, const v16i& hi_d,
+                                             v4f s, const float (&dav)[16], int lane, uint32_t c,
+                                             int64_t T, int64_t R, int64_t nchunk,
+                                             const DotsOut& dots) {
   if (SUBDOTS) {
     const int p = lane & 31, g = lane >> 5;
     const int64_t mcol = R * kTile + p;
@@ -601,19 +629,27 @@ __device__ __forceinline__ void tile_chunk(float (&acc)[16], const v16i& bias, l
       }
     }
   } else {
-    const float nb0 = -kBiasF * s.x;
-    const float nb1 = -kBiasF * s.y;
     // four phases of 16 independent fma: no VALU instruction depends on the one before it
     float t[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(lo_d[r]), s.x, nb0);
+    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(lo_d[r]), s.x, s.z);
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(t[r], dav[r], acc[r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(hi_d[r]), s.y, nb1);
+    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(hi_d[r]), s.y, s.w);
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(t[r], dav[r], acc[r]);
   }
+}
+
+// An empty statement that reads and rewrites one tile's 16 accumulators: the rescale that
+// produces them stays ahead of it (the compiler would otherwise sink whole steps' rescales to the
+// end of the unrolled loop and keep every step's MFMA results live at once).
+__device__ __forceinline__ void pin_acc(float (&a)[16]) {
+  asm volatile(""
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]),
+                 "+v"(a[12]), "+v"(a[13]), "+v"(a[14]), "+v"(a[15]));
 }
 
 // What one wave of gemm_kernel carries from chunk to chunk.
@@ -621,37 +657,37 @@ struct GemmCtx {
   uint8_t* smem;
   GemmSrc src;
   GemmLanes lanes;
-  int64_t c1, nchunk, T, R0;
+  uint32_t c1;  // the piece's chunk end
+  int64_t nchunk, T, R0;
   DotsOut dots;
   int wave, lane, tt, rp;
   bool loads_a;
 };
 
-// One chunk c held in ring slot J (chunk c0 + i lives in slot i % KRING): wait for this wave's
-// loads of chunk c+1, (layout 0) expand its row tile of chunk c+1, meet, issue the loads of chunk
-// c+KRING-1 into the slot chunk c-1 left free, then read chunk c's operands and run both tiles.
+// Step c (chunk c in ring slot J; chunk c0 + i lives in slot i % KRING), as described above.
 // Every slot offset is a compile-time constant.
 template <int LAYOUT, bool SUBDOTS, int KRING, int J>
-__device__ __forceinline__ void gemm_step(const GemmCtx& k, int64_t c, float (&acc)[2][16],
-                                          const v16i& bias) {
+__device__ __forceinline__ void gemm_step(const GemmCtx& k, uint32_t c, float (&acc)[2][16],
+                                          v16i& bias) {
   constexpr int kSlot = SlotSize<LAYOUT>::value;
   constexpr int kCur = J * kSlot;
   constexpr int kNext = ((J + 1) % KRING) * kSlot;
   constexpr int kIssue = ((J + KRING - 1) % KRING) * kSlot;
+  constexpr bool kPacked = LAYOUT == Q6K_LAYOUT_PACKED;
   // keep the steps apart: the scheduler would otherwise sink one step's rescale below the next
   // step's reads and lengthen every live range
   __builtin_amdgcn_sched_barrier(0);
-  // this wave's loads of chunk c+1 have landed (KRING-3 newer chunks may still be in flight)
-  wait_chunks<KRING - 3>(k.loads_a);
-  if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot<kNext>(k.lanes, k.lane);
-  // chunk c+1 complete in LDS for every wave; every wave is done with chunk c-1's slot
+  // the MFMA bias stays in its 16 VGPRs (instead of being rebuilt from scalars every step)
+  asm volatile("" : "+v"(bias));
+  // 1. chunk c complete in LDS for every wave; every wave is done with chunk c-1's slot
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  const int64_t ci = c + KRING - 1;
+  // 2.
+  const uint32_t ci = c + KRING - 1;
   issue_chunk<LAYOUT>(k.smem + kIssue, k.src, ci < k.c1 ? ci : k.c1 - 1, k.wave, k.lane);
-  // LDS reads of this chunk: row tile 2rp's B and d*sc, A and da, then row tile 2rp+1's
+  // 3. LDS reads of this chunk: row tile 2rp's B and scales, A and da, then row tile 2rp+1's
   v4u a, b0, b1;
   v4f d0, d1, d2, d3;
-  v2f s0, s1;
+  v2f t0, t1;
   asm volatile(
       "ds_read_b128 %0, %9 offset:%13\n\t"
       "ds_read_b64 %1, %10 offset:%14\n\t"
@@ -662,40 +698,60 @@ __device__ __forceinline__ void gemm_step(const GemmCtx& k, int64_t c, float (&a
       "ds_read_b128 %6, %12 offset:%19\n\t"
       "ds_read_b128 %7, %9 offset:%20\n\t"
       "ds_read_b64 %8, %10 offset:%21"
-      : "=&v"(b0), "=&v"(s0), "=&v"(a), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(b1),
-        "=&v"(s1)
+      : "=&v"(b0), "=&v"(t0), "=&v"(a), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(b1),
+        "=&v"(t1)
       : "v"(k.lanes.bb), "v"(k.lanes.ss), "v"(k.lanes.aa), "v"(k.lanes.dd), "n"(kCur),
         "n"(kCur), "n"(kCur), "n"(kCur), "n"(kCur + 16), "n"(kCur + 32), "n"(kCur + 48),
         "n"(kCur + 1024), "n"(kCur + 256)
       : "memory");
-  asm volatile("s_waitcnt lgkmcnt(2)"
-               : "+v"(b0), "+v"(s0), "+v"(a), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)::"memory");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(b0), "+v"(t0), "+v"(a), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3), "+v"(b1),
+                 "+v"(t1)::"memory");
+  // (d*sc0, d*sc1) and their bias products (exact, see above)
+  const v4f s0 = v4f{t0.x, t0.y, -kBiasF * t0.x, -kBiasF * t0.y};
+  const v4f s1 = v4f{t1.x, t1.y, -kBiasF * t1.x, -kBiasF * t1.y};
   const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
                          d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
   const long alo = (long)(((uint64_t)a.y << 32) | a.x);
   const long ahi = (long)(((uint64_t)a.w << 32) | a.z);
-  constexpr int kShift = LAYOUT == Q6K_LAYOUT_PACKED ? 2 : 0;
-  tile_chunk<SUBDOTS, kShift>(acc[0], bias, alo, ahi, b0, s0, dav, k.lane, c, k.T,
-                              k.R0 + 2 * k.rp, k.nchunk, k.dots);
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b1), "+v"(s1)::"memory");
-  tile_chunk<SUBDOTS, kShift>(acc[1], bias, alo, ahi, b1, s1, dav, k.lane, c, k.T,
-                              k.R0 + 2 * k.rp + 1, k.nchunk, k.dots);
+  v16i lo0, hi0, lo1, hi1;
+  tile_mfma(lo0, hi0, bias, alo, ahi, b0);
+  tile_mfma(lo1, hi1, bias, alo, ahi, b1);
+  // 4. this wave's loads of chunk c+1 have landed
+  wait_chunks<KRING - 2>(k.loads_a);
+  // 5. (tile 0's rescale, then the LDS reads of layout 0's codes of chunk c+1, whose registers
+  // are then live only beside tile 1's MFMA results)
+  constexpr int kShift = kPacked ? 2 : 0;
+  tile_rescale<SUBDOTS, kShift>(acc[0], lo0, hi0, s0, dav, k.lane, c, k.T, k.R0 + 2 * k.rp,
+                                k.nchunk, k.dots);
+  if (!SUBDOTS) pin_acc(acc[0]);
+  RawCodes raw;
+  if (kPacked) expand_read<kNext>(k.lanes, raw);
+  tile_rescale<SUBDOTS, kShift>(acc[1], lo1, hi1, s1, dav, k.lane, c, k.T, k.R0 + 2 * k.rp + 1,
+                                k.nchunk, k.dots);
+  if (!SUBDOTS) pin_acc(acc[1]);
+  // 6.
+  if (kPacked) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.s));
+    expand_write<kNext>(k.lanes, raw, k.lane);
+  }
 }
 
-// Chunks cb .. cb+KRING-1 (slots 0 .. KRING-1), stopping at the piece's end.
+// Chunks cb .. cb+KRING-1 (slots 0 .. KRING-1), stopping at the piece's end (a piece has a
+// multiple of 8 chunks, so a ring of 4 never stops early).
 template <int LAYOUT, bool SUBDOTS, int KRING, int J>
 struct GemmSteps {
-  __device__ __forceinline__ static void run(const GemmCtx& k, int64_t cb, float (&acc)[2][16],
-                                             const v16i& bias) {
-    if (cb + J >= k.c1) return;
+  __device__ __forceinline__ static void run(const GemmCtx& k, uint32_t cb, float (&acc)[2][16],
+                                             v16i& bias) {
+    if (8 % KRING != 0 && cb + J >= k.c1) return;
     gemm_step<LAYOUT, SUBDOTS, KRING, J>(k, cb + J, acc, bias);
     GemmSteps<LAYOUT, SUBDOTS, KRING, J + 1>::run(k, cb, acc, bias);
   }
 };
 template <int LAYOUT, bool SUBDOTS, int KRING>
 struct GemmSteps<LAYOUT, SUBDOTS, KRING, KRING> {
-  __device__ __forceinline__ static void run(const GemmCtx&, int64_t, float (&)[2][16],
-                                             const v16i&) {}
+  __device__ __forceinline__ static void run(const GemmCtx&, uint32_t, float (&)[2][16],
+                                             v16i&) {}
 };
 
 template <int LAYOUT, bool SUBDOTS>
@@ -710,6 +766,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
                                                       uint32_t pieces) {
   constexpr int kSlot = SlotSize<LAYOUT>::value;
   constexpr int kRing = RingSize<LAYOUT>::value;
+  constexpr bool kPacked = LAYOUT == Q6K_LAYOUT_PACKED;
   static_assert(Q6K_WG_PER_CU * kRing * kSlot <= 160 * 1024, "LDS budget");
   static_assert(kRing * kSlot + 1024 < 65536, "slot offsets fit the LDS immediate offset");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kSlot];
@@ -721,8 +778,8 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   k.tt = k.wave & 1;                                    // token tile of this wave in the workgroup
   k.rp = k.wave >> 1;                                   // row-tile pair of this wave
   const TileWork tw = tile_work<Q6K_GEMM01_XCD_ORDER != 0>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
-  const int64_t c0 = 8 * tw.s0;                         // this workgroup's chunks [c0, c1)
-  k.c1 = 8 * tw.s1;
+  const uint32_t c0 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * tw.s0));  // chunks [c0, c1)
+  k.c1 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * tw.s1));
   k.nchunk = nchunk;
   k.T = (int64_t)tw.bx * kWgTokTiles + k.tt;
   k.R0 = (int64_t)tw.by * 4;                            // the workgroup's first row tile
@@ -758,18 +815,25 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-  // Prologue: chunks c0 .. c0+kRing-2 in flight in slots 0 .. kRing-2; chunk c0 ready in slot 0.
+  // Prologue: chunks c0 .. c0+kRing-2 in flight in slots 0 .. kRing-2; this wave's share of chunk
+  // c0 landed (and, layout 0, expanded); the first step's meeting makes it every wave's.
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j)
     issue_chunk<LAYOUT>(smem + j * kSlot, k.src, c0 + j < k.c1 ? c0 + j : k.c1 - 1, wave, lane);
   wait_chunks<kRing - 2>(k.loads_a);
-  if (LAYOUT == Q6K_LAYOUT_PACKED) expand_slot<0>(k.lanes, lane);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (kPacked) {
+    RawCodes raw;
+    expand_read<0>(k.lanes, raw);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.s));
+    expand_write<0>(k.lanes, raw, lane);
+  }
 
-  for (int64_t cb = c0; cb < k.c1; cb += kRing) GemmSteps<LAYOUT, SUBDOTS, kRing, 0>::run(k, cb, acc, bias);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
+  for (uint32_t cb = c0; cb < k.c1; cb += kRing) GemmSteps<LAYOUT, SUBDOTS, kRing, 0>::run(k, cb, acc, bias);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // drain the trailing loads
 
   if (SUBDOTS) return;
+  // layout 0's accumulators hold 4 y (its B fragments are 4 x the centered codes)
+  const float out_scale = kPacked ? 0.25f : 1.0f;
   const int64_t T = k.T;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -782,9 +846,9 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
         // a lane's 16 values are one row of 16 tokens; an instruction covers 32 consecutive
         // rows of 2 tokens
         if (tw.split)
-          unsafeAtomicAdd(y + tok * ldy + mcol, acc[u][r]);
+          unsafeAtomicAdd(y + tok * ldy + mcol, acc[u][r] * out_scale);
         else
-          y[tok * ldy + mcol] = acc[u][r];
+          y[tok * ldy + mcol] = acc[u][r] * out_scale;
       }
     }
   }
@@ -823,9 +887,9 @@ constexpr float kFoldK = -65.0f * kBiasF;  // -(1.5*2^29 + 1.5*2^23), exact: 195
 
 // e = 64*E_hi + E_lo from the two biased digit products (exact, see above), in two phases of 16
 // independent operations (no VALU instruction depends on the one before it).
-__device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, const v16i& fl) {
-  float kk = kFoldK;
-  asm("" : "+v"(kk));  // a register operand: VOP2 adds without a literal
+// kk holds kFoldK in a register (VOP2 adds take no literal), set once per kernel.
+__device__ __forceinline__ void fold_digits(float (&e)[16], const v16i& fh, const v16i& fl,
+                                            float kk) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) e[r] = __int_as_float(fh[r]) + kk;
 #pragma unroll
@@ -877,6 +941,7 @@ struct FoldState {
   float da0, da1;    // their da (this lane's token)
   v4i blo[4], bhi[4];  // digit planes of chunk c in entry c % 4
   float d[16];       // d of this lane's 16 rows, for the super-block being finished
+  float kk;          // kFoldK, kept in a register
 };
 
 
@@ -981,6 +1046,7 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
                                         uint32_t xn, uint32_t dn, FoldState& st,
                                         const v16i& bias_lo, const v16i& bias_hi) {
   const int64_t c = 8 * s + J;
+  asm volatile("" : "+v"(st.kk));
   if (J == 0) {
     // both tiles have finished super-block s - 1: apply its d, then fetch super-block s's
     if (!DOTS) {
@@ -1020,7 +1086,7 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
   asm volatile("" : "+v"(fh), "+v"(fl));
   {
     float e[16];
-    fold_digits(e, fh, fl);
+    fold_digits(e, fh, fl, st.kk);
     fold_rescale<DOTS, J == 0>(st.sb[0], e, da0, k, c, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1029,7 +1095,7 @@ __device__ __forceinline__ void fold_step(const FoldCtx& k, int64_t s, uint32_t 
   asm volatile("" : "+v"(fh), "+v"(fl));
   {
     float e[16];
-    fold_digits(e, fh, fl);
+    fold_digits(e, fh, fl, st.kk);
     fold_rescale<DOTS, J == 0>(st.sb[1], e, da1, k, c, 1);
   }
 }
@@ -1089,6 +1155,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     for (int r = 0; r < 16; ++r) st.acc[u][r] = st.sb[u][r] = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) st.d[r] = 0.0f;
+  st.kk = kFoldK;
 
   // prologue: super-blocks s0 .. s0+2 of activations, chunks c0 .. c0+2 of digit planes; wait
   // for all of them, meet, read chunk c0's operands
