@@ -1169,7 +1169,9 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
   const uint32_t slot0 = (uint32_t)(s0 % kFRing) * kFSlot;
   fold_read<0, 0>(xb0 + slot0, db0 + slot0, st);
 
-  for (int64_t s = s0; s < s1; ++s) {
+  const uint32_t sb0 = __builtin_amdgcn_readfirstlane((uint32_t)s0),
+                 sb1 = __builtin_amdgcn_readfirstlane((uint32_t)s1);
+  for (uint32_t s = sb0; s < sb1; ++s) {
     const uint32_t cur = (uint32_t)(s % kFRing) * kFSlot;
     const uint32_t nxt = (uint32_t)((s + 1) % kFRing) * kFSlot;
     const uint32_t xb = xb0 + cur, dab = db0 + cur, xn = xb0 + nxt, dn = db0 + nxt;
@@ -1381,15 +1383,15 @@ struct Q4Src {
 // they are issued at iteration 8s - 3.
 template <int CI8>
 __device__ __forceinline__ void q4_issue(uint8_t* slot, uint8_t* sbuf, const Q4Src& src,
-                                         int64_t ci, int64_t c_end, int wave, int lane) {
+                                         uint32_t ci, uint32_t c_end, int wave, int lane) {
   const bool live = ci < c_end;
-  const uint32_t cl = (uint32_t)(live ? ci : c_end - 1);
+  const uint32_t cl = live ? ci : c_end - 1;
   const uint32_t l16 = lane * 16;
   bdma16(src.b, l16, cl * 1024, slot + kQ4SlotB + wave * 1024);
   if (wave < kWgTokTiles) bdma16(src.a, l16, cl * 1024, slot + kQ4SlotA + wave * 1024);
   if (CI8 == 0 && live) {
     uint8_t* par = sbuf + ((ci >> 3) & 1) * kQ4SbBytes;
-    const uint32_t s = (uint32_t)(ci >> 3);
+    const uint32_t s = ci >> 3;
     bdma16(src.sb, l16, s * 2048, par + kQ4SbSb + wave * 2048);
     bdma16(src.sb, l16 + 1024, s * 2048, par + kQ4SbSb + wave * 2048 + 1024);
     if (wave < kWgTokTiles) {
@@ -1411,7 +1413,8 @@ struct Q4Ctx {
   uint8_t* smem;
   uint8_t* sbuf;
   Q4Src src;
-  int64_t nchunk, c_end, n, m, tok_base, col;
+  uint32_t c_end;  // the piece's chunk end
+  int64_t nchunk, n, m, tok_base, col;
   DotsOut dots;
   uint32_t aa, bb, dd, ss;  // per-lane LDS addresses: A in slot 0, B in slot 0, da and SB (parity 0)
   int wave, lane;
@@ -1428,9 +1431,11 @@ __device__ __forceinline__ void q4_order(float (&v)[16]) {
 }
 
 template <bool DOTS, int CC>
-__device__ __forceinline__ void q4_step(const Q4Ctx& k, int64_t s, uint32_t par, const v16i& bias,
+__device__ __forceinline__ void q4_step(const Q4Ctx& k, uint32_t s, uint32_t par, v16i& bias,
                                         float (&acc)[2][16]) {
-  const int64_t c = 8 * s + CC;
+  const uint32_t c = 8 * s + CC;
+  // the MFMA bias stays in its 16 VGPRs (instead of being rebuilt from scalars every step)
+  asm volatile("" : "+v"(bias));
   q4_wait<kQ4Ring - 3>(k.loads_a);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   q4_issue<(CC + kQ4Ring - 1) % 8>(k.smem + ((CC + kQ4Ring - 1) % kQ4Ring) * kQ4Slot, k.sbuf,
@@ -1522,7 +1527,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
   k.src.sb = make_rsrc(reinterpret_cast<const uint8_t*>(wsb) + (R0 + k.wave) * nsb * 2048,
                        nsb * 2048);
   k.nchunk = nchunk;
-  k.c_end = 8 * tw.s1;
+  k.c_end = __builtin_amdgcn_readfirstlane((uint32_t)(8 * tw.s1));
   k.n = n;
   k.m = m;
   k.dots = dots;
@@ -1543,15 +1548,15 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
-  const int64_t c0 = 8 * tw.s0;
+  const uint32_t c0 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * tw.s0));
   q4_issue<0>(smem + 0 * kQ4Slot, k.sbuf, k.src, c0 + 0, k.c_end, k.wave, k.lane);
   q4_issue<1>(smem + 1 * kQ4Slot, k.sbuf, k.src, c0 + 1, k.c_end, k.wave, k.lane);
   q4_issue<2>(smem + 2 * kQ4Slot, k.sbuf, k.src, c0 + 2, k.c_end, k.wave, k.lane);
   q4_wait<kQ4Ring - 2>(k.loads_a);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  for (int64_t s = tw.s0; s < tw.s1; ++s) {
-    const uint32_t par = (uint32_t)(s & 1) * kQ4SbBytes;
+  for (uint32_t s = c0 / 8; s < k.c_end / 8; ++s) {
+    const uint32_t par = (s & 1) * kQ4SbBytes;
     q4_step<DOTS, 0>(k, s, par, bias, acc);
     q4_step<DOTS, 1>(k, s, par, bias, acc);
     q4_step<DOTS, 2>(k, s, par, bias, acc);
