@@ -373,12 +373,38 @@ struct DotsOut {
   int64_t tok0, ntok, row0, nrow;
 };
 
-// Slot of (tok, row)'s dots in the window, or nullptr outside it.
-__device__ __forceinline__ int32_t* dots_at(const DotsOut& w, int64_t tok, int64_t row,
-                                            int64_t per) {
+// One lane's dots slots along the 16 registers of a 32x32 tile: register r holds index
+// first + dt(r), dt(r) = 8*(r/4) + r%4, of the varying dimension (tokens when VARY_TOK, else rows);
+// the lane's other index is fixed.  The offsets pass through an empty statement at every chunk,
+// so the compiler forms the 16 slot addresses (and their bounds tests) where they are stored
+// instead of holding them all live across the chunk loop.
+struct DotsRun {
+  int64_t off;     // window offset of register 0's slot, chunk term included
+  int64_t vary;    // varying index of register 0 inside the window (may lie outside it)
+  int64_t stride;  // window offset between consecutive values of the varying index
+  int64_t limit;   // window extent along the varying index
+  bool fixed_ok;   // the fixed index lies inside the window
+};
+
+template <bool VARY_TOK>
+__device__ __forceinline__ DotsRun dots_run(const DotsOut& w, int64_t tok, int64_t row,
+                                            int64_t per, int64_t cterm) {
+  DotsRun d;
   const int64_t ti = tok - w.tok0, ri = row - w.row0;
-  if ((uint64_t)ti >= (uint64_t)w.ntok || (uint64_t)ri >= (uint64_t)w.nrow) return nullptr;
-  return w.p + (ti * w.nrow + ri) * per;
+  d.off = (ti * w.nrow + ri) * per + cterm;
+  d.vary = VARY_TOK ? ti : ri;
+  d.stride = VARY_TOK ? w.nrow * per : per;
+  d.limit = VARY_TOK ? w.ntok : w.nrow;
+  d.fixed_ok = VARY_TOK ? (uint64_t)ri < (uint64_t)w.nrow : (uint64_t)ti < (uint64_t)w.ntok;
+  asm volatile("" : "+v"(d.off), "+v"(d.vary));
+  return d;
+}
+
+// Register r's slot, or nullptr outside the window.
+__device__ __forceinline__ int32_t* dots_slot(const DotsOut& w, const DotsRun& d, int r) {
+  const int dt = 8 * (r >> 2) + (r & 3);
+  if (!d.fixed_ok || (uint64_t)(d.vary + dt) >= (uint64_t)d.limit) return nullptr;
+  return w.p + d.off + dt * d.stride;
 }
 
 // The result is uniform across the workgroup; the divisions in it run on the vector ALU, so each
@@ -618,14 +644,13 @@ __device__ __forceinline__ void tile_rescale(float (&acc)[16], const v16i& lo_d,
                                              const DotsOut& dots) {
   if (SUBDOTS) {
     const int p = lane & 31, g = lane >> 5;
-    const int64_t mcol = R * kTile + p;
+    const DotsRun d = dots_run<true>(dots, T * kTile + 4 * g, R * kTile + p, 2 * nchunk, 2 * c);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-      int32_t* o = dots_at(dots, tok, mcol, 2 * nchunk);
+      int32_t* o = dots_slot(dots, d, r);
       if (o) {
-        o[2 * c] = (lo_d[r] - kBiasI) >> SHIFT;
-        o[2 * c + 1] = (hi_d[r] - kBiasI) >> SHIFT;
+        o[0] = (lo_d[r] - kBiasI) >> SHIFT;
+        o[1] = (hi_d[r] - kBiasI) >> SHIFT;
       }
     }
   } else {
@@ -1021,12 +1046,11 @@ __device__ __forceinline__ void fold_rescale(float (&sb)[16], const float (&e)[1
                                            const FoldCtx& k, int64_t c, int u) {
   if (DOTS) {
     const int g = k.lane >> 5;
-    const int64_t tok = k.tok0 + kTile * u;
+    const DotsRun d = dots_run<false>(k.dots, k.tok0 + kTile * u, k.row0 + 4 * g, k.nchunk, c);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = k.row0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      int32_t* o = dots_at(k.dots, tok, row, k.nchunk);
-      if (o) o[c] = (int32_t)e[r];
+      int32_t* o = dots_slot(k.dots, d, r);
+      if (o) *o = (int32_t)e[r];
     }
   } else if (FIRST) {
 #pragma unroll
@@ -1480,12 +1504,11 @@ __device__ __forceinline__ void q4_step(const Q4Ctx& k, uint32_t s, uint32_t par
     const v2f pr = u ? p1 : p0;
     if (DOTS) {
       const int g = k.lane >> 5;
-      const int64_t col = k.col + u * kTile;
+      const DotsRun d = dots_run<true>(k.dots, k.tok_base + 4 * g, k.col + u * kTile, k.nchunk, c);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t tok = k.tok_base + 8 * (r >> 2) + 4 * g + (r & 3);
-        int32_t* o = dots_at(k.dots, tok, col, k.nchunk);
-        if (o) o[c] = f[r] - kBiasI;
+        int32_t* o = dots_slot(k.dots, d, r);
+        if (o) *o = f[r] - kBiasI;
       }
     } else {
       const float nb = -kBiasF * pr.x;
