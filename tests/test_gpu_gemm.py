@@ -358,3 +358,19 @@ def test_repeatability_whole_and_split_tiles():
             for r in runs[1:]:
                 diff = np.abs(r.astype(np.float64) - runs[0])
                 assert (diff <= 1e-6 * t_ref).all(), float((diff / np.maximum(t_ref, 1e-300)).max())
+
+
+def test_packed_layout_equals_expanded_bit_for_bit():
+    """Layout 0 stages 4 (q - 32) and d*sc, so its MFMAs yield 4 D, every rescale product and
+    accumulator is exactly 4 times layout 1's (scaling by a power of two commutes with rounding),
+    and its store multiplies by 1/4: on whole tiles (no split along k) the two layouts must agree
+    bit for bit.  768 tiles of 64 x 128 fill the grid of 3 workgroups per CU without a split on
+    any device of 256 to 511 CUs."""
+    import gpu_util
+    n, m, k = 2048, 3072, 512
+    raw = synthetic.weights(m, k, seed=71, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=72, kind="outlier")
+    xq, da = gpu_util.quantize(x)
+    y0 = gpu_util.gemm(xq, da, n, gpu_util.expand(raw, m, k, 0), 0, m, k)
+    y1 = gpu_util.gemm(xq, da, n, gpu_util.expand(raw, m, k, 1), 1, m, k)
+    np.testing.assert_array_equal(y0.view(np.uint32), y1.view(np.uint32))
