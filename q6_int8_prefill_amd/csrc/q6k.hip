@@ -112,26 +112,28 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
   const int g = (kk >> 3) & 1, h = kk >> 4;
   __shared__ __attribute__((aligned(16))) uint8_t codes[8 * 1024];
   __shared__ __attribute__((aligned(16))) float scales[8 * 32];
-  // all eight loads first (eight rows in flight per wave), then the arithmetic
-  float4 v[8];
+  // all loads first (eight rows, with SWIGLU sixteen, in flight per wave), then the arithmetic.
+  // The loads are unconditional, from the row and chunk clamped into the input, and lanes outside
+  // it take zeros afterwards: a load under a branch would make the compiler wait for it.
+  float4 v[8], u[8];
+  const int64_t cl = live_c ? c : nchunk - 1;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t tok = T * kTile + 8 * wave + j;
-    v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tok < n && live_c) v[j] = *reinterpret_cast<const float4*>(x + tok * ldx + c * 32 + kk);
+    const int64_t off = (tok < n ? tok : n - 1) * ldx + cl * 32 + kk;
+    v[j] = *reinterpret_cast<const float4*>(x + off);
+    if (SWIGLU) u[j] = *reinterpret_cast<const float4*>(up + off);
   }
-  if (SWIGLU) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t tok = T * kTile + 8 * wave + j;
-      if (tok < n && live_c) {
-        const float4 u = *reinterpret_cast<const float4*>(up + tok * ldx + c * 32 + kk);
-        v[j].x = swiglu_f32(v[j].x, u.x);
-        v[j].y = swiglu_f32(v[j].y, u.y);
-        v[j].z = swiglu_f32(v[j].z, u.z);
-        v[j].w = swiglu_f32(v[j].w, u.w);
-      }
+  for (int j = 0; j < 8; ++j) {
+    const int64_t tok = T * kTile + 8 * wave + j;
+    if (SWIGLU) {
+      v[j].x = swiglu_f32(v[j].x, u[j].x);
+      v[j].y = swiglu_f32(v[j].y, u[j].y);
+      v[j].z = swiglu_f32(v[j].z, u[j].z);
+      v[j].w = swiglu_f32(v[j].w, u[j].w);
     }
+    if (!(tok < n && live_c)) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
