@@ -32,7 +32,7 @@ holding clean lines: evicting the write's dirty lines inside the timed span woul
 write-back instead).  --swiglu replaces the prepass by the fused producer q6k_swiglu_quantize_act
 reading the two SwiGLU factors, and also times the unfused pair (q6k_swiglu_f32 writing h, then
 q6k_quantize_act).  --weights q4k runs the q4_K variant on the same shapes: step =
-q6k_quantize_act + q4k_act_sums + q4k_gemm.
+q4k_quantize_act (codes, da and das in one pass) + q4k_gemm.
 
 --ceilings runs the microbenchmarks of libq6k_ceilings.so instead (MFMA issue rates, vector-ALU
 issue rates at 1, 2, 4 and 8 waves per SIMD, the GEMMs' tile operation without memory traffic,
@@ -381,12 +381,14 @@ class Acts:
         self.das = torch.empty(db // 4, dtype=torch.float32, device=dev) if q4 else None
 
     def quantize(self):
-        if self.up is None:
-            self.q6k.q6k_quantize_act(self.x, self.xq, self.da)
-        else:
+        if self.up is not None:
             self.q6k.q6k_swiglu_quantize_act(self.x, self.up, self.xq, self.da)
-        if self.das is not None:
-            self.q6k.q4k_act_sums(self.xq, self.da, self.n, self.k, self.das)
+            if self.das is not None:
+                self.q6k.q4k_act_sums(self.xq, self.da, self.n, self.k, self.das)
+        elif self.das is not None:
+            self.q6k.q4k_quantize_act(self.x, self.xq, self.da, self.das)
+        else:
+            self.q6k.q6k_quantize_act(self.x, self.xq, self.da)
 
     def bytes(self):
         """prepass algorithmic bytes: f32 input(s) + int8 codes + f32 scales (and das)"""
@@ -658,7 +660,7 @@ def main(argv=None):
             config.update(producer="fused SwiGLU (gate, up f32 inputs)",
                           step="q6k_swiglu_quantize_act + q6k_gemm")
         if q4:
-            config.update(weights="q4_K", step="q6k_quantize_act + q4k_act_sums + q4k_gemm")
+            config.update(weights="q4_K", step="q4k_quantize_act + q4k_gemm")
 
     out = {
         "metric": METRIC,

@@ -18,9 +18,9 @@
  * element 64g + l in its low nibble and 64g + 32 + l in its high nibble; w = d*sc*q - dmin*m.
  *
  * Conventions, status codes and the tiled activation layout (xq, da) are those of q6k.h: the
- * activations are quantized by q6k_quantize_act (or q6k_swiglu_quantize_act), then
- * q4k_act_sums adds das = da * S per (token, chunk), S the sum of the chunk's 32 codes, in the
- * tiled order of da.  Every pointer is a device pointer owned by the caller; calls are
+ * activations are quantized by q4k_quantize_act, which also writes das = da * S per (token,
+ * chunk), S the sum of the chunk's 32 codes, in the tiled order of da; or by q6k_quantize_act (or
+ * q6k_swiglu_quantize_act) followed by q4k_act_sums, which adds das to existing xq and da.  Every pointer is a device pointer owned by the caller; calls are
  * asynchronous on `stream`; arguments are checked on the host and nothing is launched on error.
  *
  * Prepared weights (q4k_expand_weights), rows padded to MP = m rounded up to 128:
@@ -49,6 +49,16 @@ size_t q4k_weight_bytes(int64_t m, int64_t k);
  * 16-byte aligned.  Output: the codes and pairs above, w_out_bytes >= q4k_weight_bytes(m, k). */
 q6k_status q4k_expand_weights(const void* w_raw, int64_t m, int64_t k, void* w_out,
                               size_t w_out_bytes, void* stream);
+
+/* The q4_K prepass in one pass over x: q6k_quantize_act's xq and da (same arguments and rules)
+ * and das = da * S, S the sum of each (token, chunk)'s 32 codes, with the size and order of da;
+ * das 16-byte aligned, das_bytes >= da's size (Q6K_ESIZE otherwise).  The per-chunk sum travels
+ * with the scale as in "r38 — q6_K BT-style raw-byte mma kernel (LANDED)", sec. 2.2 (q4_K's
+ * rescale needs it).  xq, da and das equal those of q6k_quantize_act followed by q4k_act_sums,
+ * bit for bit. */
+q6k_status q4k_quantize_act(const float* x, int64_t n, int64_t k, int64_t ldx, void* xq,
+                            size_t xq_bytes, float* da, size_t da_bytes, float* das,
+                            size_t das_bytes, void* stream);
 
 /* das = da * S for the tiled activations of q6k_quantize_act (same n, k); das has the size and
  * order of da (q6k_act_bytes). */

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     q4k_gemm,
     q4k_gemm_dots,
     q4k_launches,
+    q4k_quantize_act,
     q4k_weight_bytes,
     LAYOUT_EXPANDED,
     LAYOUT_FOLDED,

@@ -41,6 +41,8 @@ _lib.q4k_weight_bytes.restype = _sz
 _lib.q4k_weight_bytes.argtypes = [_i64, _i64]
 _lib.q4k_expand_weights.restype = _int
 _lib.q4k_expand_weights.argtypes = [_p, _i64, _i64, _p, _sz, _p]
+_lib.q4k_quantize_act.restype = _int
+_lib.q4k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p, _sz, _p]
 _lib.q4k_act_sums.restype = _int
 _lib.q4k_act_sums.argtypes = [_p, _p, _i64, _i64, _p, _sz, _p]
 _lib.q4k_gemm.restype = _int
@@ -58,7 +60,7 @@ _lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
 EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_swiglu_quantize_act", "q6k_swiglu_f32",
            "q6k_weight_bytes", "q6k_expand_weights",
            "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots", "q6k_strerror", "q6k_stats",
-           "q4k_weight_bytes", "q4k_expand_weights", "q4k_act_sums", "q4k_gemm", "q4k_gemm_dots",
+           "q4k_weight_bytes", "q4k_expand_weights", "q4k_quantize_act", "q4k_act_sums", "q4k_gemm", "q4k_gemm_dots",
            "q4k_launches")
 
 
@@ -271,6 +273,26 @@ def q4k_expand_weights(w_raw, m, k, w_out, stream=None):
         raise ValueError("raw weight buffer too small")
     _check(_lib.q4k_expand_weights(_ptr(w_raw), m, k, _ptr(w_out), _nbytes(w_out),
                                    _stream(stream)), "q4k_expand_weights")
+
+
+def q4k_quantize_act(x, xq, da, das, n=None, k=None, ldx=None, stream=None):
+    """x f32 [n][ldx] (device) -> tiled xq, da and das = da * (sum of each chunk's codes)."""
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [n][ldx]")
+    n = x.shape[0] if n is None else n
+    k = x.shape[1] if k is None else k
+    ldx = x.stride(0) if ldx is None else ldx
+    if x.numel() and x.stride(1) != 1:
+        raise ValueError("x must be row-major")
+    if x.numel() and (n > x.shape[0] or k > x.shape[1]):
+        raise ValueError("n, k exceed the shape of x")
+    _rows_fit("x", x, n, k, ldx)
+    _flat(xq=xq, da=da, das=das)
+    _check(_lib.q4k_quantize_act(_ptr(x), n, k, ldx, _ptr(xq), _nbytes(xq), _ptr(da),
+                                 _nbytes(da), _ptr(das), _nbytes(das), _stream(stream)),
+           "q4k_quantize_act")
 
 
 def q4k_act_sums(xq, da, n, k, das, stream=None):

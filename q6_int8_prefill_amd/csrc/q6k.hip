@@ -94,12 +94,15 @@ __device__ __forceinline__ int quant_code(float x, float s, float r, bool fast) 
   return (int)fminf(fmaxf(q, -127.0f), 127.0f);
 }
 
-template <bool SWIGLU>
+// SUMS: also write das = da * S per (token, chunk), S the sum of the chunk's 32 codes, in the order
+// of da (the per-chunk activation sum the q4_K rescale needs next to da).
+template <bool SWIGLU, bool SUMS>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x,
                                                            const float* __restrict__ up,
                                                            int64_t n, int64_t ldx, int64_t nchunk,
                                                            uint8_t* __restrict__ xq,
-                                                           float* __restrict__ da, int64_t t0) {
+                                                           float* __restrict__ da,
+                                                           float* __restrict__ das, int64_t t0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // workgroup order: the 8-chunk block of k varies fastest, so workgroups running together read
   // consecutive kilobytes of the same rows (sequential DRAM streams) rather than 1 KiB pieces of
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
   const int g = (kk >> 3) & 1, h = kk >> 4;
   __shared__ __attribute__((aligned(16))) uint8_t codes[8 * 1024];
   __shared__ __attribute__((aligned(16))) float scales[8 * 32];
+  __shared__ __attribute__((aligned(16))) float sums[SUMS ? 8 * 32 : 4];
   // all loads first (eight rows, with SWIGLU sixteen, in flight per wave), then the arithmetic.
   // The loads are unconditional, from the row and chunk clamped into the input, and lanes outside
   // it take zeros afterwards: a load under a branch would make the compiler wait for it.
@@ -156,7 +160,16 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
     *reinterpret_cast<uint32_t*>(codes + (lane >> 3) * 1024 + (p + 32 * g) * kFragBytes + 8 * h +
                                  (kk & 7)) = pack4(q0, q1, q2, q3);
     // token p = 8*qq + 4*gg + r  ->  float slot 16*gg + 4*qq + r
-    if ((lane & 7) == 0) scales[(lane >> 3) * 32 + 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3)] = scale;
+    const int slot = (lane >> 3) * 32 + 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3);
+    if ((lane & 7) == 0) scales[slot] = scale;
+    if (SUMS) {
+      // the chunk's 32 codes are 4 per lane in 8 lanes: the same three exchanges as amax
+      int sum = q0 + q1 + q2 + q3;
+      sum += __builtin_amdgcn_mov_dpp(sum, 0xB1, 0xF, 0xF, true);
+      sum += __builtin_amdgcn_mov_dpp(sum, 0x4E, 0xF, 0xF, true);
+      sum += __builtin_amdgcn_mov_dpp(sum, 0x141, 0xF, 0xF, true);
+      if ((lane & 7) == 0) sums[slot] = scale * (float)sum;
+    }
   }
   __syncthreads();
   // coalesced stores: thread t writes 32 bytes of chunk t / 32's 1 KiB block; threads 0..63 the
@@ -174,6 +187,11 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
     if (cd < nchunk)
       reinterpret_cast<float4*>(da + (T * nchunk + cd) * 32)[t & 7] =
           reinterpret_cast<const float4*>(scales)[t];
+  } else if (SUMS && t < 128) {
+    const int64_t cd = kb * 8 + ((t - 64) >> 3);
+    if (cd < nchunk)
+      reinterpret_cast<float4*>(das + (T * nchunk + cd) * 32)[t & 7] =
+          reinterpret_cast<const float4*>(sums)[t - 64];
   }
 }
 
@@ -1797,28 +1815,30 @@ q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t 
   return st;
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool SUMS>
 q6k_status quantize_common(const float* x, const float* up, int64_t n, int64_t k, int64_t ldx,
-                           void* xq, size_t xq_bytes, float* da, size_t da_bytes, void* stream) {
+                           void* xq, size_t xq_bytes, float* da, size_t da_bytes, float* das,
+                           size_t das_bytes, void* stream) {
   if (n < 0) return Q6K_EINVAL;
   if (k <= 0 || k % 256) return Q6K_ESHAPE;
   size_t need_x, need_d;
   if (!act_sizes(n, k, &need_x, &need_d)) return Q6K_ESIZE;
   if (n == 0) return Q6K_OK;
-  if (!x || !xq || !da) return Q6K_EINVAL;
+  if (!x || !xq || !da || (SUMS && !das)) return Q6K_EINVAL;
   if (ldx < k) return Q6K_EINVAL;
-  if (!aligned16(x) || ldx % 4 || !aligned16(xq) || !aligned16(da)) return Q6K_EALIGN;
-  if (xq_bytes < need_x || da_bytes < need_d) return Q6K_ESIZE;
+  if (!aligned16(x) || ldx % 4 || !aligned16(xq) || !aligned16(da) || (SUMS && !aligned16(das)))
+    return Q6K_EALIGN;
+  if (xq_bytes < need_x || da_bytes < need_d || (SUMS && das_bytes < need_d)) return Q6K_ESIZE;
   const int64_t np = round_up(n, kWgTok);
   const int64_t nchunk = k / 32;
   const int64_t ntt = np / kTile, nkb = (nchunk + 7) / 8;
   if (nkb > INT32_MAX) return Q6K_ESIZE;
   // grid x = 8-chunk blocks of k, y = token tiles (at most 65535 per launch)
   for (int64_t t0 = 0; t0 < ntt; t0 += 65535)
-    hipLaunchKernelGGL(quantize_act_kernel<SWIGLU>,
+    hipLaunchKernelGGL((quantize_act_kernel<SWIGLU, SUMS>),
                        dim3((unsigned)nkb, (unsigned)std::min<int64_t>(65535, ntt - t0)),
                        dim3(256), 0, static_cast<hipStream_t>(stream), x, up, n, ldx, nchunk,
-                       static_cast<uint8_t*>(xq), da, t0);
+                       static_cast<uint8_t*>(xq), da, das, t0);
   return launch_status();
 }
 
@@ -1903,6 +1923,13 @@ q6k_status q4k_expand_weights(const void* w_raw, int64_t m, int64_t k, void* w_o
   return launch_status();
 }
 
+q6k_status q4k_quantize_act(const float* x, int64_t n, int64_t k, int64_t ldx, void* xq,
+                            size_t xq_bytes, float* da, size_t da_bytes, float* das,
+                            size_t das_bytes, void* stream) {
+  return quantize_common<false, true>(x, nullptr, n, k, ldx, xq, xq_bytes, da, da_bytes, das,
+                                      das_bytes, stream);
+}
+
 q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, float* das,
                         size_t das_bytes, void* stream) {
   if (n < 0) return Q6K_EINVAL;
@@ -1952,7 +1979,8 @@ size_t q6k_act_bytes(int64_t n, int64_t k, size_t* da_bytes) {
 
 q6k_status q6k_quantize_act(const float* x, int64_t n, int64_t k, int64_t ldx, void* xq,
                             size_t xq_bytes, float* da, size_t da_bytes, void* stream) {
-  return quantize_common<false>(x, nullptr, n, k, ldx, xq, xq_bytes, da, da_bytes, stream);
+  return quantize_common<false, false>(x, nullptr, n, k, ldx, xq, xq_bytes, da, da_bytes, nullptr,
+                                      0, stream);
 }
 
 q6k_status q6k_swiglu_quantize_act(const float* gate, const float* up, int64_t n, int64_t k,
@@ -1960,7 +1988,8 @@ q6k_status q6k_swiglu_quantize_act(const float* gate, const float* up, int64_t n
                                    size_t da_bytes, void* stream) {
   if (n > 0 && !up) return Q6K_EINVAL;
   if (n > 0 && up && !aligned16(up)) return Q6K_EALIGN;
-  return quantize_common<true>(gate, up, n, k, ld, xq, xq_bytes, da, da_bytes, stream);
+  return quantize_common<true, false>(gate, up, n, k, ld, xq, xq_bytes, da, da_bytes, nullptr, 0,
+                                     stream);
 }
 
 q6k_status q6k_swiglu_f32(const float* gate, const float* up, int64_t n, int64_t k, int64_t ld,

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     from q6_int8_prefill_amd import _lib as binding
     assert sorted(binding.EXPORTS) == names
     L = lib()
@@ -90,6 +90,20 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 ])
 def test_quantize_act_errors(args, status):
     assert lib().q6k_quantize_act(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 4, 300, 300, FAKE, 1 << 30, FAKE, 1 << 30, FAKE, 1 << 30, None), -2),   # k % 256
+    ((FAKE, -1, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, FAKE, 1 << 30, None), -1),  # n < 0
+    ((FAKE, 4, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, None, 1 << 30, None), -1),   # null das
+    ((FAKE, 4, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, FAKE + 4, 1 << 30, None), -3),  # das align
+    ((FAKE, 4, 256, 256, FAKE, 1 << 30, FAKE, 1 << 30, FAKE, 100, None), -4),       # das too small
+    ((FAKE, 4, 256, 256, FAKE, 1 << 30, FAKE, 100, FAKE, 1 << 30, None), -4),       # da too small
+    ((FAKE, 4, 256, 255, FAKE, 1 << 30, FAKE, 1 << 30, FAKE, 1 << 30, None), -1),   # ldx < k
+    ((None, 0, 256, 256, None, 0, None, 0, None, 0, None), 0),                      # empty: no-op
+])
+def test_q4k_quantize_act_errors(args, status):
+    assert lib().q4k_quantize_act(*args) == status
 
 
 @pytest.mark.parametrize("args,status", [

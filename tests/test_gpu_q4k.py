@@ -75,6 +75,32 @@ def test_act_sums(n, k):
     assert (got[n:] == 0).all()
 
 
+@pytest.mark.parametrize("n,k", [(64, 512), (65, 256), (200, 1024), (1, 256)])
+def test_fused_prepass_equals_quantize_then_sums(n, k):
+    """q4k_quantize_act writes the xq and da of q6k_quantize_act and the das of q4k_act_sums, bit
+    for bit (the same codes, scales and one f32 product per (token, chunk)), and das matches the
+    oracle's da * S."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    print(f"q4k fused prepass n={n} k={k}", flush=True)
+    x = synthetic.activations(n, k, seed=n + 3, kind="outlier")
+    xq, da, das = prep_acts(x)
+    xb, db = q6k.q6k_act_bytes(n, k)
+    xq2 = torch.full((xb,), 0x5A, dtype=torch.uint8, device=gpu_util.DEV)
+    da2 = torch.full((db // 4,), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+    das2 = torch.full_like(da2, float("nan"))
+    q6k.q4k_quantize_act(torch.from_numpy(x).to(gpu_util.DEV), xq2, da2, das2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xq2.cpu().numpy(), xq.cpu().numpy())
+    np.testing.assert_array_equal(da2.cpu().numpy().view(np.uint32), da.cpu().numpy().view(np.uint32))
+    np.testing.assert_array_equal(das2.cpu().numpy().view(np.uint32), das.cpu().numpy().view(np.uint32))
+    xq_ref, da_ref = oracle.quantize(x)
+    want = (da_ref * oracle.q4_chunksums(xq_ref).astype(np.float32)).astype(np.float32)
+    got = untile_da(das2.cpu().numpy(), n, k)
+    np.testing.assert_array_equal(got[:n].view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("n,m,k", [(64, 256, 512), (65, 40, 512), (1, 1, 256), (129, 130, 768)])
 def test_dots_bit_exact(n, m, k):
     import torch
