@@ -496,9 +496,9 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
 //      wave is done with chunk c-1, so that slot is free;
 //   2. issue the loads of chunk c+kRing-1 into the freed slot;
 //   3. read chunk c's fragments and scales from LDS, start the four MFMAs;
-//   4. wait for this wave's own loads of chunk c+1 (kRing-2 newer chunks may stay in flight) and,
-//      on layout 0, start the LDS reads of its packed codes;
-//   5. rescale chunk c (the LDS reads of step 4 land meanwhile);
+//   4. wait for this wave's own loads of chunk c+1 (kRing-2 newer chunks may stay in flight);
+//   5. rescale chunk c: tile 0, then (layout 0) start the LDS reads of this wave's packed codes
+//      of chunk c+1, then tile 1 (the reads land meanwhile);
 //   6. layout 0: expand row tile w of chunk c+1 into B fragments of 4 x the centered int8 codes
 //      and the pair (d*sc0, d*sc1) in the slot.
 // The chunk loop is unrolled over the ring, so every slot address is a per-lane base register
@@ -602,7 +602,7 @@ __device__ __forceinline__ void wait_chunks(bool loads_a) {
 struct GemmLanes {
   uint32_t aa, dd, bb, ss;         // reads: A fragment, da, B fragments, scales
   uint32_t raw, rsc, bdst, sdst;   // layout 0 expand: packed codes and scale words in, B and
-                                   // scale quads out (row tile `wave`)
+                                   // (d*sc0, d*sc1) pairs out (row tile `wave`)
 };
 
 // Layout 0: this lane's packed codes and its row's raw scale word of row tile `wave` in the slot at
