@@ -1,5 +1,5 @@
-"""The hot path recorded in a HIP graph (torch.cuda.graph) and replayed: the prepass and the layout-2
-GEMM with its split-k last round (a zeroing kernel, then float atomics) launch only kernels on
+"""The hot path recorded in a HIP graph (torch.cuda.graph) and replayed: the prepass and the GEMM
+(every layout) with its split-k last round (a zeroing kernel, then float atomics) launch only kernels on
 the caller's stream (no memset nodes), so a captured step replays to the eager results.  Each
 replay follows eager work of the program's own that clobbers every output, and is checked: codes
 and scales byte for byte against the eager run and the oracle, outputs against the eager run up
@@ -14,16 +14,17 @@ from layouts import untile_da, untile_xq
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("layout", [2, 1, 0])
 @pytest.mark.parametrize("n,m,k", [(2176, 4096, 512), (200, 384, 2048)])
-def test_captured_step_replays(n, m, k):
+def test_captured_step_replays(n, m, k, layout):
     import torch
     import gpu_util
     import q6_int8_prefill_amd as q6k
-    print(f"graph replay n={n} m={m} k={k}", flush=True)
+    print(f"graph replay layout={layout} n={n} m={m} k={k}", flush=True)
     dev = gpu_util.DEV
     raw = synthetic.weights(m, k, seed=n + 5, sc_lo=-128, sc_hi=127)
     x = synthetic.activations(n, k, seed=n + 6, kind="outlier")
-    w = gpu_util.expand(raw, m, k, 2)
+    w = gpu_util.expand(raw, m, k, layout)
     xg = torch.from_numpy(x).to(dev)
     xb, db = q6k.q6k_act_bytes(n, k)
     xq = torch.zeros(xb, dtype=torch.uint8, device=dev)
@@ -32,7 +33,7 @@ def test_captured_step_replays(n, m, k):
 
     def step():
         q6k.q6k_quantize_act(xg, xq, da)
-        q6k.q6k_gemm(xq, da, n, w, 2, m, k, y)
+        q6k.q6k_gemm(xq, da, n, w, layout, m, k, y)
 
     # eager reference of the same calls
     step()
@@ -73,3 +74,60 @@ def test_captured_step_replays(n, m, k):
     np.testing.assert_array_equal(untile_xq(xq.cpu().numpy(), n, k)[:n], xq_ref)
     np.testing.assert_array_equal(untile_da(da.cpu().numpy(), n, k)[:n].view(np.uint32),
                                   da_ref.view(np.uint32))
+
+
+def test_captured_q4k_step_replays():
+    """The q4_K step (its one-pass prepass, then the GEMM with a split-k last round) captured and
+    replayed after eager clobbering, as above."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 200, 384, 2048
+    print(f"graph replay q4k n={n} m={m} k={k}", flush=True)
+    dev = gpu_util.DEV
+    raw = synthetic.weights_q4k(m, k, seed=41)
+    x = synthetic.activations(n, k, seed=42, kind="outlier")
+    w = torch.empty(q6k.q4k_weight_bytes(m, k), dtype=torch.uint8, device=dev)
+    q6k.q4k_expand_weights(torch.from_numpy(np.ascontiguousarray(raw).reshape(-1)).to(dev), m, k, w)
+    xg = torch.from_numpy(x).to(dev)
+    xb, db = q6k.q6k_act_bytes(n, k)
+    xq = torch.zeros(xb, dtype=torch.uint8, device=dev)
+    da = torch.zeros(db // 4, dtype=torch.float32, device=dev)
+    das = torch.zeros(db // 4, dtype=torch.float32, device=dev)
+    y = torch.zeros((n, m), dtype=torch.float32, device=dev)
+
+    def step():
+        q6k.q4k_quantize_act(xg, xq, da, das)
+        q6k.q4k_gemm(xq, da, das, n, w, m, k, y)
+
+    step()
+    torch.cuda.synchronize()
+    xq_e, da_e, das_e, y_e = xq.clone(), da.clone(), das.clone(), y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    xq_ref, da_ref = oracle.quantize(x)
+    y_ref, t_ref = oracle.q4_gemm(xq_ref, da_ref, raw, m)
+    for rep in range(3):
+        xq.fill_(0xA5)
+        da.fill_(float("nan"))
+        das.fill_(float("nan"))
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xq, xq_e), rep
+        assert torch.equal(da.view(torch.int32), da_e.view(torch.int32)), rep
+        assert torch.equal(das.view(torch.int32), das_e.view(torch.int32)), rep
+        got = y.cpu().numpy()
+        diff = np.abs(got.astype(np.float64) - y_e.cpu().numpy())
+        assert (diff <= 1e-6 * t_ref + 1e-30).all(), rep
+        ok, worst = gpu_util.within_tolerance(got, y_ref, t_ref)
+        assert ok, f"replay {rep}: worst |err|/T = {worst}"
