@@ -136,8 +136,8 @@ def q6k_weight_bytes(m, k, layout):
     return int(_lib.q6k_weight_bytes(int(m), int(k), int(layout)))
 
 
-def q6k_quantize_act(x, xq, da, n=None, k=None, ldx=None, stream=None):
-    """x f32 [n][ldx] (device) -> tiled xq (uint8 buffer) and da (f32 buffer)."""
+def _x_operand(x, n, k, ldx):
+    """Shape checks of an f32 [n][ldx] activation operand; returns (n, k, ldx)."""
     if x.dtype != torch.float32:
         raise TypeError("x must be float32")
     if x.dim() != 2:
@@ -150,6 +150,12 @@ def q6k_quantize_act(x, xq, da, n=None, k=None, ldx=None, stream=None):
     if x.numel() and (n > x.shape[0] or k > x.shape[1]):
         raise ValueError("n, k exceed the shape of x")
     _rows_fit("x", x, n, k, ldx)
+    return n, k, ldx
+
+
+def q6k_quantize_act(x, xq, da, n=None, k=None, ldx=None, stream=None):
+    """x f32 [n][ldx] (device) -> tiled xq (uint8 buffer) and da (f32 buffer)."""
+    n, k, ldx = _x_operand(x, n, k, ldx)
     _flat(xq=xq, da=da)
     _check(_lib.q6k_quantize_act(_ptr(x), n, k, ldx, _ptr(xq), _nbytes(xq), _ptr(da),
                                  _nbytes(da), _stream(stream)), "q6k_quantize_act")
@@ -277,18 +283,7 @@ def q4k_expand_weights(w_raw, m, k, w_out, stream=None):
 
 def q4k_quantize_act(x, xq, da, das, n=None, k=None, ldx=None, stream=None):
     """x f32 [n][ldx] (device) -> tiled xq, da and das = da * (sum of each chunk's codes)."""
-    if x.dtype != torch.float32:
-        raise TypeError("x must be float32")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D [n][ldx]")
-    n = x.shape[0] if n is None else n
-    k = x.shape[1] if k is None else k
-    ldx = x.stride(0) if ldx is None else ldx
-    if x.numel() and x.stride(1) != 1:
-        raise ValueError("x must be row-major")
-    if x.numel() and (n > x.shape[0] or k > x.shape[1]):
-        raise ValueError("n, k exceed the shape of x")
-    _rows_fit("x", x, n, k, ldx)
+    n, k, ldx = _x_operand(x, n, k, ldx)
     _flat(xq=xq, da=da, das=das)
     _check(_lib.q4k_quantize_act(_ptr(x), n, k, ldx, _ptr(xq), _nbytes(xq), _ptr(da),
                                  _nbytes(da), _ptr(das), _nbytes(das), _stream(stream)),
