@@ -16,8 +16,8 @@ Timing protocol (all with HIP events recorded on the stream the kernels run on):
     one block of --block back-to-back launches per layout (the starting layout rotates from round
     to round), events only around each block;  per-launch time = block time / block;
   * `value` = the headline layout's GEMM effective int8 TOPS, 2*N*M*K / its mean per-launch time
-    (a launch is the GEMM kernel plus the small kernel that zeroes split tiles, when there are
-    any); the per-layout figures (mean, p10/p50/p90 over rounds, TOPS, fraction of the int8 peak)
+    (a launch is the GEMM kernel plus the small kernel that adds up the split tiles' workspace
+    slabs, when there are any); the per-layout figures (mean, p10/p50/p90 over rounds, TOPS, fraction of the int8 peak)
     are in `layouts`;
   * the prepass time comes from a third pass of K steps with events between the two kernels.
 
@@ -406,16 +406,22 @@ class Gemm:
         if layout == "q4k":
             self.w = torch.empty(q6k.q4k_weight_bytes(m, k), dtype=torch.uint8, device=dev)
             q6k.q4k_expand_weights(raw_d, m, k, self.w)
+            ws = q6k.q4k_gemm_workspace(n, m, k)
         else:
             self.w = torch.empty(q6k.q6k_weight_bytes(m, k, layout), dtype=torch.uint8, device=dev)
             q6k.q6k_expand_weights(raw_d, m, k, layout, self.w)
+            ws = q6k.q6k_gemm_workspace(n, m, k, layout)
+        # the split-k slabs, allocated once (the timed steps allocate nothing)
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
 
     def launch(self):
         a = self.acts
         if self.layout == "q4k":
-            self.q6k.q4k_gemm(a.xq, a.da, a.das, self.n, self.w, self.m, self.k, self.y)
+            self.q6k.q4k_gemm(a.xq, a.da, a.das, self.n, self.w, self.m, self.k, self.y,
+                              workspace=self.ws)
         else:
-            self.q6k.q6k_gemm(a.xq, a.da, self.n, self.w, self.layout, self.m, self.k, self.y)
+            self.q6k.q6k_gemm(a.xq, a.da, self.n, self.w, self.layout, self.m, self.k, self.y,
+                              workspace=self.ws)
 
     def ops(self):
         return 2.0 * self.n * self.m * self.k

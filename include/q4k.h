@@ -68,12 +68,19 @@ q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, f
 /* The GEMM: y[t][j] = sum over chunks c of da*(d*sc)*D - (dmin*m)*das, D the exact int32 dot of
  * the int8 activations with the 4-bit codes over the chunk.  y f32 [n][ldy], ldy >= m, 4-byte
  * aligned, y_bytes >= 4*((n-1)*ldy + m); xq, da, das, w 16-byte aligned and at least the sizes
- * above (Q6K_ESIZE otherwise); k < 2^26.  The work split is q6k_gemm's: output tiles of a
- * partial last round of workgroups are split along k, zeroed in y and added into with float
- * atomics, so the last bits of those outputs may vary from run to run. */
+ * above (Q6K_ESIZE otherwise); k < 2^26.  The work split, the workspace and its rules are
+ * q6k_gemm's (output tiles of a partial last round are split along k, their pieces stored into
+ * workspace slabs and added in piece order by a second kernel on the same stream), so y is the
+ * same bit for bit from run to run. */
 q6k_status q4k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
                     const float* das, size_t das_bytes, int64_t n, const void* w, size_t w_bytes,
-                    int64_t m, int64_t k, float* y, size_t y_bytes, int64_t ldy, void* stream);
+                    int64_t m, int64_t k, float* y, size_t y_bytes, int64_t ldy, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that q4k_gemm needs for this n, m, k on the current device (3 workgroup slots
+ * per compute unit: at most 24 MiB on a 256-CU device); 0 when no tile is split or the problem
+ * is empty.  Errors as q6k_gemm_workspace. */
+q6k_status q4k_gemm_workspace(int64_t n, int64_t m, int64_t k, size_t* bytes);
 
 /* Test-only export of the same kernel source, with the grid and work split of q4k_gemm: the int32
  * chunk dots D of tokens [tok0, tok0 + ntok) x rows [row0, row0 + nrow) to dots

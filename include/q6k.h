@@ -139,21 +139,36 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
  * super-block; the result differs from layouts 0/1 only in f32 rounding.
  * Work split (every layout): output tiles of 64 tokens x 128 rows are dealt out in rounds of one
  * per workgroup slot of the GPU; when the last round would leave slots idle, its tiles are split
- * along k into pieces of whole super-blocks.  The call then first zeroes those tiles in y and the
- * pieces add their partial sums with float atomics in no fixed order, so the last bits of those
- * outputs may vary from run to run (within the rounding of one f32 addition per piece); tiles
- * computed whole are bit-for-bit repeatable.  Two calls that write the same y concurrently on
- * different streams race.
+ * along k into pieces of whole super-blocks.  Each piece stores its partial sums into a 32 KiB
+ * slab of the workspace, and a second kernel, enqueued right after the GEMM on the same stream,
+ * adds each split tile's slabs in piece order into y.  The order of every addition is fixed, so
+ * y is the same bit for bit from run to run (and in a captured graph's replays).  The workspace
+ * is scratch: its contents are not needed before the call and mean nothing after it; two calls
+ * in flight at once (on different streams) need workspaces of their own, and two that write the
+ * same y concurrently race.
  *   xq, da  : outputs of q6k_quantize_act for the same n, k; xq_bytes, da_bytes at least what
  *             q6k_act_bytes returns (the kernels read whole padded tiles)
  *   w       : output of q6k_expand_weights for the same m, k and `layout`; w_bytes at least
  *             q6k_weight_bytes(m, k, layout)
  *   y       : f32 [n][ldy] row-major, ldy >= m, 4-byte aligned, y_bytes >= 4*((n-1)*ldy + m);
  *             only y[0..n)[0..m) is written
+ *   workspace, workspace_bytes : device memory owned by the caller, 16-byte aligned, at least
+ *             the bytes q6k_gemm_workspace returns for this n, m, k, layout on the current
+ *             device (NULL and 0 when that is 0); Q6K_EINVAL if NULL when needed, Q6K_EALIGN if
+ *             misaligned, Q6K_ESIZE if too small
  * Layout 2 also needs k < 2^25, layouts 0 and 1 k < 2^26 (Q6K_ESIZE otherwise). */
 q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
                     int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
-                    float* y, size_t y_bytes, int64_t ldy, void* stream);
+                    float* y, size_t y_bytes, int64_t ldy, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that q6k_gemm needs for this n, m, k and layout on the device current on the
+ * calling thread (the work split depends on its compute-unit count): 32 KiB per piece of a
+ * split tile, at most 32 KiB x the workgroup slots of the device (2 per compute unit on layout
+ * 2, 3 on layouts 0 and 1: 16 and 24 MiB on a 256-CU device); 0 when no tile is split or the
+ * problem is empty.  Shape errors as q6k_gemm; Q6K_EHIP if the device cannot be queried;
+ * *bytes is 0 on any error. */
+q6k_status q6k_gemm_workspace(int64_t n, int64_t m, int64_t k, int layout, size_t* bytes);
 
 /* Test-only export of the same kernel source, launched with the same grid and work split as
  * q6k_gemm for this n, m, k and layout: instead of y, stores the int32 sub-block dots D[t][j][s]

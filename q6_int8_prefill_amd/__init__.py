@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     q4k_expand_weights,
     q4k_gemm,
     q4k_gemm_dots,
+    q4k_gemm_workspace,
     q4k_launches,
     q4k_quantize_act,
     q4k_weight_bytes,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     q6k_gemm,
     q6k_gemm_chunkdots,
     q6k_gemm_subdots,
+    q6k_gemm_workspace,
     q6k_quantize_act,
     q6k_stats,
     q6k_strerror,

@@ -29,7 +29,10 @@ _lib.q6k_weight_bytes.argtypes = [_i64, _i64, _int]
 _lib.q6k_expand_weights.restype = _int
 _lib.q6k_expand_weights.argtypes = [_p, _i64, _i64, _int, _p, _sz, _p]
 _lib.q6k_gemm.restype = _int
-_lib.q6k_gemm.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64, _p]
+_lib.q6k_gemm.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64, _p,
+                          _sz, _p]
+_lib.q6k_gemm_workspace.restype = _int
+_lib.q6k_gemm_workspace.argtypes = [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]
 _WIN = [_i64, _i64, _i64, _i64]
 _lib.q6k_gemm_subdots.restype = _int
 _lib.q6k_gemm_subdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + _WIN + \
@@ -47,7 +50,9 @@ _lib.q4k_act_sums.restype = _int
 _lib.q4k_act_sums.argtypes = [_p, _p, _i64, _i64, _p, _sz, _p]
 _lib.q4k_gemm.restype = _int
 _lib.q4k_gemm.argtypes = [_p, _sz, _p, _sz, _p, _sz, _i64, _p, _sz, _i64, _i64, _p, _sz, _i64,
-                          _p]
+                          _p, _sz, _p]
+_lib.q4k_gemm_workspace.restype = _int
+_lib.q4k_gemm_workspace.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
 _lib.q4k_gemm_dots.restype = _int
 _lib.q4k_gemm_dots.argtypes = [_p, _sz, _i64, _p, _sz, _i64, _i64] + _WIN + [_p, _sz, _p]
 _lib.q4k_launches.restype = ctypes.c_uint64
@@ -59,9 +64,10 @@ _lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
 
 EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_swiglu_quantize_act", "q6k_swiglu_f32",
            "q6k_weight_bytes", "q6k_expand_weights",
-           "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots", "q6k_strerror", "q6k_stats",
-           "q4k_weight_bytes", "q4k_expand_weights", "q4k_quantize_act", "q4k_act_sums", "q4k_gemm", "q4k_gemm_dots",
-           "q4k_launches")
+           "q6k_gemm_workspace", "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots",
+           "q6k_strerror", "q6k_stats",
+           "q4k_weight_bytes", "q4k_expand_weights", "q4k_quantize_act", "q4k_act_sums",
+           "q4k_gemm_workspace", "q4k_gemm", "q4k_gemm_dots", "q4k_launches")
 
 
 class Q6KError(RuntimeError):
@@ -219,12 +225,35 @@ def _y_operand(y, n, m, ldy):
     return ldy
 
 
-def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None):
-    """y f32 [n][ldy] = GEMM of prepared activations and weights."""
+def q6k_gemm_workspace(n, m, k, layout):
+    """-> workspace bytes q6k_gemm needs for this problem on the current device (0: none)."""
+    out = _sz(0)
+    _check(_lib.q6k_gemm_workspace(int(n), int(m), int(k), int(layout), ctypes.byref(out)),
+           "q6k_gemm_workspace")
+    return int(out.value)
+
+
+def _workspace(workspace, need, like):
+    """The caller's workspace (a flat device buffer), or a fresh one of `need` bytes on the device
+    of `like` (from torch's caching allocator) when none is given."""
+    if workspace is None:
+        if need == 0:
+            return None
+        return torch.empty(need, dtype=torch.uint8, device=like.device)
+    _flat(workspace=workspace)
+    return workspace
+
+
+def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None, workspace=None):
+    """y f32 [n][ldy] = GEMM of prepared activations and weights.  `workspace`: a device buffer of
+    at least q6k_gemm_workspace(n, m, k, layout) bytes, allocated here when not given."""
     ldy = _y_operand(y, n, m, ldy)
     _flat(xq=xq, da=da, w=w)
+    need = q6k_gemm_workspace(n, m, k, layout) if workspace is None and y is not None else 0
+    ws = _workspace(workspace, need, y)
     _check(_lib.q6k_gemm(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), n, _ptr(w), _nbytes(w),
-                         layout, m, k, _ptr(y), _span(y), ldy, _stream(stream)), "q6k_gemm")
+                         layout, m, k, _ptr(y), _span(y), ldy, _ptr(ws), _nbytes(ws),
+                         _stream(stream)), "q6k_gemm")
 
 
 def _window(n, m, tok0, ntok, row0, nrow):
@@ -300,13 +329,24 @@ def q4k_act_sums(xq, da, n, k, das, stream=None):
            "q4k_act_sums")
 
 
-def q4k_gemm(xq, da, das, n, w, m, k, y, ldy=None, stream=None):
-    """y f32 [n][ldy] = q4_K GEMM of prepared activations (xq, da, das) and weights."""
+def q4k_gemm_workspace(n, m, k):
+    """-> workspace bytes q4k_gemm needs for this problem on the current device (0: none)."""
+    out = _sz(0)
+    _check(_lib.q4k_gemm_workspace(int(n), int(m), int(k), ctypes.byref(out)),
+           "q4k_gemm_workspace")
+    return int(out.value)
+
+
+def q4k_gemm(xq, da, das, n, w, m, k, y, ldy=None, stream=None, workspace=None):
+    """y f32 [n][ldy] = q4_K GEMM of prepared activations (xq, da, das) and weights; `workspace`
+    as for q6k_gemm (q4k_gemm_workspace bytes)."""
     ldy = _y_operand(y, n, m, ldy)
     _flat(xq=xq, da=da, das=das, w=w)
+    need = q4k_gemm_workspace(n, m, k) if workspace is None and y is not None else 0
+    ws = _workspace(workspace, need, y)
     _check(_lib.q4k_gemm(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), _ptr(das), _nbytes(das), n,
-                         _ptr(w), _nbytes(w), m, k, _ptr(y), _span(y), ldy, _stream(stream)),
-           "q4k_gemm")
+                         _ptr(w), _nbytes(w), m, k, _ptr(y), _span(y), ldy, _ptr(ws), _nbytes(ws),
+                         _stream(stream)), "q4k_gemm")
 
 
 def q4k_gemm_dots(xq, n, w, m, k, dots, tok0=0, ntok=None, row0=0, nrow=None, stream=None):

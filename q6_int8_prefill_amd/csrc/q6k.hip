@@ -356,10 +356,12 @@ __device__ __forceinline__ uint32_t fourth4x4(uint32_t x, uint32_t y, uint32_t z
 // Work split shared by the GEMM kernels.  Every GEMM workgroup computes one 64-token x 128-row
 // output tile (gx x gy tiles).  The tiles are dealt out in rounds of one per workgroup slot of
 // the GPU (workgroups per CU x CUs); when the last round would leave slots idle, its tiles are
-// split along k into `pieces` pieces of whole super-blocks that run side by side and add their
-// partial sums into y, which split_zero_kernel zeroes first (float atomics: the order in which
-// the pieces add, and so the last bits of those outputs, may differ from run to run).
-// Workgroups 0 .. n_full-1 take whole tiles, the rest take pieces.
+// split along k into `pieces` pieces of whole super-blocks that run side by side.  Workgroups
+// 0 .. n_full-1 take whole tiles and store them into y; workgroup n_full + i takes piece
+// i % pieces of split tile i / pieces and stores its partial sums into slab i of the caller's
+// workspace (one 64 x 128 f32 tile per piece), and split_reduce_kernel, launched next on the same
+// stream, adds each tile's slabs in piece order into y.  The sum's order is fixed, so every output
+// is the same bit for bit from run to run.
 // ---------------------------------------------------------------------------------------------
 // XCD-aware tile order: workgroup t of the dispatch order runs on XCD t % 8, and each XCD has its
 // own L2; when the grid splits evenly, XCD j takes one (gx/4) x (gy/2) rectangle of the output
@@ -382,8 +384,36 @@ __device__ __forceinline__ void tile_of(uint32_t t, uint32_t gx, uint32_t gy, ui
 struct TileWork {
   uint32_t bx, by;  // token-tile pair and row-tile quad of the output tile
   int64_t s0, s1;   // super-blocks [s0, s1) of k
-  bool split;       // a piece of a split tile: add into y atomically
+  bool split;       // a piece of a split tile: store into workspace slab `slab`
+  uint32_t slab;    // pid - n_full for a piece
 };
+
+constexpr int kSlabTok = 64;                     // tokens of an output tile (every GEMM)
+constexpr int64_t kSlabFloats = kSlabTok * 128;  // one output tile, f32 [64][128]
+
+// Where a workgroup's output tile goes: y itself, or the piece's workspace slab, addressed with
+// the tile's own (token, row) offsets, so that the store of output (tok, row) is
+// p[(tok - tok0) * ld + (row - row0)].
+struct OutDst {
+  float* p;
+  int64_t ld, tok0, row0;
+};
+
+__device__ __forceinline__ OutDst out_dst(const TileWork& tw, float* y, int64_t ldy, float* ws) {
+  OutDst o;
+  if (tw.split) {
+    o.p = ws + (int64_t)tw.slab * kSlabFloats;
+    o.ld = 128;
+    o.tok0 = (int64_t)tw.bx * kSlabTok;
+    o.row0 = (int64_t)tw.by * 128;
+  } else {
+    o.p = y;
+    o.ld = ldy;
+    o.tok0 = 0;
+    o.row0 = 0;
+  }
+  return o;
+}
 
 // Where the test exports store their integer dots: tokens [tok0, tok0 + ntok) x rows
 // [row0, row0 + nrow) of the full problem, as int32 [ntok][nrow][per], per = dots per row and
@@ -451,18 +481,23 @@ __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_
   w.s0 = __builtin_amdgcn_readfirstlane((int)w.s0);
   w.s1 = __builtin_amdgcn_readfirstlane((int)w.s1);
   w.split = __builtin_amdgcn_readfirstlane((int)w.split) != 0;
+  w.slab = __builtin_amdgcn_readfirstlane(w.split ? pid - n_full : 0u);
   return w;
 }
 
-// Zero y over the tiles that a GEMM splits along k (tiles n_full .. gx*gy-1 of the GEMM's tile
-// order, XCD-aware or plain).  Each tile of tile_tok tokens x 128 rows is spread over
-// tile_tok / 8 workgroups of 8 tokens, one row per thread and token (512-byte wave stores).
-constexpr int kZeroTok = 8;  // tokens per zeroing workgroup
-__global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, int64_t ldy,
-                                                      int64_t n, int64_t m, uint32_t gx,
-                                                      uint32_t gy, uint32_t n_full,
-                                                      uint32_t tile_tok, int xcd_order) {
-  const uint32_t parts = tile_tok / kZeroTok;
+// y over the tiles that a GEMM split along k (tiles n_full .. gx*gy-1 of the GEMM's tile order,
+// XCD-aware or plain): the sum of the tile's `pieces` workspace slabs, added in piece order.  A
+// workgroup covers kReduceTok tokens of a tile, a thread 4 consecutive rows of one token; its
+// pieces are loaded four at a time (the loads in flight together) and added one after another,
+// so the order of the additions is fixed.  vec: y is 16-byte aligned and ldy % 4 == 0.
+constexpr int kReduceTok = 8;  // tokens per reducing workgroup (256 threads x 4 rows)
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws,
+                                                           float* __restrict__ y, int64_t ldy,
+                                                           int64_t n, int64_t m, uint32_t gx,
+                                                           uint32_t gy, uint32_t n_full,
+                                                           uint32_t pieces, int xcd_order,
+                                                           int vec) {
+  constexpr uint32_t parts = kSlabTok / kReduceTok;
   const uint32_t t = n_full + blockIdx.x / parts, part = blockIdx.x % parts;
   uint32_t bx, by;
   if (xcd_order) {
@@ -471,12 +506,37 @@ __global__ __launch_bounds__(256) void split_zero_kernel(float* __restrict__ y, 
     bx = t % gx;
     by = t / gx;
   }
-  const int64_t r = (int64_t)by * 128 + (threadIdx.x & 127);
-  if (r >= m) return;
-#pragma unroll
-  for (uint32_t i = threadIdx.x >> 7; i < kZeroTok; i += 2) {
-    const int64_t tok = (int64_t)bx * tile_tok + part * kZeroTok + i;
-    if (tok < n) y[tok * ldy + r] = 0.0f;
+  const int tl = part * kReduceTok + (threadIdx.x >> 5), rl = 4 * (threadIdx.x & 31);
+  const int64_t tok = (int64_t)bx * kSlabTok + tl, r = (int64_t)by * 128 + rl;
+  if (tok >= n || r >= m) return;
+  const float4* src = reinterpret_cast<const float4*>(
+      ws + (int64_t)(t - n_full) * pieces * kSlabFloats + tl * 128 + rl);
+  constexpr int64_t kStride = kSlabFloats / 4;  // float4s from one piece's slab to the next
+  float4 v = src[0];
+  uint32_t pc = 1;
+  for (; pc + 4 <= pieces; pc += 4) {
+    const float4 a = src[pc * kStride], b = src[(pc + 1) * kStride], c = src[(pc + 2) * kStride],
+                 d = src[(pc + 3) * kStride];
+    v.x = v.x + a.x + b.x + c.x + d.x;
+    v.y = v.y + a.y + b.y + c.y + d.y;
+    v.z = v.z + a.z + b.z + c.z + d.z;
+    v.w = v.w + a.w + b.w + c.w + d.w;
+  }
+  for (; pc < pieces; ++pc) {
+    const float4 a = src[pc * kStride];
+    v.x += a.x;
+    v.y += a.y;
+    v.z += a.z;
+    v.w += a.w;
+  }
+  float* dst = y + tok * ldy + r;
+  if (vec && r + 3 < m) {
+    *reinterpret_cast<float4*>(dst) = v;
+  } else {
+    dst[0] = v.x;
+    if (r + 1 < m) dst[1] = v.y;
+    if (r + 2 < m) dst[2] = v.z;
+    if (r + 3 < m) dst[3] = v.w;
   }
 }
 
@@ -806,8 +866,8 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
                                                       const uint8_t* __restrict__ wscales,
                                                       int64_t n, int64_t m, int64_t nchunk,
                                                       float* __restrict__ y, int64_t ldy,
-                                                      DotsOut dots, uint32_t gx,
-                                                      uint32_t gy, uint32_t n_full,
+                                                      float* __restrict__ ws, DotsOut dots,
+                                                      uint32_t gx, uint32_t gy, uint32_t n_full,
                                                       uint32_t pieces) {
   constexpr int kSlot = SlotSize<LAYOUT>::value;
   constexpr int kRing = RingSize<LAYOUT>::value;
@@ -880,6 +940,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   // layout 0's accumulators hold 4 y (its B fragments are 4 x the centered codes)
   const float out_scale = kPacked ? 0.25f : 1.0f;
   const int64_t T = k.T;
+  const OutDst o = out_dst(tw, y, ldy, ws);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int64_t mcol = (k.R0 + 2 * k.rp + u) * kTile + p;
@@ -887,14 +948,9 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < n) {
-        // a lane's 16 values are one row of 16 tokens; an instruction covers 32 consecutive
-        // rows of 2 tokens
-        if (tw.split)
-          unsafeAtomicAdd(y + tok * ldy + mcol, acc[u][r] * out_scale);
-        else
-          y[tok * ldy + mcol] = acc[u][r] * out_scale;
-      }
+      // a lane's 16 values are one row of 16 tokens; an instruction covers 32 consecutive rows
+      // of 2 tokens
+      if (tok < n) o.p[(tok - o.tok0) * o.ld + (mcol - o.row0)] = acc[u][r] * out_scale;
     }
   }
 }
@@ -1148,7 +1204,7 @@ template <bool DOTS>
 __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wd, int64_t n, int64_t m,
-    int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store,
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store, float* __restrict__ ws,
     DotsOut dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot];
   const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
@@ -1252,7 +1308,9 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
                       st.acc[u][4 * q + 3]);
   __syncthreads();
   const int64_t tok_base = T0 * kTile, row_base = (int64_t)by * kWgRow;
-  if (!split && vec_store) {
+  // a piece's slab is 16-byte aligned with rows of 128 floats: always the vector path
+  const OutDst o = out_dst(tw, y, ldy, ws);
+  if (split || vec_store) {
     // two tokens per instruction, 4 rows per lane: 2 x 512 contiguous bytes
     const int half = k.lane >> 5, r4 = 4 * (k.lane & 31);
 #pragma unroll
@@ -1261,7 +1319,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
       const int64_t tok = tok_base + t, row = row_base + r4;
       if (tok >= n || row >= m) continue;
       const float4 v = *reinterpret_cast<const float4*>(out + t * kOutLd + r4);
-      float* dst = y + tok * ldy + row;
+      float* dst = o.p + (tok - o.tok0) * o.ld + (row - o.row0);
       if (row + 3 < m) {
         *reinterpret_cast<float4*>(dst) = v;
       } else {
@@ -1281,11 +1339,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
       for (int h = 0; h < 2; ++h) {
         const int64_t row = row_base + 64 * h + k.lane;
         if (row >= m) continue;
-        const float v = out[t * kOutLd + 64 * h + k.lane];
-        if (split)
-          unsafeAtomicAdd(y + tok * ldy + row, v);
-        else
-          y[tok * ldy + row] = v;
+        y[tok * ldy + row] = out[t * kOutLd + 64 * h + k.lane];
       }
     }
   }
@@ -1548,8 +1602,8 @@ template <bool DOTS>
 __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ da, const float* __restrict__ das,
     const uint8_t* __restrict__ wcodes, const float* __restrict__ wsb, int64_t n, int64_t m,
-    int64_t nchunk, float* __restrict__ y, int64_t ldy, DotsOut dots, uint32_t gx,
-    uint32_t gy, uint32_t n_full, uint32_t pieces) {
+    int64_t nchunk, float* __restrict__ y, int64_t ldy, float* __restrict__ ws, DotsOut dots,
+    uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQ4Ring * kQ4Slot + 2 * kQ4SbBytes];
   Q4Ctx k;
   k.smem = smem;
@@ -1612,6 +1666,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
 
   if (DOTS) return;
+  const OutDst o = out_dst(tw, y, ldy, ws);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int64_t mcol = k.col + u * kTile;
@@ -1619,12 +1674,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t tok = T * kTile + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (tok < n) {
-        if (tw.split)
-          unsafeAtomicAdd(y + tok * ldy + mcol, acc[u][r]);
-        else
-          y[tok * ldy + mcol] = acc[u][r];
-      }
+      if (tok < n) o.p[(tok - o.tok0) * o.ld + (mcol - o.row0)] = acc[u][r];
     }
   }
 }
@@ -1699,19 +1749,35 @@ q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitP
   return sp->nblocks > INT32_MAX ? Q6K_ESIZE : Q6K_OK;
 }
 
-// Zero y over the tiles that the plan splits (none if nothing is split), in the same tile order
-// and tile height (tokens) as the GEMM that follows.
-static_assert((kTile * kFTok) % kZeroTok == 0 && (kTile * kWgTokTiles) % kZeroTok == 0,
-              "zeroing workgroups cover whole tiles");
-void zero_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, int64_t tile_tok,
-                      bool xcd_order, float* y, int64_t ldy, int64_t n, int64_t m,
-                      hipStream_t s) {
+static_assert(kTile * kFTok == kSlabTok && kTile * kWgTokTiles == kSlabTok,
+              "every GEMM's output tile is one workspace slab");
+static_assert(kSlabTok % kReduceTok == 0 && kReduceTok * 128 == 256 * 4,
+              "reducing workgroups cover whole tiles, 4 rows per thread");
+
+// Workspace bytes of a plan: one slab per piece of a split tile.
+inline size_t plan_workspace_bytes(const SplitPlan& sp) {
+  return (size_t)(sp.nblocks - sp.n_full) * (size_t)kSlabFloats * sizeof(float);
+}
+
+// The workspace of a launch that needs `need` bytes: 16-byte aligned, at least that large.
+q6k_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return Q6K_OK;
+  if (!ws) return Q6K_EINVAL;
+  if (((uintptr_t)ws & 15) != 0) return Q6K_EALIGN;
+  return ws_bytes < need ? Q6K_ESIZE : Q6K_OK;
+}
+
+// After the GEMM on the same stream: y over the split tiles from their slabs (nothing if the plan
+// splits none).
+void reduce_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, bool xcd_order,
+                        const float* ws, float* y, int64_t ldy, int64_t n, int64_t m,
+                        hipStream_t s) {
   const int64_t nsplit = gx * gy - sp.n_full;
   if (nsplit > 0)
-    hipLaunchKernelGGL(split_zero_kernel, dim3((unsigned)(nsplit * (tile_tok / kZeroTok))),
-                       dim3(256), 0, s, y, ldy, n, m,
-                       (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full, (uint32_t)tile_tok,
-                       xcd_order ? 1 : 0);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(nsplit * (kSlabTok / kReduceTok))),
+                       dim3(256), 0, s, ws, y, ldy, n, m, (uint32_t)gx, (uint32_t)gy,
+                       (uint32_t)sp.n_full, (uint32_t)sp.pieces, xcd_order ? 1 : 0,
+                       aligned16(y) && ldy % 4 == 0 ? 1 : 0);
 }
 
 q6k_status launch_status() {
@@ -1745,15 +1811,10 @@ q6k_status check_window(const DotsOut& w, size_t dots_bytes, int64_t n, int64_t 
   return Q6K_OK;
 }
 
-template <int OUT>
-q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
-                       int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
-                       float* y, size_t y_bytes, int64_t ldy, DotsOut dots, size_t dots_bytes,
-                       void* stream) {
+// The shape rules of a q6_K GEMM (any output).
+q6k_status gemm_shape(int64_t n, int64_t m, int64_t k, int layout) {
   if (n < 0 || m < 0) return Q6K_EINVAL;
   if (!valid_layout(layout)) return Q6K_EINVAL;
-  if (OUT == kOutSubdots && layout == Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
-  if (OUT == kOutChunkdots && layout != Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
   if (k <= 0 || k % 256) return Q6K_ESHAPE;
   if (n > kMaxDim || m > kMaxDim || k > kMaxDim) return Q6K_ESIZE;
   // layout 2 addresses a row tile's digit planes (k/32 * 2048 bytes) through one 32-bit buffer
@@ -1761,6 +1822,29 @@ q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t 
   if (layout == Q6K_LAYOUT_FOLDED && k / 32 * 2048 > INT32_MAX) return Q6K_ESIZE;
   // layouts 0 and 1 address a tile's activations or codes (k/32 * 1024 bytes) likewise
   if (layout != Q6K_LAYOUT_FOLDED && k / 32 * 1024 > INT32_MAX) return Q6K_ESIZE;
+  return Q6K_OK;
+}
+
+// Output tiles (gx x gy of kSlabTok tokens x 128 rows) and work split of a non-empty q6_K GEMM
+// on the current device.
+q6k_status gemm_plan(int64_t n, int64_t m, int64_t k, int layout, int64_t* gx, int64_t* gy,
+                     SplitPlan* sp) {
+  *gx = round_up(n, kWgTok) / kSlabTok;
+  *gy = round_up(m, kWgRow) / kWgRow;
+  if (*gy > INT32_MAX || *gx > INT32_MAX) return Q6K_ESIZE;
+  const int wg_per_cu = layout == Q6K_LAYOUT_FOLDED ? kFoldedWgPerCu : Q6K_WG_PER_CU;
+  return plan_split(*gx, *gy, wg_per_cu, k / 256, sp);
+}
+
+template <int OUT>
+q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                       int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
+                       float* y, size_t y_bytes, int64_t ldy, void* wsp, size_t ws_bytes,
+                       DotsOut dots, size_t dots_bytes, void* stream) {
+  const q6k_status shape = gemm_shape(n, m, k, layout);
+  if (shape != Q6K_OK) return shape;
+  if (OUT == kOutSubdots && layout == Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
+  if (OUT == kOutChunkdots && layout != Q6K_LAYOUT_FOLDED) return Q6K_EINVAL;
   if (n == 0 || m == 0) return Q6K_OK;
   if (!xq || !da || !w) return Q6K_EINVAL;
   if (!aligned16(xq) || !aligned16(da) || !aligned16(w)) return Q6K_EALIGN;
@@ -1777,39 +1861,41 @@ q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t 
     const q6k_status ys = check_y(y, y_bytes, n, m, ldy);
     if (ys != Q6K_OK) return ys;
   }
-  const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
-  // output tiles of tile_tok tokens x 128 rows
-  const int64_t tile_tok = layout == Q6K_LAYOUT_FOLDED ? kTile * kFTok : kTile * kWgTokTiles;
-  const int64_t gx = np / tile_tok, gy = mp / kWgRow;
-  if (gy > INT32_MAX || gx > INT32_MAX) return Q6K_ESIZE;
+  int64_t gx, gy;
+  SplitPlan sp;
+  const q6k_status plan = gemm_plan(n, m, k, layout, &gx, &gy, &sp);
+  if (plan != Q6K_OK) return plan;
+  // the test exports store no y and so no slabs
+  float* slabs = nullptr;
+  if (OUT == kOutY) {
+    const q6k_status wst = check_workspace(wsp, ws_bytes, plan_workspace_bytes(sp));
+    if (wst != Q6K_OK) return wst;
+    slabs = static_cast<float*>(wsp);
+  }
   const int64_t nchunk = k / 32;
   const uint8_t* wc = static_cast<const uint8_t*>(w);
-  const uint8_t* ws = wc + codes_bytes;
+  const uint8_t* wsc = wc + codes_bytes;
   const uint8_t* a = static_cast<const uint8_t*>(xq);
   hipStream_t s = static_cast<hipStream_t>(stream);
   constexpr bool kDots = OUT != kOutY;
-  SplitPlan sp;
-  const int wg_per_cu = layout == Q6K_LAYOUT_FOLDED ? kFoldedWgPerCu : Q6K_WG_PER_CU;
-  const q6k_status plan = plan_split(gx, gy, wg_per_cu, k / 256, &sp);
-  if (plan != Q6K_OK) return plan;
-  if (OUT == kOutY)
-    zero_split_tiles(sp, gx, gy, tile_tok, layout == Q6K_LAYOUT_FOLDED || Q6K_GEMM01_XCD_ORDER, y,
-                     ldy, n, m, s);
   const dim3 grid((unsigned)sp.nblocks),
       block(layout == Q6K_LAYOUT_FOLDED ? 64 * kFWaves : 256);
   const uint32_t gx32 = (uint32_t)gx, gy32 = (uint32_t)gy, nf = (uint32_t)sp.n_full,
                  pc = (uint32_t)sp.pieces;
   if (layout == Q6K_LAYOUT_FOLDED) {
     const int vec_store = OUT == kOutY && aligned16(y) && ldy % 4 == 0;
-    hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, ws, n, m, nchunk, y,
-                       ldy, vec_store, dots, gx32, gy32, nf, pc);
+    hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, wsc, n, m, nchunk,
+                       y, ldy, vec_store, slabs, dots, gx32, gy32, nf, pc);
   } else if (layout == Q6K_LAYOUT_EXPANDED) {
     hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_EXPANDED, kDots>), grid, block, 0, s, a, da, wc,
-                       ws, n, m, nchunk, y, ldy, dots, gx32, gy32, nf, pc);
+                       wsc, n, m, nchunk, y, ldy, slabs, dots, gx32, gy32, nf, pc);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_PACKED, kDots>), grid, block, 0, s, a, da, wc, ws,
-                       n, m, nchunk, y, ldy, dots, gx32, gy32, nf, pc);
+    hipLaunchKernelGGL((gemm_kernel<Q6K_LAYOUT_PACKED, kDots>), grid, block, 0, s, a, da, wc,
+                       wsc, n, m, nchunk, y, ldy, slabs, dots, gx32, gy32, nf, pc);
   }
+  if (OUT == kOutY)
+    reduce_split_tiles(sp, gx, gy, layout == Q6K_LAYOUT_FOLDED || Q6K_GEMM01_XCD_ORDER, slabs, y,
+                       ldy, n, m, s);
   const q6k_status st = launch_status();
   if (st == Q6K_OK) g_launches[layout].fetch_add(1, std::memory_order_relaxed);
   return st;
@@ -1842,15 +1928,32 @@ q6k_status quantize_common(const float* x, const float* up, int64_t n, int64_t k
   return launch_status();
 }
 
-template <bool DOTS>
-q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
-                           const float* das, size_t das_bytes, int64_t n, const void* w,
-                           size_t w_bytes, int64_t m, int64_t k, float* y, size_t y_bytes,
-                           int64_t ldy, DotsOut dots, size_t dots_bytes, void* stream) {
+// The shape rules of a q4_K GEMM (any output).
+q6k_status q4k_gemm_shape(int64_t n, int64_t m, int64_t k) {
   if (n < 0 || m < 0) return Q6K_EINVAL;
   if (k <= 0 || k % 256) return Q6K_ESHAPE;
   if (n > kMaxDim || m > kMaxDim || k > kMaxDim) return Q6K_ESIZE;
   if (k / 32 * 1024 > INT32_MAX) return Q6K_ESIZE;  // one 32-bit buffer range per tile
+  return Q6K_OK;
+}
+
+// Output tiles and work split of a non-empty q4_K GEMM on the current device.
+q6k_status q4k_gemm_plan(int64_t n, int64_t m, int64_t k, int64_t* gx, int64_t* gy,
+                         SplitPlan* sp) {
+  *gx = round_up(n, kWgTok) / kSlabTok;
+  *gy = round_up(m, kWgRow) / kWgRow;
+  if (*gy > 65535 || *gx > INT32_MAX) return Q6K_ESIZE;
+  return plan_split(*gx, *gy, Q4K_WG_PER_CU, k / 256, sp);
+}
+
+template <bool DOTS>
+q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                           const float* das, size_t das_bytes, int64_t n, const void* w,
+                           size_t w_bytes, int64_t m, int64_t k, float* y, size_t y_bytes,
+                           int64_t ldy, void* wsp, size_t ws_bytes, DotsOut dots,
+                           size_t dots_bytes, void* stream) {
+  const q6k_status shape = q4k_gemm_shape(n, m, k);
+  if (shape != Q6K_OK) return shape;
   if (n == 0 || m == 0) return Q6K_OK;
   if (!xq || !w || (!DOTS && (!da || !das))) return Q6K_EINVAL;
   if (!aligned16(xq) || !aligned16(w) || (!DOTS && (!aligned16(da) || !aligned16(das))))
@@ -1869,9 +1972,17 @@ q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, siz
     const q6k_status ys = check_y(y, y_bytes, n, m, ldy);
     if (ys != Q6K_OK) return ys;
   }
-  const int64_t np = round_up(n, kWgTok), mp = round_up(m, kWgRow);
-  const int64_t gx = np / (kTile * 2), gy = mp / kWgRow;
-  if (gy > 65535 || gx > INT32_MAX) return Q6K_ESIZE;
+  int64_t gx, gy;
+  SplitPlan sp;
+  const q6k_status plan = q4k_gemm_plan(n, m, k, &gx, &gy, &sp);
+  if (plan != Q6K_OK) return plan;
+  float* slabs = nullptr;
+  if (!DOTS) {
+    const q6k_status wst = check_workspace(wsp, ws_bytes, plan_workspace_bytes(sp));
+    if (wst != Q6K_OK) return wst;
+    slabs = static_cast<float*>(wsp);
+  }
+  const int64_t mp = round_up(m, kWgRow);
   const int64_t nchunk = k / 32;
   const uint8_t* wc = static_cast<const uint8_t*>(w);
   const float* ws = reinterpret_cast<const float*>(wc + (size_t)mp * (size_t)k);
@@ -1879,14 +1990,11 @@ q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, siz
   const float* dap = DOTS ? reinterpret_cast<const float*>(xq) : da;
   const float* dasp = DOTS ? reinterpret_cast<const float*>(xq) : das;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SplitPlan sp;
-  const q6k_status plan = plan_split(gx, gy, Q4K_WG_PER_CU, k / 256, &sp);
-  if (plan != Q6K_OK) return plan;
-  if (!DOTS) zero_split_tiles(sp, gx, gy, kTile * kWgTokTiles, true, y, ldy, n, m, s);
   hipLaunchKernelGGL((q4k_gemm_kernel<DOTS>), dim3((unsigned)sp.nblocks), dim3(256), 0, s,
                      static_cast<const uint8_t*>(xq), dap, dasp, wc, ws, n, m, nchunk, y, ldy,
-                     dots, (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full,
+                     slabs, dots, (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full,
                      (uint32_t)sp.pieces);
+  if (!DOTS) reduce_split_tiles(sp, gx, gy, true, slabs, y, ldy, n, m, s);
   const q6k_status st = launch_status();
   if (st == Q6K_OK) g_q4k_launches.fetch_add(1, std::memory_order_relaxed);
   return st;
@@ -1949,11 +2057,25 @@ q6k_status q4k_act_sums(const void* xq, const float* da, int64_t n, int64_t k, f
   return launch_status();
 }
 
+q6k_status q4k_gemm_workspace(int64_t n, int64_t m, int64_t k, size_t* bytes) {
+  if (!bytes) return Q6K_EINVAL;
+  *bytes = 0;
+  const q6k_status shape = q4k_gemm_shape(n, m, k);
+  if (shape != Q6K_OK || n == 0 || m == 0) return shape;
+  int64_t gx, gy;
+  SplitPlan sp;
+  const q6k_status plan = q4k_gemm_plan(n, m, k, &gx, &gy, &sp);
+  if (plan == Q6K_OK) *bytes = plan_workspace_bytes(sp);
+  return plan;
+}
+
 q6k_status q4k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
                     const float* das, size_t das_bytes, int64_t n, const void* w, size_t w_bytes,
-                    int64_t m, int64_t k, float* y, size_t y_bytes, int64_t ldy, void* stream) {
+                    int64_t m, int64_t k, float* y, size_t y_bytes, int64_t ldy, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   return q4k_gemm_common<false>(xq, xq_bytes, da, da_bytes, das, das_bytes, n, w, w_bytes, m, k,
-                                y, y_bytes, ldy, DotsOut{nullptr, 0, 0, 0, 0}, 0, stream);
+                                y, y_bytes, ldy, workspace, workspace_bytes,
+                                DotsOut{nullptr, 0, 0, 0, 0}, 0, stream);
 }
 
 q6k_status q4k_gemm_dots(const void* xq, size_t xq_bytes, int64_t n, const void* w,
@@ -1961,7 +2083,8 @@ q6k_status q4k_gemm_dots(const void* xq, size_t xq_bytes, int64_t n, const void*
                          int64_t row0, int64_t nrow, int32_t* dots, size_t dots_bytes,
                          void* stream) {
   return q4k_gemm_common<true>(xq, xq_bytes, nullptr, 0, nullptr, 0, n, w, w_bytes, m, k, nullptr,
-                               0, 0, DotsOut{dots, tok0, ntok, row0, nrow}, dots_bytes, stream);
+                               0, 0, nullptr, 0, DotsOut{dots, tok0, ntok, row0, nrow}, dots_bytes,
+                               stream);
 }
 
 uint64_t q4k_launches(void) { return g_q4k_launches.load(std::memory_order_relaxed); }
@@ -2040,11 +2163,25 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
   return launch_status();
 }
 
+q6k_status q6k_gemm_workspace(int64_t n, int64_t m, int64_t k, int layout, size_t* bytes) {
+  if (!bytes) return Q6K_EINVAL;
+  *bytes = 0;
+  const q6k_status shape = gemm_shape(n, m, k, layout);
+  if (shape != Q6K_OK || n == 0 || m == 0) return shape;
+  int64_t gx, gy;
+  SplitPlan sp;
+  const q6k_status plan = gemm_plan(n, m, k, layout, &gx, &gy, &sp);
+  if (plan == Q6K_OK) *bytes = plan_workspace_bytes(sp);
+  return plan;
+}
+
 q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
                     int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
-                    float* y, size_t y_bytes, int64_t ldy, void* stream) {
+                    float* y, size_t y_bytes, int64_t ldy, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   return gemm_common<kOutY>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k, y, y_bytes,
-                            ldy, DotsOut{nullptr, 0, 0, 0, 0}, 0, stream);
+                            ldy, workspace, workspace_bytes, DotsOut{nullptr, 0, 0, 0, 0}, 0,
+                            stream);
 }
 
 q6k_status q6k_gemm_subdots(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
@@ -2052,7 +2189,7 @@ q6k_status q6k_gemm_subdots(const void* xq, size_t xq_bytes, const float* da, si
                             int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
                             int32_t* dots, size_t dots_bytes, void* stream) {
   return gemm_common<kOutSubdots>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k,
-                                  nullptr, 0, 0, DotsOut{dots, tok0, ntok, row0, nrow},
+                                  nullptr, 0, 0, nullptr, 0, DotsOut{dots, tok0, ntok, row0, nrow},
                                   dots_bytes, stream);
 }
 
@@ -2061,8 +2198,8 @@ q6k_status q6k_gemm_chunkdots(const void* xq, size_t xq_bytes, const float* da, 
                               int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
                               int32_t* dots, size_t dots_bytes, void* stream) {
   return gemm_common<kOutChunkdots>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k,
-                                    nullptr, 0, 0, DotsOut{dots, tok0, ntok, row0, nrow},
-                                    dots_bytes, stream);
+                                    nullptr, 0, 0, nullptr, 0,
+                                    DotsOut{dots, tok0, ntok, row0, nrow}, dots_bytes, stream);
 }
 
 const char* q6k_strerror(int status) {

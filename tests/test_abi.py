@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     from q6_int8_prefill_amd import _lib as binding
     assert sorted(binding.EXPORTS) == names
     L = lib()
@@ -124,7 +124,8 @@ BIG = 1 << 40  # a buffer size that passes every size check
 
 def gemm_args(xq=FAKE, xqb=BIG, da=FAKE, dab=BIG, n=4, w=FAKE, wb=BIG, layout=1, m=8, k=256,
               y=FAKE, yb=BIG, ldy=8):
-    return (xq, xqb, da, dab, n, w, wb, layout, m, k, y, yb, ldy, None)
+    # no workspace: every case below fails (or is empty) before the work split is planned
+    return (xq, xqb, da, dab, n, w, wb, layout, m, k, y, yb, ldy, None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -173,7 +174,24 @@ def test_gemm_size_limits():
     assert L.q6k_gemm(*gemm_args(layout=2, n=(1 << 40) + 1)) == -4
     assert L.q6k_gemm(*gemm_args(layout=2, m=(1 << 40) + 1, ldy=(1 << 40) + 1)) == -4
     assert L.q4k_gemm(FAKE, BIG, FAKE, BIG, FAKE, BIG, 4, FAKE, BIG, 8, 1 << 26, FAKE, BIG, 8,
-                      None) == -4
+                      None, 0, None) == -4
+
+
+def test_workspace_query_errors():
+    # shape errors come before the device is asked for its compute units; *bytes is 0 on error
+    L = lib()
+    out = ctypes.c_size_t(123)
+    for args, status in (((4, 8, 100, 1), -2), ((4, 8, 256, 3), -1), ((-1, 8, 256, 1), -1),
+                         ((4, 8, 1 << 25, 2), -4), ((0, 8, 256, 1), 0), ((4, 0, 256, 2), 0)):
+        out.value = 123
+        assert L.q6k_gemm_workspace(*args, ctypes.byref(out)) == status, args
+        assert out.value == 0, args
+    assert L.q6k_gemm_workspace(4, 8, 256, 1, None) == -1
+    for args, status in (((4, 8, 100), -2), ((4, 8, 1 << 26), -4), ((0, 8, 256), 0)):
+        out.value = 123
+        assert L.q4k_gemm_workspace(*args, ctypes.byref(out)) == status, args
+        assert out.value == 0, args
+    assert L.q4k_gemm_workspace(4, 8, 256, None) == -1
 
 
 def dots_args(layout, win=(0, 4, 0, 8), dots=FAKE, dotsb=BIG, k=256, n=4, m=8):
@@ -240,7 +258,8 @@ def test_q4k_sizes_and_errors():
     assert L.q4k_act_sums(FAKE, FAKE, 4, 256, FAKE, 10, None) == -4
     assert L.q4k_act_sums(FAKE, FAKE + 4, 4, 256, FAKE, 1 << 30, None) == -3
     def q4(xq=FAKE, da=FAKE, das=FAKE, n=4, k=256, ldy=8, wb=BIG, yb=BIG, dab=BIG):
-        return L.q4k_gemm(xq, BIG, da, dab, das, dab, n, FAKE, wb, 8, k, FAKE, yb, ldy, None)
+        return L.q4k_gemm(xq, BIG, da, dab, das, dab, n, FAKE, wb, 8, k, FAKE, yb, ldy, None, 0,
+                          None)
     assert q4(das=None) == -1                     # null das
     assert q4(ldy=7) == -1                        # ldy < m
     assert q4(k=100) == -2

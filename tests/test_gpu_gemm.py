@@ -265,7 +265,8 @@ def test_gemm_zero_scales_give_zero(layout):
 def test_folded_split_k_pieces(n, m, k):
     """Layout 2 deals its 64-token x 128-row output tiles out in rounds of one per workgroup slot
     and splits the tiles of a partial last round along k into pieces of whole super-blocks, whose
-    partial sums are added into y after a zeroing pass.  On a 256-CU device these shapes give
+    partial sums go to workspace slabs that a second kernel adds into y in piece order.  On a
+    256-CU device these shapes give
     pieces of unequal length (10 super-blocks over 4 pieces; 100 over 64).  The integer numerators
     must stay bit-exact and the outputs within tolerance, checked on a sample of tokens."""
     import gpu_util
@@ -317,9 +318,9 @@ def test_gemm_whole_tiles_ragged_rows(layout, ldy):
 def test_gemm_partly_split_grid(layout):
     """2176 x 4096 outputs: 1088 tiles of 64 x 128 (544 of 128 x 128), more than one round of
     workgroup slots with a short last round, so some tiles are computed whole and the rest are
-    split along k, zeroed first and added into; the zeroing must hit exactly the split tiles of
-    the GEMM's own tile order (every output is checked finite, sampled tokens against the
-    oracle)."""
+    split along k into workspace slabs that a second kernel adds up; the reduction must hit
+    exactly the split tiles of the GEMM's own tile order (y starts as NaN: every output is checked
+    finite, sampled tokens against the oracle)."""
     import gpu_util
     n, m, k = 2176, 4096, 512
     print(f"partly split grid layout={layout}", flush=True)
@@ -335,29 +336,72 @@ def test_gemm_partly_split_grid(layout):
     assert ok, f"worst |err|/T = {worst}"
 
 
-def test_repeatability_whole_and_split_tiles():
-    """Tiles computed whole are bit-for-bit repeatable; tiles split along k add their pieces with
-    float atomics in run-dependent order, so their last bits may vary by a few roundings of the
-    partial sums, each at most sum|terms| in magnitude."""
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_repeatability_whole_and_split_tiles(layout):
+    """Every output is bit-for-bit repeatable: tiles computed whole by construction, tiles split
+    along k because their pieces' slabs are added in piece order by one thread per output.  The
+    second problem is all split tiles (a workspace is needed); the first, 6 x CUs tiles of 64 x
+    128, fills whole rounds of 2 and of 3 workgroups per CU (3072 tokens on 256 CUs)."""
     import torch
     import gpu_util
     import q6_int8_prefill_amd as q6k
-    for n, m, k, split in ((2048, 4096, 512, False), (200, 384, 2048, True)):
-        print(f"repeatability n={n} m={m} k={k}", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for n, m, k, split in ((12 * cus, 4096, 512, False), (200, 384, 2048, True)):
+        print(f"repeatability layout={layout} n={n} m={m} k={k}", flush=True)
+        assert (q6k.q6k_gemm_workspace(n, m, k, layout) > 0) == split
         raw = synthetic.weights(m, k, seed=n + 9, sc_lo=-128, sc_hi=127)
         x = synthetic.activations(n, k, seed=n + 10, kind="outlier")
         xq, da = gpu_util.quantize(x)
-        w = gpu_util.expand(raw, m, k, 2)
-        runs = [gpu_util.gemm(xq, da, n, w, 2, m, k) for _ in range(3)]
-        if not split:
-            for r in runs[1:]:
-                np.testing.assert_array_equal(r.view(np.uint32), runs[0].view(np.uint32))
-        else:
-            xq_ref, da_ref = oracle.quantize(x)
-            _, t_ref = oracle.gemm(xq_ref, da_ref, raw, m)
-            for r in runs[1:]:
-                diff = np.abs(r.astype(np.float64) - runs[0])
-                assert (diff <= 1e-6 * t_ref).all(), float((diff / np.maximum(t_ref, 1e-300)).max())
+        w = gpu_util.expand(raw, m, k, layout)
+        runs = [gpu_util.gemm(xq, da, n, w, layout, m, k) for _ in range(3)]
+        assert np.isfinite(runs[0]).all()
+        for r in runs[1:]:
+            np.testing.assert_array_equal(r.view(np.uint32), runs[0].view(np.uint32))
+
+
+def test_workspace_rules_and_size():
+    """Through the C ABI: the workspace q6k_gemm_workspace reports is one 32 KiB slab per piece of
+    a split tile (at most one per workgroup slot); a call that needs one rejects a missing,
+    misaligned or short workspace before launching anything, and a caller's workspace full of NaN
+    gives the same y, bit for bit, as one the binding allocates."""
+    import ctypes
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    from q6_int8_prefill_amd import _lib
+    L = _lib._lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n, m, k = 200, 384, 2048
+    print(f"workspace rules n={n} m={m} k={k}", flush=True)
+    for layout, slots in ((2, 2 * cus), (1, 3 * cus), (0, 3 * cus)):
+        tiles = (-(-n // 128) * 128 // 64) * (-(-m // 128))   # 64 x 128 output tiles
+        pieces = min(slots // tiles, k // 256)                  # every tile split, whole super-blocks
+        assert q6k.q6k_gemm_workspace(n, m, k, layout) == tiles * pieces * 32768, layout
+    assert q6k.q4k_gemm_workspace(n, m, k) == q6k.q6k_gemm_workspace(n, m, k, 1)
+    assert q6k.q6k_gemm_workspace(12 * cus, 4096, 512, 2) == 0  # whole rounds only
+    raw = synthetic.weights(m, k, seed=71, sc_lo=-128, sc_hi=127)
+    x = synthetic.activations(n, k, seed=72, kind="outlier")
+    xq, da = gpu_util.quantize(x)
+    for layout in (2, 1):
+        need = q6k.q6k_gemm_workspace(n, m, k, layout)
+        w = gpu_util.expand(raw, m, k, layout)
+        y = torch.full((n, m), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+        ws = torch.full((need // 4 + 4,), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+
+        def call(p, nb):
+            return L.q6k_gemm(xq.data_ptr(), xq.numel(), da.data_ptr(), da.numel() * 4, n,
+                              w.data_ptr(), w.numel(), layout, m, k, y.data_ptr(), y.numel() * 4,
+                              m, p, nb, torch.cuda.current_stream().cuda_stream)
+        assert call(None, 0) == -1
+        assert call(ws.data_ptr() + 4, need) == -3
+        assert call(ws.data_ptr(), need - 1) == -4
+        torch.cuda.synchronize()
+        assert torch.isnan(y).all()                            # nothing ran
+        assert call(ws.data_ptr(), need) == 0
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        ref = gpu_util.gemm(xq, da, n, w, layout, m, k)
+        np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 def test_packed_layout_equals_expanded_bit_for_bit():

@@ -1,9 +1,10 @@
 """The hot path recorded in a HIP graph (torch.cuda.graph) and replayed: the prepass and the GEMM
-(every layout) with its split-k last round (a zeroing kernel, then float atomics) launch only kernels on
-the caller's stream (no memset nodes), so a captured step replays to the eager results.  Each
-replay follows eager work of the program's own that clobbers every output, and is checked: codes
-and scales byte for byte against the eager run and the oracle, outputs against the eager run up
-to the order of the split tiles' additions, and against the oracle within the output tolerance."""
+(every layout) with its split-k last round (pieces into workspace slabs, then the reducing
+kernel) launch only kernels on the caller's stream (no memset nodes), so a captured step replays
+to the eager results.  Each replay follows eager work of the program's own that clobbers every
+output and the workspace, and is checked: codes, scales and outputs bit for bit against the eager
+run, codes and scales against the oracle, and outputs against the oracle within the output
+tolerance."""
 import numpy as np
 import pytest
 
@@ -30,10 +31,12 @@ def test_captured_step_replays(n, m, k, layout):
     xq = torch.zeros(xb, dtype=torch.uint8, device=dev)
     da = torch.zeros(db // 4, dtype=torch.float32, device=dev)
     y = torch.zeros((n, m), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(q6k.q6k_gemm_workspace(n, m, k, layout) // 4, 1), dtype=torch.float32,
+                     device=dev)
 
     def step():
         q6k.q6k_quantize_act(xg, xq, da)
-        q6k.q6k_gemm(xq, da, n, w, layout, m, k, y)
+        q6k.q6k_gemm(xq, da, n, w, layout, m, k, y, workspace=ws)
 
     # eager reference of the same calls
     step()
@@ -59,16 +62,14 @@ def test_captured_step_replays(n, m, k, layout):
         xq.fill_(0xA5)
         da.fill_(float("nan"))
         y.fill_(float("nan"))
+        ws.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(xq, xq_e), rep
         assert torch.equal(da.view(torch.int32), da_e.view(torch.int32)), rep
+        assert torch.equal(y.view(torch.int32), y_e.view(torch.int32)), rep
         got = y.cpu().numpy()
-        assert np.isfinite(got).all(), rep
-        # against the eager run: equal up to the order of the split tiles' additions
-        diff = np.abs(got.astype(np.float64) - y_e.cpu().numpy())
-        assert (diff[rows] <= 1e-6 * t_ref + 1e-30).all(), rep
         ok, worst = gpu_util.within_tolerance(got[rows], y_ref, t_ref)
         assert ok, f"replay {rep}: worst |err|/T = {worst}"
     np.testing.assert_array_equal(untile_xq(xq.cpu().numpy(), n, k)[:n], xq_ref)
@@ -78,7 +79,8 @@ def test_captured_step_replays(n, m, k, layout):
 
 def test_captured_q4k_step_replays():
     """The q4_K step (its one-pass prepass, then the GEMM with a split-k last round) captured and
-    replayed after eager clobbering, as above."""
+    replayed after eager clobbering, as above; here the binding allocates the GEMM's workspace
+    inside the capture (from the graph's memory pool)."""
     import torch
     import gpu_util
     import q6_int8_prefill_amd as q6k
@@ -126,8 +128,7 @@ def test_captured_q4k_step_replays():
         assert torch.equal(xq, xq_e), rep
         assert torch.equal(da.view(torch.int32), da_e.view(torch.int32)), rep
         assert torch.equal(das.view(torch.int32), das_e.view(torch.int32)), rep
+        assert torch.equal(y.view(torch.int32), y_e.view(torch.int32)), rep
         got = y.cpu().numpy()
-        diff = np.abs(got.astype(np.float64) - y_e.cpu().numpy())
-        assert (diff <= 1e-6 * t_ref + 1e-30).all(), rep
         ok, worst = gpu_util.within_tolerance(got, y_ref, t_ref)
         assert ok, f"replay {rep}: worst |err|/T = {worst}"

@@ -190,7 +190,8 @@ def test_split_k_pieces():
 
 def test_partly_split_grid():
     """1088 output tiles on a 768-slot device: 768 computed whole, the other 320 split along k,
-    zeroed first and added into; every output finite, sampled tokens against the oracle."""
+    their pieces reduced from workspace slabs; every output finite (y starts as NaN), sampled
+    tokens against the oracle."""
     n, m, k = 2176, 4096, 512
     print("q4k partly split grid", flush=True)
     raw = synthetic.weights_q4k(m, k, seed=61)
