@@ -21,7 +21,8 @@
  *
  * Conventions for every entry point
  *   - Every buffer pointer is a DEVICE pointer owned by the caller; the library never allocates,
- *     frees or retains memory.  `stream` is a hipStream_t (NULL = the null stream).
+ *     frees or retains memory (apart from q6k_gemm_noalloc's static scratch array, which is
+ *     part of the loaded code object).  `stream` is a hipStream_t (NULL = the null stream).
  *   - Calls are asynchronous on `stream` and never synchronize.  Arguments are checked on the
  *     host before anything is launched; on any error nothing is launched and the output buffers
  *     are untouched.  A fault inside a kernel surfaces at the caller's next synchronization.
@@ -83,7 +84,8 @@ typedef enum {
   Q6K_ESHAPE = -2, /* k not a positive multiple of 256 */
   Q6K_EALIGN = -3, /* a pointer or leading dimension breaks the 16-byte alignment rule */
   Q6K_ESIZE = -4,  /* a buffer is smaller than the call reads or writes, or sizes overflow */
-  Q6K_EHIP = -5    /* the HIP runtime rejected a launch */
+  Q6K_EHIP = -5,   /* the HIP runtime rejected a launch */
+  Q6K_ESCRATCH = -6 /* q6k_gemm_noalloc: the problem needs more than its static scratch holds */
 } q6k_status;
 
 enum { Q6K_LAYOUT_PACKED = 0, Q6K_LAYOUT_EXPANDED = 1, Q6K_LAYOUT_FOLDED = 2 };
@@ -161,6 +163,20 @@ q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_
                     int64_t n, const void* w, size_t w_bytes, int layout, int64_t m, int64_t k,
                     float* y, size_t y_bytes, int64_t ldy, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): q6k_gemm with its split-k workspace taken
+ * from a static device array of the library instead of a caller buffer.  Same arguments (minus
+ * the workspace), kernels, work split and results (bit for bit) as q6k_gemm.  The array holds
+ * 24 MiB (768 slabs of 32 KiB: 3 workgroup slots per compute unit on a 256-CU device, the most
+ * any layout needs there); a problem that needs more returns Q6K_ESCRATCH and launches nothing.
+ * Each GPU holds its own copy, from the first call on it until the process ends; the call
+ * itself allocates and frees nothing.  Every call on one GPU uses that GPU's one array (no part
+ * of it needs clearing: a call reads only what it wrote), so calls that overlap on one GPU (on
+ * different streams, or from several threads) race; calls on one stream are ordered. */
+q6k_status q6k_gemm_noalloc(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                            int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
+                            int64_t k, float* y, size_t y_bytes, int64_t ldy, void* stream);
 
 /* Workspace bytes that q6k_gemm needs for this n, m, k and layout on the device current on the
  * calling thread (the work split depends on its compute-unit count): 32 KiB per piece of a

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     q6k_expand_weights,
     q6k_gemm,
     q6k_gemm_chunkdots,
+    q6k_gemm_noalloc,
     q6k_gemm_subdots,
     q6k_gemm_workspace,
     q6k_quantize_act,

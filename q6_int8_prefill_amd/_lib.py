@@ -31,6 +31,9 @@ _lib.q6k_expand_weights.argtypes = [_p, _i64, _i64, _int, _p, _sz, _p]
 _lib.q6k_gemm.restype = _int
 _lib.q6k_gemm.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64, _p,
                           _sz, _p]
+_lib.q6k_gemm_noalloc.restype = _int
+_lib.q6k_gemm_noalloc.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64,
+                                  _p]
 _lib.q6k_gemm_workspace.restype = _int
 _lib.q6k_gemm_workspace.argtypes = [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]
 _WIN = [_i64, _i64, _i64, _i64]
@@ -64,7 +67,8 @@ _lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
 
 EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_swiglu_quantize_act", "q6k_swiglu_f32",
            "q6k_weight_bytes", "q6k_expand_weights",
-           "q6k_gemm_workspace", "q6k_gemm", "q6k_gemm_subdots", "q6k_gemm_chunkdots",
+           "q6k_gemm_workspace", "q6k_gemm", "q6k_gemm_noalloc", "q6k_gemm_subdots",
+           "q6k_gemm_chunkdots",
            "q6k_strerror", "q6k_stats",
            "q4k_weight_bytes", "q4k_expand_weights", "q4k_quantize_act", "q4k_act_sums",
            "q4k_gemm_workspace", "q4k_gemm", "q4k_gemm_dots", "q4k_launches")
@@ -254,6 +258,16 @@ def q6k_gemm(xq, da, n, w, layout, m, k, y, ldy=None, stream=None, workspace=Non
     _check(_lib.q6k_gemm(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), n, _ptr(w), _nbytes(w),
                          layout, m, k, _ptr(y), _span(y), ldy, _ptr(ws), _nbytes(ws),
                          _stream(stream)), "q6k_gemm")
+
+
+def q6k_gemm_noalloc(xq, da, n, w, layout, m, k, y, ldy=None, stream=None):
+    """q6k_gemm with the split-k workspace in the library's static device array (allocates
+    nothing; calls that overlap on one GPU race)."""
+    ldy = _y_operand(y, n, m, ldy)
+    _flat(xq=xq, da=da, w=w)
+    _check(_lib.q6k_gemm_noalloc(_ptr(xq), _nbytes(xq), _ptr(da), _nbytes(da), n, _ptr(w),
+                                 _nbytes(w), layout, m, k, _ptr(y), _span(y), ldy,
+                                 _stream(stream)), "q6k_gemm_noalloc")
 
 
 def _window(n, m, tok0, ntok, row0, nrow):

@@ -22,6 +22,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "q4k.h"
 #include "q6k.h"
@@ -2000,6 +2001,36 @@ q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, siz
   return st;
 }
 
+// The workspace of q6k_gemm_noalloc: split-k slabs in static device memory, one copy per GPU the
+// library runs on, held until the process ends.  kScratchSlabs = 3 workgroup slots per CU x 256
+// CUs, the most any q6_K layout splits into on such a device (24 MiB).  Host code never uses the
+// array's name as an address: each device's address comes from hipGetSymbolAddress, taken on the
+// first call on that device with the device current, and kept in scratch_addr.
+constexpr int64_t kScratchSlabs = 768;
+constexpr size_t kScratchBytes = (size_t)kScratchSlabs * kSlabFloats * sizeof(float);
+static __device__ __attribute__((aligned(256))) float scratch[kScratchSlabs * kSlabFloats];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's address of `scratch`.
+q6k_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q6K_EHIP;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return Q6K_EHIP;
+      scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return Q6K_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2184,6 +2215,24 @@ q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_
                             stream);
 }
 
+q6k_status q6k_gemm_noalloc(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
+                            int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
+                            int64_t k, float* y, size_t y_bytes, int64_t ldy, void* stream) {
+  const q6k_status shape = gemm_shape(n, m, k, layout);
+  if (shape != Q6K_OK || n == 0 || m == 0) return shape;
+  size_t need = 0;
+  const q6k_status ws = q6k_gemm_workspace(n, m, k, layout, &need);
+  if (ws != Q6K_OK) return ws;
+  if (need > kScratchBytes) return Q6K_ESCRATCH;
+  void* p = nullptr;
+  if (need > 0) {
+    const q6k_status sp = scratch_ptr(&p);
+    if (sp != Q6K_OK) return sp;
+  }
+  return gemm_common<kOutY>(xq, xq_bytes, da, da_bytes, n, w, w_bytes, layout, m, k, y, y_bytes,
+                            ldy, p, need, DotsOut{nullptr, 0, 0, 0, 0}, 0, stream);
+}
+
 q6k_status q6k_gemm_subdots(const void* xq, size_t xq_bytes, const float* da, size_t da_bytes,
                             int64_t n, const void* w, size_t w_bytes, int layout, int64_t m,
                             int64_t k, int64_t tok0, int64_t ntok, int64_t row0, int64_t nrow,
@@ -2210,6 +2259,7 @@ const char* q6k_strerror(int status) {
     case Q6K_EALIGN: return "pointer or leading dimension not 16-byte aligned";
     case Q6K_ESIZE: return "buffer smaller than required, or problem too large";
     case Q6K_EHIP: return "HIP runtime rejected a kernel launch";
+    case Q6K_ESCRATCH: return "problem needs more split-k scratch than q6k_gemm_noalloc's static array holds";
     default: return "unknown status";
   }
 }

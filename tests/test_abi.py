@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     from q6_int8_prefill_amd import _lib as binding
     assert sorted(binding.EXPORTS) == names
     L = lib()
@@ -192,6 +192,20 @@ def test_workspace_query_errors():
         assert L.q4k_gemm_workspace(*args, ctypes.byref(out)) == status, args
         assert out.value == 0, args
     assert L.q4k_gemm_workspace(4, 8, 256, None) == -1
+
+
+def test_noalloc_errors():
+    # the argument rules of q6k_gemm; shape errors come before the device is asked for anything
+    L = lib()
+
+    def call(**kw):
+        return L.q6k_gemm_noalloc(*(gemm_args(**kw)[:13] + (None,)))
+    assert call(layout=3) == -1
+    assert call(k=100) == -2
+    assert call(n=-1) == -1
+    assert call(layout=2, k=1 << 25) == -4
+    assert call(n=0) == 0 and call(m=0) == 0
+    assert L.q6k_strerror(-6) and b"scratch" in L.q6k_strerror(-6)
 
 
 def dots_args(layout, win=(0, 4, 0, 8), dots=FAKE, dotsb=BIG, k=256, n=4, m=8):
