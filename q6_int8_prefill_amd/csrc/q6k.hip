@@ -551,17 +551,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 // wave fills its share of a slot with gfx950 direct-to-LDS loads through buffer resources
 // (buffer_load_dwordx4 ... lds, 16 bytes per lane, no registers): row tile w's weight codes and
 // scales, and, for waves 0 and 1, token tile w's activations and da.  Loads run kRing-1 chunks
-// ahead of the compute.  Step c (chunk c, slot c % kRing) of a wave:
-//   1. meet: every wave's share of chunk c is in its slot (each wave waited for its own loads of
-//      chunk c during step c-1, and layout 0 expanded its row tile of chunk c there), and every
-//      wave is done with chunk c-1, so that slot is free;
-//   2. issue the loads of chunk c+kRing-1 into the freed slot;
-//   3. read chunk c's fragments and scales from LDS, start the four MFMAs;
-//   4. wait for this wave's own loads of chunk c+1 (kRing-2 newer chunks may stay in flight);
-//   5. rescale chunk c: tile 0, then (layout 0) start the LDS reads of this wave's packed codes
-//      of chunk c+1, then tile 1 (the reads land meanwhile);
-//   6. layout 0: expand row tile w of chunk c+1 into B fragments of 4 x the centered int8 codes
-//      and the pair (d*sc0, d*sc1) in the slot.
+// ahead of the compute.  Step c (chunk c, slot c % kRing) of a wave, entered with chunk c complete
+// in LDS for every wave and this wave's A and B fragments of chunk c on their way to registers:
+//   1. wait for the fragments, start the LDS reads of chunk c's da and scale pairs, start the
+//      four MFMAs (the reads land behind them);
+//   2. issue the loads of chunk c+kRing-1 into chunk c-1's slot, which every wave finished
+//      reading before the meeting of step c-1;
+//   3. wait for this wave's own loads of chunk c+1 (kRing-2 newer chunks may stay in flight) and
+//      for the da and scale reads;
+//   4. layout 0: start the LDS reads of this wave's packed codes of chunk c+1; rescale tile 0 of
+//      chunk c (the reads land meanwhile); expand row tile w of chunk c+1 into B fragments of
+//      4 x the centered int8 codes and the pair (d*sc0, d*sc1) in its slot;
+//   5. meet: every wave's share of chunk c+1 is in its slot (loads landed, layout 0 expanded),
+//      and every wave is done with chunk c's da and scales;
+//   6. start the LDS reads of chunk c+1's fragments, then rescale tile 1 of chunk c (the reads
+//      land meanwhile).
 // The chunk loop is unrolled over the ring, so every slot address is a per-lane base register
 // plus an immediate offset (no address arithmetic per chunk).  LDS reads and writes are inline
 // assembly with explicit waits: the compiler would otherwise wait for every outstanding
@@ -770,11 +774,29 @@ struct GemmCtx {
   bool loads_a;
 };
 
+// This wave's MFMA operands of one chunk: its token tile's A fragment and the B fragments of its
+// two row tiles, read from LDS one step ahead of their MFMAs.
+struct GemmFrags {
+  v4u a, b0, b1;
+};
+
+template <int OFF>
+__device__ __forceinline__ void read_frags(const GemmLanes& L, GemmFrags& f) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7"
+      : "=&v"(f.a), "=&v"(f.b0), "=&v"(f.b1)
+      : "v"(L.aa), "v"(L.bb), "n"(OFF), "n"(OFF), "n"(OFF + 1024)
+      : "memory");
+}
+
 // Step c (chunk c in ring slot J; chunk c0 + i lives in slot i % KRING), as described above.
-// Every slot offset is a compile-time constant.
+// Every slot offset is a compile-time constant.  On entry chunk c is complete in LDS for every
+// wave and its fragments are on their way into f; on exit the same holds for chunk c + 1.
 template <int LAYOUT, bool SUBDOTS, int KRING, int J>
 __device__ __forceinline__ void gemm_step(const GemmCtx& k, uint32_t c, float (&acc)[2][16],
-                                          v16i& bias) {
+                                          v16i& bias, GemmFrags& f) {
   constexpr int kSlot = SlotSize<LAYOUT>::value;
   constexpr int kCur = J * kSlot;
   constexpr int kNext = ((J + 1) % KRING) * kSlot;
@@ -785,62 +807,63 @@ __device__ __forceinline__ void gemm_step(const GemmCtx& k, uint32_t c, float (&
   __builtin_amdgcn_sched_barrier(0);
   // the MFMA bias stays in its 16 VGPRs (instead of being rebuilt from scalars every step)
   asm volatile("" : "+v"(bias));
-  // 1. chunk c complete in LDS for every wave; every wave is done with chunk c-1's slot
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  // 2.
-  const uint32_t ci = c + KRING - 1;
-  issue_chunk<LAYOUT>(k.smem + kIssue, k.src, ci < k.c1 ? ci : k.c1 - 1, k.wave, k.lane);
-  // 3. LDS reads of this chunk: row tile 2rp's B and scales, A and da, then row tile 2rp+1's
-  v4u a, b0, b1;
+  // 1. the fragments of chunk c have landed; read its da and scale pairs (they land behind the
+  // MFMAs)
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.a), "+v"(f.b0), "+v"(f.b1)::"memory");
   v4f d0, d1, d2, d3;
   v2f t0, t1;
   asm volatile(
-      "ds_read_b128 %0, %9 offset:%13\n\t"
-      "ds_read_b64 %1, %10 offset:%14\n\t"
-      "ds_read_b128 %2, %11 offset:%15\n\t"
-      "ds_read_b128 %3, %12 offset:%16\n\t"
-      "ds_read_b128 %4, %12 offset:%17\n\t"
-      "ds_read_b128 %5, %12 offset:%18\n\t"
-      "ds_read_b128 %6, %12 offset:%19\n\t"
-      "ds_read_b128 %7, %9 offset:%20\n\t"
-      "ds_read_b64 %8, %10 offset:%21"
-      : "=&v"(b0), "=&v"(t0), "=&v"(a), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(b1),
-        "=&v"(t1)
-      : "v"(k.lanes.bb), "v"(k.lanes.ss), "v"(k.lanes.aa), "v"(k.lanes.dd), "n"(kCur),
-        "n"(kCur), "n"(kCur), "n"(kCur), "n"(kCur + 16), "n"(kCur + 32), "n"(kCur + 48),
-        "n"(kCur + 1024), "n"(kCur + 256)
+      "ds_read_b64 %0, %6 offset:%8\n\t"
+      "ds_read_b128 %2, %7 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%9\n\t"
+      "ds_read_b128 %4, %7 offset:%10\n\t"
+      "ds_read_b128 %5, %7 offset:%11\n\t"
+      "ds_read_b64 %1, %6 offset:%12"
+      : "=&v"(t0), "=&v"(t1), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(k.lanes.ss), "v"(k.lanes.dd), "n"(kCur), "n"(kCur + 16), "n"(kCur + 32),
+        "n"(kCur + 48), "n"(kCur + 256)
       : "memory");
+  // (the reads stay ahead of the MFMAs, so their registers are never the fragments' registers,
+  // which an MFMA may still be reading when a read lands)
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. the MFMAs of both tiles
+  const long alo = (long)(((uint64_t)f.a.y << 32) | f.a.x);
+  const long ahi = (long)(((uint64_t)f.a.w << 32) | f.a.z);
+  v16i lo0, hi0, lo1, hi1;
+  tile_mfma(lo0, hi0, bias, alo, ahi, f.b0);
+  tile_mfma(lo1, hi1, bias, alo, ahi, f.b1);
+  // 3. chunk c+KRING-1 into chunk c-1's slot: every wave has passed a meeting since its last
+  // read of that slot
+  const uint32_t ci = c + KRING - 1;
+  issue_chunk<LAYOUT>(k.smem + kIssue, k.src, ci < k.c1 ? ci : k.c1 - 1, k.wave, k.lane);
+  // 4. this wave's loads of chunk c+1 have landed
+  wait_chunks<KRING - 2>(k.loads_a);
   asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(b0), "+v"(t0), "+v"(a), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3), "+v"(b1),
-                 "+v"(t1)::"memory");
+               : "+v"(t0), "+v"(t1), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3)::"memory");
   // (d*sc0, d*sc1) and their bias products (exact, see above)
   const v4f s0 = v4f{t0.x, t0.y, -kBiasF * t0.x, -kBiasF * t0.y};
   const v4f s1 = v4f{t1.x, t1.y, -kBiasF * t1.x, -kBiasF * t1.y};
   const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
                          d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
-  const long alo = (long)(((uint64_t)a.y << 32) | a.x);
-  const long ahi = (long)(((uint64_t)a.w << 32) | a.z);
-  v16i lo0, hi0, lo1, hi1;
-  tile_mfma(lo0, hi0, bias, alo, ahi, b0);
-  tile_mfma(lo1, hi1, bias, alo, ahi, b1);
-  // 4. this wave's loads of chunk c+1 have landed
-  wait_chunks<KRING - 2>(k.loads_a);
-  // 5. (tile 0's rescale, then the LDS reads of layout 0's codes of chunk c+1, whose registers
-  // are then live only beside tile 1's MFMA results)
+  // 5. layout 0: the LDS reads of this wave's packed codes of chunk c+1, landing behind tile 0's
+  // rescale; then their expand into the slot
+  RawCodes raw;
+  if (kPacked) expand_read<kNext>(k.lanes, raw);
   constexpr int kShift = kPacked ? 2 : 0;
   tile_rescale<SUBDOTS, kShift>(acc[0], lo0, hi0, s0, dav, k.lane, c, k.T, k.R0 + 2 * k.rp,
                                 k.nchunk, k.dots);
   if (!SUBDOTS) pin_acc(acc[0]);
-  RawCodes raw;
-  if (kPacked) expand_read<kNext>(k.lanes, raw);
-  tile_rescale<SUBDOTS, kShift>(acc[1], lo1, hi1, s1, dav, k.lane, c, k.T, k.R0 + 2 * k.rp + 1,
-                                k.nchunk, k.dots);
-  if (!SUBDOTS) pin_acc(acc[1]);
-  // 6.
   if (kPacked) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.s));
     expand_write<kNext>(k.lanes, raw, k.lane);
   }
+  // 6. chunk c+1 complete in LDS for every wave (loads landed, layout 0's expand written)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // 7. its fragments, landing behind tile 1's rescale
+  read_frags<kNext>(k.lanes, f);
+  tile_rescale<SUBDOTS, kShift>(acc[1], lo1, hi1, s1, dav, k.lane, c, k.T, k.R0 + 2 * k.rp + 1,
+                                k.nchunk, k.dots);
+  if (!SUBDOTS) pin_acc(acc[1]);
 }
 
 // Chunks cb .. cb+KRING-1 (slots 0 .. KRING-1), stopping at the piece's end (a piece has a
@@ -848,16 +871,16 @@ __device__ __forceinline__ void gemm_step(const GemmCtx& k, uint32_t c, float (&
 template <int LAYOUT, bool SUBDOTS, int KRING, int J>
 struct GemmSteps {
   __device__ __forceinline__ static void run(const GemmCtx& k, uint32_t cb, float (&acc)[2][16],
-                                             v16i& bias) {
+                                             v16i& bias, GemmFrags& f) {
     if (8 % KRING != 0 && cb + J >= k.c1) return;
-    gemm_step<LAYOUT, SUBDOTS, KRING, J>(k, cb + J, acc, bias);
-    GemmSteps<LAYOUT, SUBDOTS, KRING, J + 1>::run(k, cb, acc, bias);
+    gemm_step<LAYOUT, SUBDOTS, KRING, J>(k, cb + J, acc, bias, f);
+    GemmSteps<LAYOUT, SUBDOTS, KRING, J + 1>::run(k, cb, acc, bias, f);
   }
 };
 template <int LAYOUT, bool SUBDOTS, int KRING>
 struct GemmSteps<LAYOUT, SUBDOTS, KRING, KRING> {
-  __device__ __forceinline__ static void run(const GemmCtx&, uint32_t, float (&)[2][16],
-                                             v16i&) {}
+  __device__ __forceinline__ static void run(const GemmCtx&, uint32_t, float (&)[2][16], v16i&,
+                                             GemmFrags&) {}
 };
 
 template <int LAYOUT, bool SUBDOTS>
@@ -922,7 +945,8 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
     for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
 
   // Prologue: chunks c0 .. c0+kRing-2 in flight in slots 0 .. kRing-2; this wave's share of chunk
-  // c0 landed (and, layout 0, expanded); the first step's meeting makes it every wave's.
+  // c0 landed (and, layout 0, expanded), the meeting makes it every wave's, then chunk c0's
+  // fragments are read.
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j)
     issue_chunk<LAYOUT>(smem + j * kSlot, k.src, c0 + j < k.c1 ? c0 + j : k.c1 - 1, wave, lane);
@@ -933,8 +957,12 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.s));
     expand_write<0>(k.lanes, raw, lane);
   }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  GemmFrags f;
+  read_frags<0>(k.lanes, f);
 
-  for (uint32_t cb = c0; cb < k.c1; cb += kRing) GemmSteps<LAYOUT, SUBDOTS, kRing, 0>::run(k, cb, acc, bias);
+  for (uint32_t cb = c0; cb < k.c1; cb += kRing)
+    GemmSteps<LAYOUT, SUBDOTS, kRing, 0>::run(k, cb, acc, bias, f);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // drain the trailing loads
 
   if (SUBDOTS) return;
