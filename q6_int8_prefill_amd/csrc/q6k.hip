@@ -861,6 +861,7 @@ __device__ __forceinline__ void gemm_step(const GemmCtx& k, uint32_t c, float (&
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // 7. its fragments, landing behind tile 1's rescale
   read_frags<kNext>(k.lanes, f);
+  __builtin_amdgcn_sched_barrier(0);  // the reads go out before any of tile 1's rescale
   tile_rescale<SUBDOTS, kShift>(acc[1], lo1, hi1, s1, dav, k.lane, c, k.T, k.R0 + 2 * k.rp + 1,
                                 k.nchunk, k.dots);
   if (!SUBDOTS) pin_acc(acc[1]);
@@ -1557,74 +1558,108 @@ __device__ __forceinline__ void q4_order(float (&v)[16]) {
                  "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
 }
 
+// The rescale of output tile u for chunk c (or, DOTS, the store of its chunk dots).
+template <bool DOTS>
+__device__ __forceinline__ void q4_tile(const Q4Ctx& k, uint32_t c, int u, const v16i& f, v2f pr,
+                                        const float (&dav)[16], const float (&dsv)[16],
+                                        float (&acc)[16]) {
+  if (DOTS) {
+    const int g = k.lane >> 5;
+    const DotsRun d = dots_run<true>(k.dots, k.tok_base + 4 * g, k.col + u * kTile, k.nchunk, c);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int32_t* o = dots_slot(k.dots, d, r);
+      if (o) *o = f[r] - kBiasI;
+    }
+  } else {
+    const float nb = -kBiasF * pr.x;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(f[r]), pr.x, nb);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(t[r], dav[r], acc[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = __builtin_fmaf(pr.y, dsv[r], acc[r]);
+  }
+  q4_order(acc);  // keep the steps in program order (bounded register lifetimes)
+}
+
+// This wave's MFMA operands of one chunk (A fragment, B fragments of its two row tiles), read from
+// LDS one step ahead of their MFMAs.
+struct Q4Frags {
+  v4i a, b0, b1;
+};
+
+template <int OFF>
+__device__ __forceinline__ void q4_read_frags(const Q4Ctx& k, Q4Frags& f) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7"
+      : "=&v"(f.a), "=&v"(f.b0), "=&v"(f.b1)
+      : "v"(k.aa), "v"(k.bb), "n"(OFF + kQ4SlotA), "n"(OFF + kQ4SlotB),
+        "n"(OFF + kQ4SlotB + 1024)
+      : "memory");
+}
+
+// Step CC of super-block s (chunk c = 8s + CC in ring slot CC % kQ4Ring), entered with chunk c
+// complete in LDS for every wave and its fragments on their way into f:
+//   1. wait for the fragments, start the LDS reads of the chunk's (d*sc, -dmin*m) pairs, da and
+//      da*S, start both MFMAs (the reads land behind them);
+//   2. issue the loads of chunk c+3 into chunk c-1's slot (every wave finished reading it before
+//      the meeting of step c-1), wait for this wave's own loads of chunk c+1 and for the reads;
+//   3. tile 0's rescale; meet (chunk c+1 complete for every wave, every wave done with chunk c's
+//      scales); start the reads of chunk c+1's fragments; tile 1's rescale (they land meanwhile).
 template <bool DOTS, int CC>
 __device__ __forceinline__ void q4_step(const Q4Ctx& k, uint32_t s, uint32_t par, v16i& bias,
-                                        float (&acc)[2][16]) {
+                                        float (&acc)[2][16], Q4Frags& f) {
   const uint32_t c = 8 * s + CC;
+  constexpr int kS = (CC % kQ4Ring) * kQ4Slot;
+  constexpr int kN = ((CC + 1) % kQ4Ring) * kQ4Slot;
   // the MFMA bias stays in its 16 VGPRs (instead of being rebuilt from scalars every step)
   asm volatile("" : "+v"(bias));
-  q4_wait<kQ4Ring - 3>(k.loads_a);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  q4_issue<(CC + kQ4Ring - 1) % 8>(k.smem + ((CC + kQ4Ring - 1) % kQ4Ring) * kQ4Slot, k.sbuf,
-                                   k.src, c + kQ4Ring - 1, k.c_end, k.wave, k.lane);
-  constexpr int kS = (CC % kQ4Ring) * kQ4Slot;
-  v4i a, b0, b1;
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.a), "+v"(f.b0), "+v"(f.b1)::"memory");
   v4f d0, d1, d2, d3, s0, s1, s2, s3;
   v2f p0, p1;
   const uint32_t ddp = k.dd + par, ssp = k.ss + par;
   asm volatile(
-      "ds_read_b128 %0, %13 offset:%17\n\t"
-      "ds_read_b128 %1, %14 offset:%18\n\t"
-      "ds_read_b128 %2, %14 offset:%19\n\t"
-      "ds_read_b64 %3, %16 offset:%20\n\t"
-      "ds_read_b64 %4, %16 offset:%21\n\t"
-      "ds_read_b128 %5, %15 offset:%22\n\t"
-      "ds_read_b128 %6, %15 offset:%23\n\t"
-      "ds_read_b128 %7, %15 offset:%24\n\t"
-      "ds_read_b128 %8, %15 offset:%25\n\t"
-      "ds_read_b128 %9, %15 offset:%26\n\t"
-      "ds_read_b128 %10, %15 offset:%27\n\t"
-      "ds_read_b128 %11, %15 offset:%28\n\t"
-      "ds_read_b128 %12, %15 offset:%29\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b0), "=&v"(b1), "=&v"(p0), "=&v"(p1), "=&v"(d0), "=&v"(d1), "=&v"(d2),
-        "=&v"(d3), "=&v"(s0), "=&v"(s1), "=&v"(s2), "=&v"(s3)
-      : "v"(k.aa), "v"(k.bb), "v"(ddp), "v"(ssp), "n"(kS + kQ4SlotA), "n"(kS + kQ4SlotB),
-        "n"(kS + kQ4SlotB + 1024), "n"(CC * 256), "n"(CC * 256 + 2048), "n"(CC * 128),
+      "ds_read_b64 %0, %11 offset:%12\n\t"
+      "ds_read_b64 %1, %11 offset:%13\n\t"
+      "ds_read_b128 %2, %10 offset:%14\n\t"
+      "ds_read_b128 %3, %10 offset:%15\n\t"
+      "ds_read_b128 %4, %10 offset:%16\n\t"
+      "ds_read_b128 %5, %10 offset:%17\n\t"
+      "ds_read_b128 %6, %10 offset:%18\n\t"
+      "ds_read_b128 %7, %10 offset:%19\n\t"
+      "ds_read_b128 %8, %10 offset:%20\n\t"
+      "ds_read_b128 %9, %10 offset:%21"
+      : "=&v"(p0), "=&v"(p1), "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3), "=&v"(s0), "=&v"(s1),
+        "=&v"(s2), "=&v"(s3)
+      : "v"(ddp), "v"(ssp), "n"(CC * 256), "n"(CC * 256 + 2048), "n"(CC * 128),
         "n"(CC * 128 + 16), "n"(CC * 128 + 32), "n"(CC * 128 + 48),
         "n"(kQ4SbDas + CC * 128), "n"(kQ4SbDas + CC * 128 + 16),
         "n"(kQ4SbDas + CC * 128 + 32), "n"(kQ4SbDas + CC * 128 + 48)
       : "memory");
+  // (the reads stay ahead of the MFMAs, so their registers are never the fragments' registers,
+  // which an MFMA may still be reading when a read lands)
+  __builtin_amdgcn_sched_barrier(0);
+  const v16i f0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a, f.b0, bias, 0, 0, 0);
+  const v16i f1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a, f.b1, bias, 0, 0, 0);
+  q4_issue<(CC + kQ4Ring - 1) % 8>(k.smem + ((CC + kQ4Ring - 1) % kQ4Ring) * kQ4Slot, k.sbuf,
+                                   k.src, c + kQ4Ring - 1, k.c_end, k.wave, k.lane);
+  q4_wait<kQ4Ring - 2>(k.loads_a);
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(p0), "+v"(p1), "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3), "+v"(s0), "+v"(s1),
+                 "+v"(s2), "+v"(s3)::"memory");
   const float dav[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
                          d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
   const float dsv[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                          s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
-  const v16i f0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b0, bias, 0, 0, 0);
-  const v16i f1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b1, bias, 0, 0, 0);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const v16i& f = u ? f1 : f0;
-    const v2f pr = u ? p1 : p0;
-    if (DOTS) {
-      const int g = k.lane >> 5;
-      const DotsRun d = dots_run<true>(k.dots, k.tok_base + 4 * g, k.col + u * kTile, k.nchunk, c);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int32_t* o = dots_slot(k.dots, d, r);
-        if (o) *o = f[r] - kBiasI;
-      }
-    } else {
-      const float nb = -kBiasF * pr.x;
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = __builtin_fmaf(__int_as_float(f[r]), pr.x, nb);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(t[r], dav[r], acc[u][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[u][r] = __builtin_fmaf(pr.y, dsv[r], acc[u][r]);
-    }
-    q4_order(acc[u]);  // keep the steps in program order (bounded register lifetimes)
-  }
+  q4_tile<DOTS>(k, c, 0, f0, p0, dav, dsv, acc[0]);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  q4_read_frags<kN>(k, f);
+  __builtin_amdgcn_sched_barrier(0);  // the reads go out before any of tile 1's rescale
+  q4_tile<DOTS>(k, c, 1, f1, p1, dav, dsv, acc[1]);
 }
 
 template <bool DOTS>
@@ -1680,19 +1715,22 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
   q4_issue<2>(smem + 2 * kQ4Slot, k.sbuf, k.src, c0 + 2, k.c_end, k.wave, k.lane);
   q4_wait<kQ4Ring - 2>(k.loads_a);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  Q4Frags f;
+  q4_read_frags<0>(k, f);
 
   for (uint32_t s = c0 / 8; s < k.c_end / 8; ++s) {
     const uint32_t par = (s & 1) * kQ4SbBytes;
-    q4_step<DOTS, 0>(k, s, par, bias, acc);
-    q4_step<DOTS, 1>(k, s, par, bias, acc);
-    q4_step<DOTS, 2>(k, s, par, bias, acc);
-    q4_step<DOTS, 3>(k, s, par, bias, acc);
-    q4_step<DOTS, 4>(k, s, par, bias, acc);
-    q4_step<DOTS, 5>(k, s, par, bias, acc);
-    q4_step<DOTS, 6>(k, s, par, bias, acc);
-    q4_step<DOTS, 7>(k, s, par, bias, acc);
+    q4_step<DOTS, 0>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 1>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 2>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 3>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 4>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 5>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 6>(k, s, par, bias, acc, f);
+    q4_step<DOTS, 7>(k, s, par, bias, acc, f);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing (unused) loads
+  // drain the trailing (unused) loads and fragment reads
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
   if (DOTS) return;
   const OutDst o = out_dst(tw, y, ldy, ws);
