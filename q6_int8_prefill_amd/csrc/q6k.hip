@@ -1323,7 +1323,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     for (int r = 0; r < 16; ++r) st.acc[u][r] = __builtin_fmaf(st.sb[u][r], st.d[r], st.acc[u][r]);
 
   // The workgroup's (32 kFTok)-token x 128-row output tile goes through LDS (the ring is free once
-  // every wave has passed the first barrier), so that each store or atomic instruction below
+  // every wave has passed the first barrier), so that each store instruction below
   // covers consecutive rows of one token instead of 64 scattered 4-row pieces.
   constexpr int kOutLd = 132;  // floats per token in LDS: 128 rows + 4 of padding
   static_assert(kTile * kFTok * kOutLd * 4 <= kFRing * kFSlot, "output tile fits the ring");
@@ -1507,8 +1507,8 @@ struct Q4Src {
 // Loads of chunk ci (ci % 8 == CI8) into `slot`; chunks past the end repeat the last one so each
 // wave issues at least 1 load per chunk (2 for waves 0 and 1).  At a super-block's first chunk the
 // per-super-block planes follow (extra loads, only for real chunks): they go to the buffers of the
-// super-block's parity, last read for super-block s - 2 (before the barrier of iteration 8s - 8);
-// they are issued at iteration 8s - 3.
+// super-block's parity, last read for super-block s - 2 (at the start of step 8s - 9, before that
+// step's meeting); they are issued in step 8s - 3 and land before the meeting of step 8s - 1.
 template <int CI8>
 __device__ __forceinline__ void q4_issue(uint8_t* slot, uint8_t* sbuf, const Q4Src& src,
                                          uint32_t ci, uint32_t c_end, int wave, int lane) {
