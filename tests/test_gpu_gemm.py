@@ -363,7 +363,7 @@ def test_workspace_rules_and_size():
     """Through the C ABI: the workspace q6k_gemm_workspace reports is one 32 KiB slab per piece of
     a split tile (at most one per workgroup slot); a call that needs one rejects a missing,
     misaligned or short workspace before launching anything, and a caller's workspace full of NaN
-    gives the same y, bit for bit, as one the binding allocates."""
+    gives the same y, bit for bit, as one the binding allocates.  The same for q4k_gemm."""
     import ctypes
     import torch
     import gpu_util
@@ -402,6 +402,34 @@ def test_workspace_rules_and_size():
         got = y.cpu().numpy()
         ref = gpu_util.gemm(xq, da, n, w, layout, m, k)
         np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # q4k_gemm: the same rules
+    raw4 = synthetic.weights_q4k(m, k, seed=73)
+    w4 = torch.empty(q6k.q4k_weight_bytes(m, k), dtype=torch.uint8, device=gpu_util.DEV)
+    q6k.q4k_expand_weights(torch.from_numpy(np.ascontiguousarray(raw4).reshape(-1)).to(
+        gpu_util.DEV), m, k, w4)
+    das = torch.empty_like(da)
+    q6k.q4k_act_sums(xq, da, n, k, das)
+    need = q6k.q4k_gemm_workspace(n, m, k)
+    y = torch.full((n, m), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+    ws = torch.full((need // 4 + 4,), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+
+    def call4(p, nb):
+        return L.q4k_gemm(xq.data_ptr(), xq.numel(), da.data_ptr(), da.numel() * 4,
+                          das.data_ptr(), das.numel() * 4, n, w4.data_ptr(), w4.numel(), m, k,
+                          y.data_ptr(), y.numel() * 4, m, p, nb,
+                          torch.cuda.current_stream().cuda_stream)
+    assert call4(None, 0) == -1
+    assert call4(ws.data_ptr() + 4, need) == -3
+    assert call4(ws.data_ptr(), need - 1) == -4
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+    assert call4(ws.data_ptr(), need) == 0
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    y2 = torch.full((n, m), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+    q6k.q4k_gemm(xq, da, das, n, w4, m, k, y2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
 
 def test_packed_layout_equals_expanded_bit_for_bit():
