@@ -97,6 +97,13 @@ __device__ __forceinline__ int quant_code(float x, float s, float r, bool fast) 
 
 // SUMS: also write das = da * S per (token, chunk), S the sum of the chunk's 32 codes, in the order
 // of da (the per-chunk activation sum the q4_K rescale needs next to da).
+// 16 bytes of a tensor read exactly once: a nontemporal load (streams at ~6.0 TB/s on MI355X
+// against ~5.4 for a plain load in a 2 GiB read probe).
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+
 template <bool SWIGLU, bool SUMS>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x,
                                                            const float* __restrict__ up,
@@ -126,8 +133,8 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restri
   for (int j = 0; j < 8; ++j) {
     const int64_t tok = T * kTile + 8 * wave + j;
     const int64_t off = (tok < n ? tok : n - 1) * ldx + cl * 32 + kk;
-    v[j] = *reinterpret_cast<const float4*>(x + off);
-    if (SWIGLU) u[j] = *reinterpret_cast<const float4*>(up + off);
+    v[j] = load_stream(x + off);
+    if (SWIGLU) u[j] = load_stream(up + off);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
