@@ -312,7 +312,9 @@ class Probes:
         dst = torch.empty(mib << 17, dtype=torch.int32, device="cuda")
         stream = torch.cuda.current_stream()
         res = {}
-        for mode, nbytes, moved in ((0, mib << 20, mib << 20), (1, mib << 19, mib << 20)):
+        names = {0: "read", 1: "copy", 2: "read_nontemporal"}
+        for mode, nbytes, moved in ((0, mib << 20, mib << 20), (2, mib << 20, mib << 20),
+                                    (1, mib << 19, mib << 20)):
             best = None
             for _ in range(6):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -325,7 +327,7 @@ class Probes:
                 torch.cuda.synchronize()
                 t = e0.elapsed_time(e1) * 1e-3
                 best = t if best is None else min(best, t)
-            res["read" if mode == 0 else "copy"] = {
+            res[names[mode]] = {
                 "bytes_moved": moved, "gbs": round(moved / best / 1e9, 1)}
         return res
 

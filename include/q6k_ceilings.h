@@ -49,7 +49,7 @@ enum {
   Q6C_TILEOP_FOLDED_PIPE = 2, /* FOLDED with each tile's MFMAs issued half a step ahead of its fold */
   Q6C_TILEOP_ZERO_C = 3       /* FOLDED's instruction mix, MFMA accumulator input an inline zero */
 };
-enum { Q6C_STREAM_READ = 0, Q6C_STREAM_COPY = 1 };
+enum { Q6C_STREAM_READ = 0, Q6C_STREAM_COPY = 1, Q6C_STREAM_READ_NT = 2 };
 enum {
   Q6C_OVERLAP_ROLES = 0,     /* 12 waves per CU: waves 0-3 MFMA only, waves 4-11 VALU only */
   Q6C_OVERLAP_SAME_WAVE = 1  /* 4 waves per CU: each alternates 1 MFMA and 8 independent VALU */
@@ -82,7 +82,8 @@ int q6c_overlap(int kind, int iters_mfma, int iters_valu, uint64_t* out, size_t 
                 void* stream);
 
 /* HBM stream over `bytes` (multiple of 16, 16-byte aligned): READ xors src into one word per
- * thread of 8 workgroups per CU (dst_bytes >= 4 * 256 * 8 * CUs), COPY copies src to dst. */
+ * thread of 8 workgroups per CU (dst_bytes >= 4 * 256 * 8 * CUs), READ_NT does the same with
+ * nontemporal loads (the prepass reads its input so), COPY copies src to dst. */
 int q6c_stream(int mode, const void* src, void* dst, size_t bytes, size_t dst_bytes,
                void* stream);
 

@@ -412,17 +412,28 @@ __global__ __launch_bounds__(768, 1) void overlap_kernel(int iters_mfma, int ite
 // ---------------------------------------------------------------------------------------------
 // HBM streams: grid-stride 16-byte accesses, 4 in flight per lane.
 // ---------------------------------------------------------------------------------------------
+typedef unsigned stream_v4u __attribute__((ext_vector_type(4)));
+
+// 16 bytes at src + i, with a plain or a nontemporal load
+template <bool NT>
+__device__ __forceinline__ stream_v4u stream_load(const uint4* src, int64_t i) {
+  const stream_v4u* p = reinterpret_cast<const stream_v4u*>(src + i);
+  return NT ? __builtin_nontemporal_load(p) : *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, int64_t n16,
                                                    uint32_t* __restrict__ sink) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   uint32_t x = 0;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const stream_v4u a = stream_load<NT>(src, i), b = stream_load<NT>(src, i + stride),
+                     c = stream_load<NT>(src, i + 2 * stride), d = stream_load<NT>(src, i + 3 * stride);
     x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
   for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+    const stream_v4u a = stream_load<NT>(src, i);
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
@@ -554,11 +565,16 @@ int q6c_stream(int mode, const void* src, void* dst, size_t bytes, size_t dst_by
   if (cus <= 0) return Q6K_EHIP;
   const int64_t blocks = (int64_t)cus * 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mode == Q6C_STREAM_READ) {
+  if (mode == Q6C_STREAM_READ || mode == Q6C_STREAM_READ_NT) {
     if (dst_bytes < (size_t)blocks * 256 * 4) return Q6K_ESIZE;
-    hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint4*>(src), (int64_t)(bytes / 16),
-                       static_cast<uint32_t*>(dst));
+    if (mode == Q6C_STREAM_READ)
+      hipLaunchKernelGGL(read_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s,
+                         static_cast<const uint4*>(src), (int64_t)(bytes / 16),
+                         static_cast<uint32_t*>(dst));
+    else
+      hipLaunchKernelGGL(read_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s,
+                         static_cast<const uint4*>(src), (int64_t)(bytes / 16),
+                         static_cast<uint32_t*>(dst));
   } else if (mode == Q6C_STREAM_COPY) {
     if (dst_bytes < bytes) return Q6K_ESIZE;
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
