@@ -1816,6 +1816,10 @@ q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitP
   const int64_t ntiles = gx * gy, slots = (int64_t)wg_per_cu * cus;
   const int64_t rem = ntiles % slots;
   int64_t pieces = rem ? std::min<int64_t>(slots / rem, nsb) : 1;
+  // A split saves each split tile nsb - ceil(nsb / pieces) super-blocks of time and costs the
+  // reducing kernel, 5-7 us or the time of 2-3 super-blocks: below 3 saved it does not pay (64 x
+  // 256 x 512, two super-blocks: layout 2 9.1 us unsplit against 13.4 us in two pieces).
+  if (pieces >= 2 && nsb - (nsb + pieces - 1) / pieces < 3) pieces = 1;
   if (pieces < 2) pieces = 1;
   sp->n_full = pieces > 1 ? ntiles - rem : ntiles;
   sp->pieces = pieces;

@@ -291,13 +291,14 @@ def test_folded_split_k_pieces(n, m, k):
 def test_gemm_whole_tiles_ragged_rows(layout, ldy):
     """Enough tiles (1664) that most are computed whole, with m not a multiple of 4 and leading
     dimensions that do (4100) and do not (4094, 4097) allow 16-byte stores: every store path of
-    the epilogues (vector, scalar, partial last row group, and the split pieces of layout 2), with
-    the columns past m untouched."""
+    the epilogues (vector, scalar, partial last row group) and of the split pieces' reduction,
+    with the columns past m untouched."""
     import torch
     import gpu_util
     import q6_int8_prefill_amd as q6k
-    n, m, k = 3314, 4094, 512
+    n, m, k = 3314, 4094, 2048
     print(f"whole tiles layout={layout} ldy={ldy}", flush=True)
+    assert q6k.q6k_gemm_workspace(n, m, k, layout) > 0  # the last round is split
     raw = synthetic.weights(m, k, seed=ldy, sc_lo=-128, sc_hi=127)
     x = synthetic.activations(n, k, seed=ldy + 1, kind="outlier")
     xq, da, w = prepare(x, raw, m, layout)
@@ -322,8 +323,10 @@ def test_gemm_partly_split_grid(layout):
     exactly the split tiles of the GEMM's own tile order (y starts as NaN: every output is checked
     finite, sampled tokens against the oracle)."""
     import gpu_util
-    n, m, k = 2176, 4096, 512
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 2176, 4096, 2048
     print(f"partly split grid layout={layout}", flush=True)
+    assert q6k.q6k_gemm_workspace(n, m, k, layout) > 0
     raw = synthetic.weights(m, k, seed=55, sc_lo=-128, sc_hi=127)
     x = synthetic.activations(n, k, seed=56, kind="outlier")
     xq, da, w = prepare(x, raw, m, layout)

@@ -192,8 +192,10 @@ def test_partly_split_grid():
     """1088 output tiles on a 768-slot device: 768 computed whole, the other 320 split along k,
     their pieces reduced from workspace slabs; every output finite (y starts as NaN), sampled
     tokens against the oracle."""
-    n, m, k = 2176, 4096, 512
+    import q6_int8_prefill_amd as q6k
+    n, m, k = 2176, 4096, 2048
     print("q4k partly split grid", flush=True)
+    assert q6k.q4k_gemm_workspace(n, m, k) > 0
     raw = synthetic.weights_q4k(m, k, seed=61)
     x = synthetic.activations(n, k, seed=62, kind="outlier")
     xq, da, das = prep_acts(x)
