@@ -444,7 +444,7 @@ class Gemm:
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the GEMM runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU split is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
     if args.ceilings:

@@ -1,5 +1,5 @@
-"""bench.py's contract on the host: more than one GPU is refused with a message (this build runs
-on one GPU), and the HBM traffic it reports comes from the committed counter summary only while
+"""bench.py's contract on the host: more than one GPU is refused with a message (the GEMM runs on
+one GPU), and the HBM traffic it reports comes from the committed counter summary only while
 that summary was taken on the current kernel code."""
 import os
 import subprocess
