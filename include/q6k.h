@@ -50,7 +50,7 @@
  *                  k = 32c + 16*(b/8) + 8g + b%8
  *     scales f32 : at byte offset MP*k, float ((R*nchunk + c)*32 + p)*2 + h = d*sc[2c + h] of row
  *                  32R + p (sub-block index counted along the whole row)
- *   layout 0 (Q6K_LAYOUT_PACKED), 6 bits per weight plus 4 scale bytes per 32 weights:
+ *   layout 0 (Q6K_LAYOUT_PACKED), 6 bits per weight plus layout 1's scale plane:
  *     codes      : 12 bytes at ((R*nchunk + c)*64 + l)*12 for row 32R + p, three little-endian
  *                  words X, Y, Z; with a_e (e = 0..7) the 6-bit codes at k = 32c + 8g + e and
  *                  b_e those at k = 32c + 16 + 8g + e, byte t (t = 0..3) of
@@ -58,8 +58,8 @@
  *                    Y = a_{t+4} << 2 | ((b_{t+4} >> 2) & 3)
  *                    Z = b_t << 2     | (b_{t+4} >> 4)
  *                  (the GEMM turns a byte s into (s & 0xFC) ^ 0x80 = 4 * (q - 32))
- *     scales     : at byte offset MP*k*3/4, 4 bytes at ((R*nchunk + c)*32 + p)*4:
- *                  int8 sc[2c], int8 sc[2c+1], f16 d (little-endian) of row 32R + p
+ *     scales f32 : at byte offset MP*k*3/4, as layout 1's: float ((R*nchunk + c)*32 + p)*2 + h
+ *                  = d*sc[2c + h] of row 32R + p
  *   layout 2 (Q6K_LAYOUT_FOLDED), the int8 sub-block scale applied to the codes ahead of time:
  *     v = sc[k/16] * (q - 32) (in [-4064, 4096]) of row 32R + p at k = 32c + 16*(b/8) + 8g + b%8
  *     is stored as two int8 digits, lo = ((v + 32) mod 64) - 32 and hi = (v - lo) / 64:
@@ -126,7 +126,7 @@ size_t q6k_weight_bytes(int64_t m, int64_t k, int layout);
 
 /* Load-time weight preparation.  Input: raw q6_K blocks, row j's super-block b at byte
  * (j*(k/256) + b)*210 (byte map of "r38 ..." sec. 2.1; 2-byte aligned: Q6K_EALIGN otherwise).  Output: layout 0 (6-bit
- * codes regrouped for wide loads plus the raw scale bytes; expanded to centered int8 inside the
+ * codes regrouped for wide loads plus the f32 d*sc plane; expanded to centered int8 inside the
  * GEMM, "r41 ..." sec. 2), layout 1 (centered int8 plane plus f32 d*sc plane, "r53 ..." sec.
  * 2.3 and the W_dsc plane of "r42 ..." sec. 3.2) or layout 2 (two int8 digit planes of
  * sc * (q - 32) plus one f32 d per super-block).  Padding rows are written as zeros. */

@@ -335,9 +335,13 @@ __global__ __launch_bounds__(256) void expand_kernel(const uint8_t* __restrict__
       dst[1] = w1;
       dst[2] = w2;
     }
-    uint32_t s = (uint32_t)(uint8_t)sc0 | ((uint32_t)(uint8_t)sc1 << 8) | ((uint32_t)dbits << 16);
-    if (R * kTile + p >= m) s = 0;
-    reinterpret_cast<uint32_t*>(scales)[tc * 32 + p] = s;
+    // the (d*sc0, d*sc1) plane of layout 1
+    const float d = __half2float(__ushort_as_half(dbits));
+    float2 sp;
+    sp.x = d * (float)sc0;  // exact: an 11-bit significand times an 8-bit integer
+    sp.y = d * (float)sc1;
+    if (R * kTile + p >= m) sp.x = sp.y = 0.0f;
+    reinterpret_cast<float2*>(scales)[tc * 32 + p] = sp;
   }
 }
 
@@ -600,11 +604,10 @@ constexpr int kSlotD = 2048;     // 2 token tiles x 32 da f32
 constexpr int kSlotB = 2304;     // 4 row tiles x 1 KiB of centered int8 B fragments
 constexpr int kSlotS = 6400;     // 4 row tiles x 32 rows x (dsc0, dsc1) f32
 constexpr int kSlotRawB = 7424;  // layout 0: 4 row tiles x 768 B of packed 6-bit codes
-constexpr int kSlotRawS = 10496; // layout 0: 4 row tiles x 32 raw scale words
 
 template <int LAYOUT>
 struct SlotSize {
-  static constexpr int value = LAYOUT == Q6K_LAYOUT_EXPANDED ? 7424 : 11008;
+  static constexpr int value = LAYOUT == Q6K_LAYOUT_EXPANDED ? 7424 : 10496;
 };
 // LDS slots per workgroup (loads run kRing-1 chunks ahead), sized so that Q6K_WG_PER_CU
 // workgroups fit in the 160 KiB of LDS of a CU.
@@ -647,13 +650,11 @@ template <int LAYOUT>
 __device__ __forceinline__ void issue_chunk(uint8_t* slot, const GemmSrc& src, uint32_t c, int wave,
                                             int lane) {
   const uint32_t l16 = lane * 16;
-  if (LAYOUT == Q6K_LAYOUT_EXPANDED) {
+  if (LAYOUT == Q6K_LAYOUT_EXPANDED)
     bdma16(src.b, l16, c * 1024, slot + kSlotB + wave * 1024);
-    if (lane < 16) bdma16(src.s, l16, c * 256, slot + kSlotS + wave * 256);
-  } else {
-    if (lane < 48) bdma16(src.b, l16, c * 768, slot + kSlotRawB + wave * 768);
-    if (lane < 8) bdma16(src.s, l16, c * 128, slot + kSlotRawS + wave * 128);
-  }
+  else if (lane < 48)
+    bdma16(src.b, l16, c * 768, slot + kSlotRawB + wave * 768);
+  if (lane < 16) bdma16(src.s, l16, c * 256, slot + kSlotS + wave * 256);
   if (wave < kWgTokTiles) {
     bdma16(src.a, l16, c * 1024, slot + kSlotA + wave * 1024);
     if (lane < 8) bdma16(src.d, l16, c * 128, slot + kSlotD + wave * 128);
@@ -673,47 +674,36 @@ __device__ __forceinline__ void wait_chunks(bool loads_a) {
 // which the LDS instructions take as an immediate offset (no per-chunk address arithmetic).
 struct GemmLanes {
   uint32_t aa, dd, bb, ss;         // reads: A fragment, da, B fragments, scales
-  uint32_t raw, rsc, bdst, sdst;   // layout 0 expand: packed codes and scale words in, B and
-                                   // (d*sc0, d*sc1) pairs out (row tile `wave`)
+  uint32_t raw, bdst;              // layout 0 expand: packed codes in, B fragments out (row
+                                   // tile `wave`)
 };
 
-// Layout 0: this lane's packed codes and its row's raw scale word of row tile `wave` in the slot at
-// byte offset OFF.  No wait: the caller waits (with the registers as operands) after other work.
+// Layout 0: this lane's packed codes of row tile `wave` in the slot at byte offset OFF.  No wait:
+// the caller waits (with the registers as operands) after other work.
 struct RawCodes {
-  uint32_t x, y, z, s;
+  uint32_t x, y, z;
 };
 template <int OFF>
 __device__ __forceinline__ void expand_read(const GemmLanes& L, RawCodes& r) {
   asm volatile(
-      "ds_read_b32 %0, %4 offset:%6\n\t"
-      "ds_read_b32 %1, %4 offset:%7\n\t"
-      "ds_read_b32 %2, %4 offset:%8\n\t"
-      "ds_read_b32 %3, %5 offset:%6"
-      : "=&v"(r.x), "=&v"(r.y), "=&v"(r.z), "=&v"(r.s)
-      : "v"(L.raw), "v"(L.rsc), "n"(OFF), "n"(OFF + 4), "n"(OFF + 8)
+      "ds_read_b32 %0, %3 offset:%4\n\t"
+      "ds_read_b32 %1, %3 offset:%5\n\t"
+      "ds_read_b32 %2, %3 offset:%6"
+      : "=&v"(r.x), "=&v"(r.y), "=&v"(r.z)
+      : "v"(L.raw), "n"(OFF), "n"(OFF + 4), "n"(OFF + 8)
       : "memory");
 }
 
 // Layout 0: write row tile `wave` of the slot at OFF as B fragments of 4 x the centered int8
-// codes and, from lanes 0-31 (one row each), the pair (d*sc0, d*sc1).  (Also staging the bias
-// products -1.5*2^23 d*sc, which saves the steps four multiplies, measured 1.5 % slower: more LDS
-// traffic.)
+// codes.  (Its (d*sc0, d*sc1) pairs arrive by direct-to-LDS load, as on layout 1.)
 template <int OFF>
-__device__ __forceinline__ void expand_write(const GemmLanes& L, const RawCodes& r, int lane) {
+__device__ __forceinline__ void expand_write(const GemmLanes& L, const RawCodes& r) {
   v4u b;
   b.x = center4x4(r.x);
   b.y = center4x4(r.y);
   b.z = center4x4(r.z);
   b.w = fourth4x4(r.x, r.y, r.z);
   asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(L.bdst), "v"(b), "n"(OFF) : "memory");
-  if (lane < 32) {
-    // d*sc, exact: an 11-bit significand times an int8
-    const float d = __half2float(__ushort_as_half((unsigned short)(r.s >> 16)));
-    v2f v;
-    v.x = d * (float)(int8_t)(r.s & 255);
-    v.y = d * (float)(int8_t)((r.s >> 8) & 255);
-    asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(L.sdst), "v"(v), "n"(OFF) : "memory");
-  }
 }
 
 // The MFMAs of one 32x32 output tile for one chunk (halves 0 and 1).
@@ -861,8 +851,8 @@ __device__ __forceinline__ void gemm_step(const GemmCtx& k, uint32_t c, float (&
                                 k.nchunk, k.dots);
   if (!SUBDOTS) pin_acc(acc[0]);
   if (kPacked) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.s));
-    expand_write<kNext>(k.lanes, raw, k.lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z));
+    expand_write<kNext>(k.lanes, raw);
   }
   // 6. chunk c+1 complete in LDS for every wave (loads landed, layout 0's expand written)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -931,7 +921,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
     k.src.s = make_rsrc(wscales + (k.R0 + wave) * nchunk * 256, nchunk * 256);
   } else {
     k.src.b = make_rsrc(wcodes + (k.R0 + wave) * nchunk * 768, nchunk * 768);
-    k.src.s = make_rsrc(wscales + (k.R0 + wave) * nchunk * 128, nchunk * 128);
+    k.src.s = make_rsrc(wscales + (k.R0 + wave) * nchunk * 256, nchunk * 256);
   }
   const int p = lane & 31, g = lane >> 5;
   k.lanes.aa = lds_addr(smem + kSlotA + k.tt * 1024 + lane * 16);
@@ -939,9 +929,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   k.lanes.bb = lds_addr(smem + kSlotB + k.rp * 2048 + lane * 16);
   k.lanes.ss = lds_addr(smem + kSlotS + k.rp * 512 + p * 8);
   k.lanes.raw = lds_addr(smem + kSlotRawB + wave * 768 + lane * 12);
-  k.lanes.rsc = lds_addr(smem + kSlotRawS + wave * 128 + p * 4);
   k.lanes.bdst = lds_addr(smem + kSlotB + wave * 1024 + lane * 16);
-  k.lanes.sdst = lds_addr(smem + kSlotS + wave * 256 + lane * 8);
 
   v16i bias;
 #pragma unroll
@@ -962,8 +950,8 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   if (kPacked) {
     RawCodes raw;
     expand_read<0>(k.lanes, raw);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z), "+v"(raw.s));
-    expand_write<0>(k.lanes, raw, lane);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(raw.x), "+v"(raw.y), "+v"(raw.z));
+    expand_write<0>(k.lanes, raw);
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   GemmFrags f;
@@ -1786,7 +1774,7 @@ bool weight_sizes(int64_t m, int64_t k, int layout, size_t* codes, size_t* scale
     *scales = (size_t)mp * (size_t)(k / 16) * sizeof(float);
   } else {
     *codes = (size_t)mp * (size_t)k / 4 * 3;
-    *scales = (size_t)mp * (size_t)(k / 32) * 4;
+    *scales = (size_t)mp * (size_t)(k / 16) * sizeof(float);
   }
   return true;
 }

@@ -40,7 +40,7 @@ def untile_expanded(buf, m, k):
 
 
 def untile_packed(buf, m, k):
-    """layout 0 bytes -> (6-bit codes uint8 [MP][k], sc int8 [MP][k/16], d-bits uint16 [MP][k/32]).
+    """layout 0 bytes -> (6-bit codes uint8 [MP][k], dsc f32 [MP][k/16]).
 
     Per lane three words X, Y, Z: byte t of X / Y / Z holds a_t / a_{t+4} / b_t in bits 2-7 and
     bits 0-1 / 2-3 / 4-5 of b_{t+4} in bits 0-1."""
@@ -58,11 +58,8 @@ def untile_packed(buf, m, k):
     bb[..., 4:8] = (x & 3) | ((y & 3) << 2) | ((z & 3) << 4)
     full = np.stack([a, bb], axis=4)  # T,c,g,p,h,e
     codes = full.transpose(0, 3, 1, 4, 2, 5).reshape(mp, k).astype(np.uint8)
-    s = b[nb: nb + mp * nchunk * 4].reshape(mp // 32, nchunk, 32, 4).transpose(0, 2, 1, 3)
-    s = s.reshape(mp, nchunk, 4)
-    sc = s[:, :, 0:2].reshape(mp, k // 16).view(np.int8)
-    dbits = s[:, :, 2:4].copy().view("<u2").reshape(mp, nchunk)
-    return codes, sc, dbits
+    sc = b[nb: nb + mp * (k // 16) * 4].view(np.float32).reshape(mp // 32, nchunk, 32, 2)
+    return codes, sc.transpose(0, 2, 1, 3).reshape(mp, k // 16)
 
 
 def untile_folded(buf, m, k):

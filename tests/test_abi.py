@@ -66,8 +66,8 @@ def test_size_queries():
     assert q6k.q6k_act_bytes(0, 256) == (0, 0)
     assert q6k.q6k_act_bytes(5, 300) == (0, 0)
     assert q6k.q6k_weight_bytes(40, 512, 1) == 128 * 512 * 5 // 4
-    assert q6k.q6k_weight_bytes(40, 512, 0) == 128 * 512 * 7 // 8
-    assert q6k.q6k_weight_bytes(4096, 11008, 0) == 4096 * 11008 * 7 // 8
+    assert q6k.q6k_weight_bytes(40, 512, 0) == 128 * 512
+    assert q6k.q6k_weight_bytes(4096, 11008, 0) == 4096 * 11008
     assert q6k.q6k_weight_bytes(40, 512, 2) == 128 * 512 * 2 + 128 * 2 * 4
     assert q6k.q6k_weight_bytes(4096, 11008, 2) == 4096 * 11008 * 2 + 4096 * 43 * 4
     assert q6k.q6k_weight_bytes(40, 512, 3) == 0
@@ -145,7 +145,7 @@ def gemm_args(xq=FAKE, xqb=BIG, da=FAKE, dab=BIG, n=4, w=FAKE, wb=BIG, layout=1,
     (dict(dab=128 * 8 * 4 - 1), -4),
     (dict(wb=128 * 256 * 5 // 4 - 1), -4),             # layout 1: 1.25 B per weight
     (dict(layout=2, wb=128 * 256 * 2 + 128 * 4 - 1), -4),
-    (dict(layout=0, wb=128 * 256 * 7 // 8 - 1), -4),
+    (dict(layout=0, wb=128 * 256 - 1), -4),                # layout 0: 1 B per weight
     (dict(yb=4 * (3 * 8 + 8) - 1), -4),                # y: (n-1)*ldy + m floats
     (dict(yb=4 * (3 * 10 + 8) - 1, ldy=10), -4),
     (dict(ldy=(1 << 40) + 1), -4),
@@ -158,7 +158,7 @@ def test_gemm_one_byte_short_weights():
     # every other buffer at its exact size, the weights one byte short (a passing call would
     # launch on these fake pointers, so only the failing side is checked)
     L = lib()
-    for layout, wb in ((0, 128 * 256 * 7 // 8), (1, 128 * 256 * 5 // 4), (2, 128 * 256 * 2 + 128 * 4)):
+    for layout, wb in ((0, 128 * 256), (1, 128 * 256 * 5 // 4), (2, 128 * 256 * 2 + 128 * 4)):
         assert L.q6k_gemm(*gemm_args(layout=layout, wb=wb - 1, xqb=128 * 256, dab=4096,
                                      yb=4 * 32)) == -4
 

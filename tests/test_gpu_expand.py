@@ -40,14 +40,13 @@ def check_packed(raw, m, k):
     import gpu_util
     print(f"expand layout 0 m={m} k={k}", flush=True)
     w = gpu_util.expand(raw, m, k, 0).cpu().numpy()
-    codes, sc, dbits = untile_packed(w, m, k)
-    wc, sc_ref, _ = oracle.decode(raw, m, k)
+    codes, dsc = untile_packed(w, m, k)
+    wc, sc, d = oracle.decode(raw, m, k)
     np.testing.assert_array_equal(codes[:m].astype(np.int32) - 32, wc.astype(np.int32))
-    np.testing.assert_array_equal(sc[:m], sc_ref)
-    rawd = raw.reshape(m, k // 256, 210)[:, :, 208:210].copy().view("<u2").reshape(m, k // 256)
-    np.testing.assert_array_equal(dbits[:m], np.repeat(rawd, 8, axis=1))
-    assert (codes[m:] == 0).all() and (sc[m:] == 0).all() and (dbits[m:] == 0).all()
-    assert w.size == round_up(m, 128) * k * 7 // 8
+    want = (np.repeat(d, 16, axis=1) * sc.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(dsc[:m].view(np.uint32), want.view(np.uint32))
+    assert (codes[m:] == 0).all() and (dsc[m:] == 0).all()
+    assert w.size == round_up(m, 128) * k
 
 
 def check_folded(raw, m, k):
