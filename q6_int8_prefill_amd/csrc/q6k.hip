@@ -561,7 +561,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 // Staging: a ring of kRing LDS slots, one 32-k chunk of the workgroup's operands per slot.  Each
 // wave fills its share of a slot with gfx950 direct-to-LDS loads through buffer resources
 // (buffer_load_dwordx4 ... lds, 16 bytes per lane, no registers): row tile w's weight codes and
-// scales, and, for waves 0 and 1, token tile w's activations and da.  Loads run kRing-1 chunks
+// (d*sc0, d*sc1) pairs, and, for waves 0 and 1, token tile w's activations and da.  Loads run kRing-1 chunks
 // ahead of the compute.  Step c (chunk c, slot c % kRing) of a wave, entered with chunk c complete
 // in LDS for every wave and this wave's A and B fragments of chunk c on their way to registers:
 //   1. wait for the fragments, start the LDS reads of chunk c's da and scale pairs, start the
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 //      for the da and scale reads;
 //   4. layout 0: start the LDS reads of this wave's packed codes of chunk c+1; rescale tile 0 of
 //      chunk c (the reads land meanwhile); expand row tile w of chunk c+1 into B fragments of
-//      4 x the centered int8 codes and the pair (d*sc0, d*sc1) in its slot;
+//      4 x the centered int8 codes in its slot;
 //   5. meet: every wave's share of chunk c+1 is in its slot (loads landed, layout 0 expanded),
 //      and every wave is done with chunk c's da and scales;
 //   6. start the LDS reads of chunk c+1's fragments, then rescale tile 1 of chunk c (the reads
