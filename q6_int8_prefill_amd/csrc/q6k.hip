@@ -1609,8 +1609,7 @@ template <bool DOTS, int CC>
 __device__ __forceinline__ void q4_step(const Q4Ctx& k, uint32_t s, uint32_t par, v16i& bias,
                                         float (&acc)[2][16], Q4Frags& f) {
   const uint32_t c = 8 * s + CC;
-  constexpr int kS = (CC % kQ4Ring) * kQ4Slot;
-  constexpr int kN = ((CC + 1) % kQ4Ring) * kQ4Slot;
+  constexpr int kN = ((CC + 1) % kQ4Ring) * kQ4Slot;  // slot of chunk c + 1
   // the MFMA bias stays in its 16 VGPRs (instead of being rebuilt from scalars every step)
   asm volatile("" : "+v"(bias));
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.a), "+v"(f.b0), "+v"(f.b1)::"memory");
