@@ -7,7 +7,7 @@ before timing starts.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1|2] [--layouts 0,1,2]
                     [--workload NAME] [--weights q6k|q4k] [--cold] [--swiglu]
-                    [--no-cpu-baseline] [--copy-probe-mib MIB] [--ceilings]
+                    [--no-cpu-baseline] [--copy-probe-mib MIB] [--ceilings] [--timeline]
 
 Timing protocol (all with HIP events recorded on the stream the kernels run on):
   * ms_per_step: K steps of prepass + GEMM of the headline layout (--layout) back to back, events
@@ -33,6 +33,11 @@ write-back instead).  --swiglu replaces the prepass by the fused producer q6k_sw
 reading the two SwiGLU factors, and also times the unfused pair (q6k_swiglu_f32 writing h, then
 q6k_quantize_act).  --weights q4k runs the q4_K variant on the same shapes: step =
 q4k_quantize_act (codes, da and das in one pass) + q4k_gemm.
+
+--timeline runs the GEMMs through libq6k_timeline.so (same kernels, each workgroup also writing
+where and when it ran) and prints, per layout, tile durations, each XCD's shader clock and last
+end, CU hand-over gaps, the start lags of workgroups sharing an operand tile, and an L2 model's
+fabric fetch beside the committed FETCH_SIZE figure (use a few --steps: the model is Python).
 
 --ceilings runs the microbenchmarks of libq6k_ceilings.so instead (MFMA issue rates, vector-ALU
 issue rates at 1, 2, 4 and 8 waves per SIMD, the GEMMs' tile operation without memory traffic,
@@ -98,6 +103,9 @@ def parse(argv=None):
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ceilings", action="store_true",
                     help="run the unit microbenchmarks instead of the GEMM")
+    ap.add_argument("--timeline", action="store_true",
+                    help="record per-workgroup timelines of --steps GEMM launches per layout "
+                         "with libq6k_timeline.so instead of timing")
     return ap.parse_args(argv)
 
 
@@ -154,17 +162,30 @@ def kernel_source_digest():
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def counter_traffic(workload, layout):
-    """HBM-side bytes of one GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
-    or None if there is none for this workload or the kernel code changed since it was taken."""
+def _counter_entry(workload, layout):
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_code_sha256_16") != kernel_source_digest():
+        return None, None
+    return rec, rec.get("layouts", {}).get(str(layout))
+
+
+def counter_fetch(workload, layout):
+    """FETCH_SIZE bytes of one GEMM launch from the committed summary (scaled as its traffic
+    figure is), or None."""
+    rec, entry = _counter_entry(workload, layout)
+    if entry is None:
         return None
-    entry = rec.get("layouts", {}).get(str(layout))
+    return int(entry["gemm_fetch_size_kib"] * 1024 * rec["fetch_scale"])
+
+
+def counter_traffic(workload, layout):
+    """HBM-side bytes of one GEMM launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None if there is none for this workload or the kernel code changed since it was taken."""
+    _, entry = _counter_entry(workload, layout)
     return None if entry is None else int(entry["traffic_bytes"])
 
 
@@ -441,6 +462,63 @@ class Gemm:
         return float(self.n) * self.m * per_chunk * (self.k // 32)
 
 
+# ------------------------------------------------------------------------------------------------
+# Workgroup timelines (libq6k_timeline.so)
+# ------------------------------------------------------------------------------------------------
+def run_timeline(args, torch, acts, gemms, layouts):
+    """--timeline: after --warmup launches of each layout, --steps blocks of --block back-to-back
+    launches of each (interleaved, the starting layout rotating), the last launch of every block
+    recorded; per layout the summary of the recorded launch of median span and the L2 model of
+    every recorded launch, beside the committed FETCH_SIZE."""
+    import numpy as np
+
+    from q6_int8_prefill_amd import timeline as tl
+
+    rec = tl.Recorder()
+    try:
+        for _ in range(args.warmup):
+            for L in layouts:
+                gemms[L].launch()
+        torch.cuda.synchronize()
+        runs = {L: [] for L in layouts}
+        for r in range(args.steps):
+            for j in range(len(layouts)):
+                L = layouts[(r + j) % len(layouts)]
+                rec.clear()
+                # --block launches back to back, as the timed blocks run them: every workgroup
+                # rewrites its record, so the records read are the last launch's
+                for _ in range(args.block):
+                    gemms[L].launch()
+                torch.cuda.synchronize()
+                runs[L].append(tl.decode(rec.read()))
+    finally:
+        rec.close()
+    out = {"mode": "timeline", "workload": args.workload, "recorded_launches": args.steps,
+           "block": args.block, "warmup": args.warmup, "layouts": {}}
+    for L in layouts:
+        g = gemms[L]
+        # 64-token x 128-row output tiles; tokens are padded to 128 in the activation buffers
+        nsb, gx, gy = g.k // 256, 2 * -(-g.n // 128), -(-g.m // 128)
+        scale_words = 2 if acts.das is not None else 1
+        # one 64-token tile's or one 128-row tile's bytes per super-block, as stored
+        act_block = (acts.xq.numel() + acts.da.numel() * 4 * scale_words) / (gx * nsb)
+        wgt_block = g.w.numel() / (gy * nsb)
+        spans = [float(d["end"].max()) for d in runs[L]]
+        med = runs[L][int(np.argsort(spans)[len(spans) // 2])]
+        model = [tl.l2_model(d, act_block, wgt_block) for d in runs[L]]
+        out["layouts"][str(L)] = {
+            "kernel": KERNEL_NAMES[L],
+            "span_us": [round(v, 2) for v in spans],
+            "median_launch": tl.summarize(med),
+            "l2_model": {
+                "l2_bytes": tl.L2_BYTES, "act_block_bytes": act_block,
+                "wgt_block_bytes": wgt_block,
+                "fetch_bytes_mean": int(np.mean([v["fetch_bytes"] for v in model])),
+                "distinct_block_bytes": model[0]["distinct_block_bytes"]},
+            "counter_fetch_bytes": counter_fetch(args.workload, L)}
+    print(json.dumps(out))
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -450,6 +528,10 @@ def main(argv=None):
     if args.ceilings:
         run_ceilings(args)
         return
+    if args.timeline and args.workload == "sweep32":
+        print("bench.py: --timeline records one GEMM's launches; pick a single-GEMM workload",
+              file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -503,6 +585,9 @@ def main(argv=None):
         units.append((acts, {L: Gemm(q6k, torch, acts, raw_d, m, L, y, dev) for L in layouts}))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
+    if args.timeline:
+        run_timeline(args, torch, units[0][0], units[0][1], layouts)
+        return
 
     # load-time weight preparation of the first matrix in the headline layout, timed once
     a0, g0 = units[0][0], units[0][1][head]

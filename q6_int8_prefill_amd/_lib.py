@@ -14,56 +14,73 @@ lib_path = os.path.join(_HERE, "_build", "libq6k.so")
 if not os.path.exists(lib_path):
     raise ImportError(f"libq6k.so is not built ({lib_path}); run __graft_entry__.build()")
 
-_lib = ctypes.CDLL(lib_path)
 _p, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
-_lib.q6k_act_bytes.restype = _sz
-_lib.q6k_act_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
-_lib.q6k_quantize_act.restype = _int
-_lib.q6k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
-_lib.q6k_swiglu_quantize_act.restype = _int
-_lib.q6k_swiglu_quantize_act.argtypes = [_p, _p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
-_lib.q6k_swiglu_f32.restype = _int
-_lib.q6k_swiglu_f32.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p]
-_lib.q6k_weight_bytes.restype = _sz
-_lib.q6k_weight_bytes.argtypes = [_i64, _i64, _int]
-_lib.q6k_expand_weights.restype = _int
-_lib.q6k_expand_weights.argtypes = [_p, _i64, _i64, _int, _p, _sz, _p]
-_lib.q6k_gemm.restype = _int
-_lib.q6k_gemm.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64, _p,
-                          _sz, _p]
-_lib.q6k_gemm_noalloc.restype = _int
-_lib.q6k_gemm_noalloc.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64,
-                                  _p]
-_lib.q6k_gemm_workspace.restype = _int
-_lib.q6k_gemm_workspace.argtypes = [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]
 _WIN = [_i64, _i64, _i64, _i64]
-_lib.q6k_gemm_subdots.restype = _int
-_lib.q6k_gemm_subdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + _WIN + \
-    [_p, _sz, _p]
-_lib.q6k_gemm_chunkdots.restype = _int
-_lib.q6k_gemm_chunkdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + _WIN + \
-    [_p, _sz, _p]
-_lib.q4k_weight_bytes.restype = _sz
-_lib.q4k_weight_bytes.argtypes = [_i64, _i64]
-_lib.q4k_expand_weights.restype = _int
-_lib.q4k_expand_weights.argtypes = [_p, _i64, _i64, _p, _sz, _p]
-_lib.q4k_quantize_act.restype = _int
-_lib.q4k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p, _sz, _p]
-_lib.q4k_act_sums.restype = _int
-_lib.q4k_act_sums.argtypes = [_p, _p, _i64, _i64, _p, _sz, _p]
-_lib.q4k_gemm.restype = _int
-_lib.q4k_gemm.argtypes = [_p, _sz, _p, _sz, _p, _sz, _i64, _p, _sz, _i64, _i64, _p, _sz, _i64,
-                          _p, _sz, _p]
-_lib.q4k_gemm_workspace.restype = _int
-_lib.q4k_gemm_workspace.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
-_lib.q4k_gemm_dots.restype = _int
-_lib.q4k_gemm_dots.argtypes = [_p, _sz, _i64, _p, _sz, _i64, _i64] + _WIN + [_p, _sz, _p]
-_lib.q4k_launches.restype = ctypes.c_uint64
-_lib.q4k_launches.argtypes = []
-_lib.q6k_strerror.restype = ctypes.c_char_p
-_lib.q6k_strerror.argtypes = [_int]
-_lib.q6k_stats.restype = None
-_lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+
+
+def _declare(lib):
+    """Result and argument types of every call of q6k.h and q4k.h on a loaded library."""
+    lib.q6k_act_bytes.restype = _sz
+    lib.q6k_act_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.q6k_quantize_act.restype = _int
+    lib.q6k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
+    lib.q6k_swiglu_quantize_act.restype = _int
+    lib.q6k_swiglu_quantize_act.argtypes = [_p, _p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p]
+    lib.q6k_swiglu_f32.restype = _int
+    lib.q6k_swiglu_f32.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p]
+    lib.q6k_weight_bytes.restype = _sz
+    lib.q6k_weight_bytes.argtypes = [_i64, _i64, _int]
+    lib.q6k_expand_weights.restype = _int
+    lib.q6k_expand_weights.argtypes = [_p, _i64, _i64, _int, _p, _sz, _p]
+    lib.q6k_gemm.restype = _int
+    lib.q6k_gemm.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz, _i64, _p,
+                             _sz, _p]
+    lib.q6k_gemm_noalloc.restype = _int
+    lib.q6k_gemm_noalloc.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64, _p, _sz,
+                                     _i64, _p]
+    lib.q6k_gemm_workspace.restype = _int
+    lib.q6k_gemm_workspace.argtypes = [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]
+    lib.q6k_gemm_subdots.restype = _int
+    lib.q6k_gemm_subdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + \
+        _WIN + [_p, _sz, _p]
+    lib.q6k_gemm_chunkdots.restype = _int
+    lib.q6k_gemm_chunkdots.argtypes = [_p, _sz, _p, _sz, _i64, _p, _sz, _int, _i64, _i64] + \
+        _WIN + [_p, _sz, _p]
+    lib.q4k_weight_bytes.restype = _sz
+    lib.q4k_weight_bytes.argtypes = [_i64, _i64]
+    lib.q4k_expand_weights.restype = _int
+    lib.q4k_expand_weights.argtypes = [_p, _i64, _i64, _p, _sz, _p]
+    lib.q4k_quantize_act.restype = _int
+    lib.q4k_quantize_act.argtypes = [_p, _i64, _i64, _i64, _p, _sz, _p, _sz, _p, _sz, _p]
+    lib.q4k_act_sums.restype = _int
+    lib.q4k_act_sums.argtypes = [_p, _p, _i64, _i64, _p, _sz, _p]
+    lib.q4k_gemm.restype = _int
+    lib.q4k_gemm.argtypes = [_p, _sz, _p, _sz, _p, _sz, _i64, _p, _sz, _i64, _i64, _p, _sz, _i64,
+                             _p, _sz, _p]
+    lib.q4k_gemm_workspace.restype = _int
+    lib.q4k_gemm_workspace.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+    lib.q4k_gemm_dots.restype = _int
+    lib.q4k_gemm_dots.argtypes = [_p, _sz, _i64, _p, _sz, _i64, _i64] + _WIN + [_p, _sz, _p]
+    lib.q4k_launches.restype = ctypes.c_uint64
+    lib.q4k_launches.argtypes = []
+    lib.q6k_strerror.restype = ctypes.c_char_p
+    lib.q6k_strerror.argtypes = [_int]
+    lib.q6k_stats.restype = None
+    lib.q6k_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    return lib
+
+
+_lib = _declare(ctypes.CDLL(lib_path))
+
+
+def use_library(path):
+    """Send every call of this module to the library at `path` from now on, and return its
+    handle.  For libq6k_timeline.so: a second build of the same source, with the same calls,
+    whose GEMM workgroups also record where and when they ran (include/q6k_timeline.h)."""
+    global _lib
+    _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
 
 EXPORTS = ("q6k_act_bytes", "q6k_quantize_act", "q6k_swiglu_quantize_act", "q6k_swiglu_f32",
            "q6k_weight_bytes", "q6k_expand_weights",

@@ -26,6 +26,9 @@
 
 #include "q4k.h"
 #include "q6k.h"
+#ifdef Q6K_TIMELINE
+#include "q6k_timeline.h"
+#endif
 
 namespace {
 
@@ -399,6 +402,42 @@ struct TileWork {
   bool split;       // a piece of a split tile: store into workspace slab `slab`
   uint32_t slab;    // pid - n_full for a piece
 };
+
+// Workgroup timeline, compiled in only by the instrumented build of this file (Q6K_TIMELINE
+// defined, libq6k_timeline.so): the first thread of GEMM workgroup b writes record b of the
+// last launch, eight words: start and end on the 100 MHz constant clock, start and end shader
+// cycles, the XCD (high word) and HW_ID register (low word), the tile (bx, by), its k range of
+// super-blocks (s0, s1) and whether it is a split-k piece.  The product build has no trace of it.
+#ifdef Q6K_TIMELINE
+constexpr int kTimelineWgs = 16384;
+__device__ uint64_t q6k_timeline_rec[kTimelineWgs * 8];
+struct WgStamp {
+  uint64_t t, c;
+};
+__device__ __forceinline__ WgStamp wg_stamp() {
+  return WgStamp{__builtin_amdgcn_s_memrealtime(), __builtin_amdgcn_s_memtime()};
+}
+__device__ __forceinline__ void wg_record(const WgStamp& s, const TileWork& tw) {
+  if (threadIdx.x != 0 || blockIdx.x >= (uint32_t)kTimelineWgs) return;
+  uint32_t xcc, hw;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  const uint64_t t1 = __builtin_amdgcn_s_memrealtime(), c1 = __builtin_amdgcn_s_memtime();
+  uint64_t* o = q6k_timeline_rec + 8 * (uint64_t)blockIdx.x;
+  o[0] = s.t;
+  o[1] = t1;
+  o[2] = s.c;
+  o[3] = c1;
+  o[4] = ((uint64_t)xcc << 32) | hw;
+  o[5] = (uint64_t)tw.bx | ((uint64_t)tw.by << 32);
+  o[6] = (uint64_t)tw.s0 | ((uint64_t)tw.s1 << 32);
+  o[7] = tw.split ? 1 : 0;
+}
+#else
+struct WgStamp {};
+__device__ __forceinline__ WgStamp wg_stamp() { return WgStamp{}; }
+__device__ __forceinline__ void wg_record(const WgStamp&, const TileWork&) {}
+#endif
 
 constexpr int kSlabTok = 64;                     // tokens of an output tile (every GEMM)
 constexpr int64_t kSlabFloats = kSlabTok * 128;  // one output tile, f32 [64][128]
@@ -897,6 +936,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   static_assert(Q6K_WG_PER_CU * kRing * kSlot <= 160 * 1024, "LDS budget");
   static_assert(kRing * kSlot + 1024 < 65536, "slot offsets fit the LDS immediate offset");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kSlot];
+  const WgStamp stamp = wg_stamp();
   GemmCtx k;
   k.smem = smem;
   k.lane = threadIdx.x & 63;
@@ -978,6 +1018,7 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
       if (tok < n) o.p[(tok - o.tok0) * o.ld + (mcol - o.row0)] = acc[u][r] * out_scale;
     }
   }
+  wg_record(stamp, tw);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1232,6 +1273,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     int64_t nchunk, float* __restrict__ y, int64_t ldy, int vec_store, float* __restrict__ ws,
     DotsOut dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot];
+  const WgStamp stamp = wg_stamp();
   const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
   const bool split = tw.split;
   const uint32_t bx = tw.bx, by = tw.by;
@@ -1368,6 +1410,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
       }
     }
   }
+  wg_record(stamp, tw);
 }
 
 
@@ -1663,6 +1706,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
     int64_t nchunk, float* __restrict__ y, int64_t ldy, float* __restrict__ ws, DotsOut dots,
     uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQ4Ring * kQ4Slot + 2 * kQ4SbBytes];
+  const WgStamp stamp = wg_stamp();
   Q4Ctx k;
   k.smem = smem;
   k.sbuf = smem + kQ4Ring * kQ4Slot;
@@ -1738,6 +1782,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
       if (tok < n) o.p[(tok - o.tok0) * o.ld + (mcol - o.row0)] = acc[u][r];
     }
   }
+  wg_record(stamp, tw);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -2332,5 +2377,29 @@ void q6k_stats(uint64_t out[3]) {
   if (!out) return;
   for (int i = 0; i < 3; ++i) out[i] = g_launches[i].load(std::memory_order_relaxed);
 }
+
+#ifdef Q6K_TIMELINE
+int64_t q6k_timeline_capacity(void) { return kTimelineWgs; }
+
+q6k_status q6k_timeline_clear(void* stream) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(q6k_timeline_rec)) != hipSuccess) return Q6K_EHIP;
+  return hipMemsetAsync(p, 0, sizeof(q6k_timeline_rec), (hipStream_t)stream) == hipSuccess
+             ? Q6K_OK
+             : Q6K_EHIP;
+}
+
+q6k_status q6k_timeline_read(uint64_t* records, int64_t max_wgs) {
+  if (!records || max_wgs < 0) return Q6K_EINVAL;
+  const int64_t n = std::min<int64_t>(max_wgs, kTimelineWgs);
+  if (n == 0) return Q6K_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(q6k_timeline_rec)) != hipSuccess) return Q6K_EHIP;
+  return hipMemcpy(records, p, (size_t)n * 8 * sizeof(uint64_t), hipMemcpyDeviceToHost) ==
+                 hipSuccess
+             ? Q6K_OK
+             : Q6K_EHIP;
+}
+#endif
 
 }  // extern "C"

@@ -33,6 +33,28 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(L, name), name
 
 
+def test_timeline_library_exports_its_declared_symbols():
+    # the workgroup-timeline build of the same source: every product call plus the three calls of
+    # its own header; the product library has none of those
+    text = open(os.path.join(ROOT, "include", "q6k_timeline.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(q6k_timeline_[a-z_]+)\s*\(", text)))
+    assert names == ["q6k_timeline_capacity", "q6k_timeline_clear", "q6k_timeline_read"]
+    T = ctypes.CDLL(os.path.join(ROOT, "q6_int8_prefill_amd", "_build", "libq6k_timeline.so"))
+    for name in declared_functions() + names:
+        assert hasattr(T, name), name
+    for name in names:
+        assert not hasattr(lib(), name), name
+    T.q6k_timeline_capacity.restype = ctypes.c_int64
+    assert T.q6k_timeline_capacity() == 16384
+    # host-side argument checks (no device needed)
+    T.q6k_timeline_read.restype = ctypes.c_int
+    T.q6k_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    assert T.q6k_timeline_read(None, 4) == -1
+    assert T.q6k_timeline_read(FAKE, -1) == -1
+    assert T.q6k_timeline_read(FAKE, 0) == 0
+
+
 def test_ceilings_library_exports_its_declared_symbols():
     # the measurement library beside the product: every q6c_ call its header declares
     text = open(os.path.join(ROOT, "include", "q6k_ceilings.h")).read()
