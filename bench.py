@@ -8,6 +8,7 @@ before timing starts.  Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout 0|1|2] [--layouts 0,1,2]
                     [--workload NAME] [--weights q6k|q4k] [--cold] [--swiglu]
                     [--no-cpu-baseline] [--copy-probe-mib MIB] [--ceilings] [--timeline]
+                    [--activations normal|outlier|swiglu|zero]
 
 Timing protocol (all with HIP events recorded on the stream the kernels run on):
   * ms_per_step: K steps of prepass + GEMM of the headline layout (--layout) back to back, events
@@ -32,12 +33,16 @@ holding clean lines: evicting the write's dirty lines inside the timed span woul
 write-back instead).  --swiglu replaces the prepass by the fused producer q6k_swiglu_quantize_act
 reading the two SwiGLU factors, and also times the unfused pair (q6k_swiglu_f32 writing h, then
 q6k_quantize_act).  --weights q4k runs the q4_K variant on the same shapes: step =
-q4k_quantize_act (codes, da and das in one pass) + q4k_gemm.
+q4k_quantize_act (codes, da and das in one pass) + q4k_gemm.  --activations replaces the
+workload's activation distribution (named in `config`): 'zero' runs every launch unchanged on
+all-zero operands, which shows how far the sustained clock depends on the data.
 
 --timeline runs the GEMMs through libq6k_timeline.so (same kernels, each workgroup also writing
 where and when it ran) and prints, per layout, tile durations, each XCD's shader clock and last
 end, CU hand-over gaps, the start lags of workgroups sharing an operand tile, and an L2 model's
-fabric fetch beside the committed FETCH_SIZE figure (use a few --steps: the model is Python).
+fabric fetch (for the recorded schedule, and for the same tiles with each XCD's concurrent
+workgroups in lockstep) beside the committed FETCH_SIZE figure (use a few --steps: the model is
+Python).
 
 --ceilings runs the microbenchmarks of libq6k_ceilings.so instead (MFMA issue rates, vector-ALU
 issue rates at 1, 2, 4 and 8 waves per SIMD, the GEMMs' tile operation without memory traffic,
@@ -93,6 +98,10 @@ def parse(argv=None):
     ap.add_argument("--workload", default="ffn_down_n3314")
     ap.add_argument("--weights", default="q6k", choices=["q6k", "q4k"],
                     help="weight format: q6_K (the headline) or the q4_K variant")
+    ap.add_argument("--activations", default=None,
+                    choices=["normal", "outlier", "swiglu", "zero"],
+                    help="activation distribution (default: the workload's own); 'zero' runs the "
+                         "same launches on all-zero operands, for the clock's data dependence")
     ap.add_argument("--cold", action="store_true")
     ap.add_argument("--swiglu", action="store_true",
                     help="feed the GEMM from the fused SwiGLU -> int8 producer (gate, up inputs)")
@@ -474,6 +483,7 @@ def run_timeline(args, torch, acts, gemms, layouts):
 
     from q6_int8_prefill_amd import timeline as tl
 
+    acts.quantize()  # the GEMMs' int8 operand and its scales
     rec = tl.Recorder()
     try:
         for _ in range(args.warmup):
@@ -506,6 +516,7 @@ def run_timeline(args, torch, acts, gemms, layouts):
         spans = [float(d["end"].max()) for d in runs[L]]
         med = runs[L][int(np.argsort(spans)[len(spans) // 2])]
         model = [tl.l2_model(d, act_block, wgt_block) for d in runs[L]]
+        locked = tl.l2_model(tl.lockstep(med), act_block, wgt_block)
         out["layouts"][str(L)] = {
             "kernel": KERNEL_NAMES[L],
             "span_us": [round(v, 2) for v in spans],
@@ -514,6 +525,7 @@ def run_timeline(args, torch, acts, gemms, layouts):
                 "l2_bytes": tl.L2_BYTES, "act_block_bytes": act_block,
                 "wgt_block_bytes": wgt_block,
                 "fetch_bytes_mean": int(np.mean([v["fetch_bytes"] for v in model])),
+                "fetch_bytes_lockstep": locked["fetch_bytes"],
                 "distinct_block_bytes": model[0]["distinct_block_bytes"]},
             "counter_fetch_bytes": counter_fetch(args.workload, L)}
     print(json.dumps(out))
@@ -528,6 +540,10 @@ def main(argv=None):
     if args.ceilings:
         run_ceilings(args)
         return
+    if args.activations and (args.swiglu or args.workload == "sweep32"):
+        print("bench.py: --activations sets the activations of a single-GEMM workload; the SwiGLU "
+              "producer and the sweep draw their own", file=sys.stderr)
+        sys.exit(2)
     if args.timeline and args.workload == "sweep32":
         print("bench.py: --timeline records one GEMM's launches; pick a single-GEMM workload",
               file=sys.stderr)
@@ -577,7 +593,7 @@ def main(argv=None):
             x_d, up_d = torch.from_numpy(gate).to(dev), torch.from_numpy(up).to(dev)
             x = None  # the CPU baseline quantizes x; here the input is the factor pair
         else:
-            x = synthetic.activations(n, k, spec["seed"], spec["x"])
+            x = synthetic.activations(n, k, spec["seed"], args.activations or spec["x"])
             x_d = torch.from_numpy(x).to(dev)
         raw_d = torch.from_numpy(raw.reshape(-1)).to(dev)
         acts = Acts(q6k, torch, x_d, n, k, dev, up_d=up_d, q4=q4)
@@ -749,6 +765,8 @@ def main(argv=None):
     else:
         config = {"workload": args.workload, "n": g0.n, "m": g0.m, "k": g0.k, "layout": head,
                   "cold": args.cold, "step": "q6k_quantize_act + q6k_gemm"}
+        if args.activations:
+            config.update(activations=args.activations)
         if args.swiglu:
             config.update(producer="fused SwiGLU (gate, up f32 inputs)",
                           step="q6k_swiglu_quantize_act + q6k_gemm")

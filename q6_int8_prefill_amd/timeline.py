@@ -9,7 +9,9 @@ functions below are plain numpy over those records:
     in time the workgroups that share an operand tile start;
   * `l2_model` - the bytes each XCD's L2 fetches across the memory fabric if it held the most
     recently used operand blocks (one tile's slice of one 256-k super-block) up to its capacity,
-    each block requested when the workgroup's progress, taken as linear in time, reaches it.
+    each block requested when the workgroup's progress, taken as linear in time, reaches it;
+  * `lockstep` - the same launch rescheduled so that the workgroups running together on an XCD
+    walk k together (what the model gives for it bounds what synchronizing them could save).
 """
 import ctypes
 import os
@@ -142,6 +144,33 @@ def summarize(d):
             "token_tile": [round(v / per_sb, 2) for v in _pct(tok_lag, (50, 90))]
             if len(tok_lag) else None},
     }
+
+
+def lockstep(d):
+    """The same workgroups on the same XCDs, rescheduled so that those running together walk k
+    together: each XCD's workgroups, in their recorded start order, run in rounds of the XCD's
+    slot count (the workgroups that started with the launch); a round starts when the previous
+    one's last workgroup ends, and every workgroup advances at the launch's median rate per
+    super-block.  Returns a copy of `d` with the new start and end times."""
+    e = dict(d)
+    nsb = (d["s1"] - d["s0"]).astype(np.float64)
+    whole = ~d["split"]
+    rate = float(np.median((d["end"] - d["start"])[whole] / nsb[whole])) if whole.any() else \
+        float(np.median((d["end"] - d["start"]) / nsb))
+    start, end = np.zeros(len(nsb)), np.zeros(len(nsb))
+    first = d["start"].min() if len(nsb) else 0.0
+    for x in np.unique(d["xcd"]):
+        idx = np.nonzero(d["xcd"] == x)[0]
+        idx = idx[np.argsort(d["start"][idx], kind="stable")]
+        slots = max(1, int((d["start"][idx] - first < 1.0).sum()))
+        t = 0.0
+        for r in range(0, len(idx), slots):
+            grp = idx[r:r + slots]
+            start[grp] = t
+            end[grp] = t + rate * nsb[grp]
+            t = end[grp].max()
+    e["start"], e["end"] = start, end
+    return e
 
 
 def l2_model(d, act_block, wgt_block, l2_bytes=L2_BYTES):

@@ -50,7 +50,10 @@ def activations(n, k, seed, kind="normal"):
     normal  : N(0,1)
     outlier : N(0,1) with round(0.01*k) seeded channels scaled by 20
     swiglu  : a * silu(b), a, b ~ N(0,1), silu evaluated in f64
+    zero    : all zeros (the degenerate input: every chunk's codes and scale are 0)
     """
+    if kind == "zero":
+        return np.zeros((n, k), dtype=np.float32)
     rng = np.random.Generator(np.random.PCG64(seed + 10**6))
     if kind == "normal":
         return rng.standard_normal(size=(n, k), dtype=np.float32)

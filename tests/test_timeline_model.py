@@ -87,3 +87,24 @@ def test_l2_model_split_piece_covers_its_own_superblocks():
             (1, rec(8.0, 12.0, 1, 0, 1, 0, 0, 2, 4, split=True))]
     m = tl.l2_model(tl.decode(records(rows)), act_block=100, wgt_block=1000, l2_bytes=1 << 20)
     assert m["fetch_bytes"] == 4 * 1100
+
+
+def test_lockstep_brings_sharing_workgroups_together():
+    # one XCD with 2 slots: the second round's two workgroups share row tile 2, but the slot of
+    # the slower first-round workgroup frees 2 us (1 super-block) later.  With room for about one
+    # super-block of their operands the late one refetches each weight block; in lockstep (both
+    # rounds at the median 2 us per super-block) the pair shares them.
+    rows = [(0, rec(0.0, 8.0, 1, 0, 1, 0, 0, 0, 4)),
+            (1, rec(0.0, 10.0, 1, 0, 2, 1, 1, 0, 4)),
+            (2, rec(8.0, 16.0, 1, 0, 1, 2, 2, 0, 4)),
+            (3, rec(10.0, 18.0, 1, 0, 2, 3, 2, 0, 4))]
+    d = tl.decode(records(rows))
+    e = tl.lockstep(d)
+    assert list(e["start"]) == [0.0, 0.0, 8.0, 8.0] and list(e["end"]) == [8.0, 8.0, 16.0, 16.0]
+    before = tl.l2_model(d, act_block=100, wgt_block=1000, l2_bytes=1300)
+    after = tl.l2_model(e, act_block=100, wgt_block=1000, l2_bytes=1300)
+    assert after["distinct_block_bytes"] == before["distinct_block_bytes"] == 4 * 4 * 100 + \
+        3 * 4 * 1000
+    # lockstep: every block once; recorded: row tile 2's weights twice
+    assert after["fetch_bytes"] == after["distinct_block_bytes"]
+    assert before["fetch_bytes"] == after["fetch_bytes"] + 4 * 1000
