@@ -210,7 +210,8 @@ VALU_KINDS = {0: "v_fma_f32", 1: "v_fmac_f32", 2: "v_add_f32", 3: "v_mul_f32",
 TILEOP_KINDS = {0: ("folded: 2 x v_mfma_i32_32x32x32_i8 + 48 VALU", 48),
                 1: ("two halves: 2 x v_mfma_i32_32x32x16_i8 + 64 VALU", 64),
                 2: ("folded, MFMAs issued half a step ahead of the fold", 48),
-                3: ("folded mix, MFMA accumulator input an inline zero (cost of reading C)", 48)}
+                3: ("folded mix, MFMA accumulator input an inline zero (cost of reading C)", 48),
+                4: ("f16 digits: 4 x v_mfma_f32_32x32x16_f16 chained from zero + 16 VALU", 16)}
 
 
 class Probes:
@@ -389,7 +390,7 @@ def run_ceilings(args):
     out = {"mode": "ceilings", "n_gpus": 1, "wall_clock_khz": pr.wall_khz,
            "mfma": each(pr.mfma, *[(k, w) for k in (0, 1, 2, 3) for w in (1, 2)]),
            "valu": each(pr.valu, *[(k, w) for k in (0, 1, 2, 3, 4, 5) for w in (1, 2, 4, 8)]),
-           "tileop": each(pr.tileop, *[(k, w) for k in (0, 1, 2, 3) for w in (1, 2, 3, 4)]),
+           "tileop": each(pr.tileop, *[(k, w) for k in (0, 1, 2, 3, 4) for w in (1, 2, 3, 4)]),
            "overlap": pr.overlap(),
            "hbm": pr.hbm(),
            "spec": {"int8_dense_tops": INT8_PEAK_TOPS, "hbm_gbs": HBM_PEAK_GBS,

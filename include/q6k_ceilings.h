@@ -47,7 +47,9 @@ enum {
   Q6C_TILEOP_FOLDED = 0,     /* per tile and chunk: 2 x 32x32x32 int8 MFMA + 48 VALU (fold, rescale) */
   Q6C_TILEOP_HALVES = 1,     /* per tile and chunk: 2 x 32x32x16 int8 MFMA + 64 VALU (two halves) */
   Q6C_TILEOP_FOLDED_PIPE = 2, /* FOLDED with each tile's MFMAs issued half a step ahead of its fold */
-  Q6C_TILEOP_ZERO_C = 3       /* FOLDED's instruction mix, MFMA accumulator input an inline zero */
+  Q6C_TILEOP_ZERO_C = 3,      /* FOLDED's instruction mix, MFMA accumulator input an inline zero */
+  Q6C_TILEOP_F16 = 4          /* per tile and chunk: 4 x 32x32x16 f16 MFMA on the digit planes as
+                                 f16 integers, chained from zero (E exact in f32) + 16 VALU (da) */
 };
 enum { Q6C_STREAM_READ = 0, Q6C_STREAM_COPY = 1, Q6C_STREAM_READ_NT = 2 };
 enum {

@@ -262,6 +262,33 @@ __global__ __launch_bounds__(256, 2) void tileop_kernel(int iters, uint64_t* out
       }
       asm volatile("" : "+v"(da0), "+v"(da1));
     }
+  } else if (KIND == Q6C_TILEOP_F16) {
+    // the folded operation on f16 MFMAs: the activation codes and the two digit planes (lo and
+    // 64*hi) as f16 integers, two K=16 halves each, four v_mfma_f32_32x32x16_f16 per tile and
+    // chunk chained from an inline zero (every partial sum an integer below 2^24, so E is exact
+    // in f32 with no fold), then one fma with da per output
+    v8h fa0, fa1, fl, fh;
+    for (int i = 0; i < 8; ++i) {
+      fa0[i] = (_Float16)(float)((lane * 7 + i * 13) % 255 - 127);
+      fa1[i] = (_Float16)(float)((lane * 11 + i * 5) % 255 - 127);
+      fl[i] = (_Float16)(float)((lane * 3 + i * 17) % 64 - 32);
+      fh[i] = (_Float16)(float)(64 * ((lane * 5 + i * 3) % 33 - 16));
+    }
+    const v16f zero = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v8h bl = u ? fh : fl, bh = u ? fl : fh;
+        v16f e = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa0, bl, zero, 0, 0, 0);
+        e = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa1, bl, e, 0, 0, 0);
+        e = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa0, bh, e, 0, 0, 0);
+        e = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa1, bh, e, 0, 0, 0);
+        const float dav = u ? da1 : da0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sb[u][r] = __builtin_fmaf(e[r], dav, sb[u][r]);
+      }
+      asm volatile("" : "+v"(da0), "+v"(da1));
+    }
   } else if (KIND == Q6C_TILEOP_FOLDED) {
     v16i bias_lo, bias_hi;
     for (int r = 0; r < 16; ++r) {
@@ -532,6 +559,8 @@ int q6c_tileop(int kind, int iters, int waves_per_simd, uint64_t* out, size_t ou
       return launch_probe(tileop_kernel<Q6C_TILEOP_ZERO_C>, iters, waves_per_simd, out, out_bytes, stream);
     case Q6C_TILEOP_FOLDED_PIPE:
       return launch_probe(tileop_kernel<Q6C_TILEOP_FOLDED_PIPE>, iters, waves_per_simd, out, out_bytes, stream);
+    case Q6C_TILEOP_F16:
+      return launch_probe(tileop_kernel<Q6C_TILEOP_F16>, iters, waves_per_simd, out, out_bytes, stream);
     default:
       return Q6K_EINVAL;
   }
