@@ -806,7 +806,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": value, "peak": INT8_PEAK_TOPS,
                      "unit": "TOPS", "frac": round(value / INT8_PEAK_TOPS, 4),
                      "traffic": (counter_traffic(args.workload, head)
-                                 if not (sweep or args.cold or q4 or args.swiglu) else None),
+                                 if not (sweep or args.cold or args.swiglu) else None),
                      "kernel": KERNEL_NAMES[head],
                      "algorithmic_per_launch": {"int8_ops": g0.ops(), "bytes": g0.bytes()}},
         # the unit that binds this method's GEMM: its f32 rescale on the vector ALU
