@@ -143,11 +143,16 @@ q6k_status q6k_expand_weights(const void* w_raw, int64_t m, int64_t k, int layou
  * per workgroup slot of the GPU; when the last round would leave slots idle, its tiles are split
  * along k into pieces of whole super-blocks.  Each piece stores its partial sums into a 32 KiB
  * slab of the workspace, and a second kernel, enqueued right after the GEMM on the same stream,
- * adds each split tile's slabs in piece order into y.  The order of every addition is fixed, so
- * y is the same bit for bit from run to run (and in a captured graph's replays).  The workspace
- * is scratch: its contents are not needed before the call and mean nothing after it; two calls
- * in flight at once (on different streams) need workspaces of their own, and two that write the
- * same y concurrently race.
+ * adds each split tile's slabs in piece order into y.  On layout 2, when whole rounds precede
+ * the split tiles, their pieces are graded (piece i of P weighs P - i) and handed out in the
+ * order the workgroups start, largest first, through a 4-byte claim counter in the workspace
+ * after the slabs (the launch sets it to 0 as it starts and the second kernel again after it),
+ * so that the workgroups that start last take the smallest pieces.  A piece's k-range and slab
+ * depend only on (tile, piece), and the order of every addition is fixed, so y is the same bit
+ * for bit from run to run (and in a captured graph's replays).  The workspace is scratch: its
+ * contents are not needed before the call and mean nothing after it; two calls in flight at
+ * once (on different streams) need workspaces of their own, and two that write the same y
+ * concurrently race.
  *   xq, da  : outputs of q6k_quantize_act for the same n, k; xq_bytes, da_bytes at least what
  *             q6k_act_bytes returns (the kernels read whole padded tiles)
  *   w       : output of q6k_expand_weights for the same m, k and `layout`; w_bytes at least
@@ -168,8 +173,9 @@ q6k_status q6k_gemm(const void* xq, size_t xq_bytes, const float* da, size_t da_
  * serving loops, harnesses that forbid allocation): q6k_gemm with its split-k workspace taken
  * from a static device array of the library instead of a caller buffer.  Same arguments (minus
  * the workspace), kernels, work split and results (bit for bit) as q6k_gemm.  The array holds
- * 24 MiB (768 slabs of 32 KiB: 3 workgroup slots per compute unit on a 256-CU device, the most
- * any layout needs there); a problem that needs more returns Q6K_ESCRATCH and launches nothing.
+ * 24 MiB + 256 bytes (768 slabs of 32 KiB: 3 workgroup slots per compute unit on a 256-CU
+ * device, the most any layout needs there, and the claim counter); a problem that needs more
+ * returns Q6K_ESCRATCH and launches nothing.
  * Each GPU holds its own copy, from the first call on it until the process ends; the call
  * itself allocates and frees nothing.  Every call on one GPU uses that GPU's one array (no part
  * of it needs clearing: a call reads only what it wrote), so calls that overlap on one GPU (on
@@ -181,7 +187,8 @@ q6k_status q6k_gemm_noalloc(const void* xq, size_t xq_bytes, const float* da, si
 /* Workspace bytes that q6k_gemm needs for this n, m, k and layout on the device current on the
  * calling thread (the work split depends on its compute-unit count): 32 KiB per piece of a
  * split tile, at most 32 KiB x the workgroup slots of the device (2 per compute unit on layout
- * 2, 3 on layouts 0 and 1: 16 and 24 MiB on a 256-CU device); 0 when no tile is split or the
+ * 2, 3 on layouts 0 and 1: 16 and 24 MiB on a 256-CU device), plus 256 bytes for the claim
+ * counter when layout 2 hands its pieces out in start order; 0 when no tile is split or the
  * problem is empty.  Shape errors as q6k_gemm; Q6K_EHIP if the device cannot be queried;
  * *bytes is 0 on any error. */
 q6k_status q6k_gemm_workspace(int64_t n, int64_t m, int64_t k, int layout, size_t* bytes);

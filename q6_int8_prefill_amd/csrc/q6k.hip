@@ -373,7 +373,8 @@ __device__ __forceinline__ uint32_t fourth4x4(uint32_t x, uint32_t y, uint32_t z
 // the GPU (workgroups per CU x CUs); when the last round would leave slots idle, its tiles are
 // split along k into `pieces` pieces of whole super-blocks that run side by side.  Workgroups
 // 0 .. n_full-1 take whole tiles and store them into y; workgroup n_full + i takes piece
-// i % pieces of split tile i / pieces and stores its partial sums into slab i of the caller's
+// i % pieces of split tile i / pieces (or, on layout 2 behind whole rounds, the piece it claims
+// as it starts: tile_work) and stores its partial sums into that piece's slab of the caller's
 // workspace (one 64 x 128 f32 tile per piece), and split_reduce_kernel, launched next on the same
 // stream, adds each tile's slabs in piece order into y.  The sum's order is fixed, so every output
 // is the same bit for bit from run to run.
@@ -512,28 +513,73 @@ __device__ __forceinline__ int32_t* dots_slot(const DotsOut& w, const DotsRun& d
 // The result is uniform across the workgroup; the divisions in it run on the vector ALU, so each
 // field goes through readfirstlane to tell the compiler (and keep everything derived from it in
 // scalar registers).
+// Super-block bound j of a split tile's pieces.  grade 0: equal pieces.  grade G >= 1: piece i
+// weighs P - i + G - 1, so piece 0 is the largest and the sizes fall off linearly; the host
+// checks that every piece keeps at least one super-block.
+__host__ __device__ inline int64_t tail_bound(int64_t nsb, uint32_t P, uint32_t grade,
+                                              uint32_t j) {
+  if (grade == 0) return nsb * j / P;
+  const int64_t g = (int64_t)grade - 1;
+  const int64_t wj = (int64_t)j * (P + g) - (int64_t)j * (j - 1) / 2;
+  const int64_t wp = (int64_t)P * (P + g) - (int64_t)P * (P - 1) / 2;
+  return nsb * wj / wp;
+}
+
+// `pieces` carries the piece count P in its low 16 bits and the grade in the next 8.  With a
+// grade and a workspace, the tail is claimed: the split tiles' workgroups start as slots free up
+// behind the whole rounds, at different times on different XCDs and CUs, and each takes the next
+// claim c of the launch at its start (one fetch-and-add on the claim word that follows the slabs
+// in the workspace) -- piece c / nsplit (the largest pieces first) of split tile c % nsplit -- so
+// the workgroups that start last get the smallest pieces and the launch's last ends draw
+// together.  A piece's k-range and slab depend only on (tile, piece), never on which workgroup
+// ran it, so the reduction's sums are the same bit for bit.  The claim word starts each launch at
+// 0: workgroup 0, a whole tile (the host claims only behind a whole round, so every split tile's
+// workgroup is dispatched after a workgroup of the first round has run a whole tile), stores 0
+// as it starts, and split_reduce_kernel, next on the stream, stores 0 again after the launch.
 template <bool XCD_ORDER>
 __device__ __forceinline__ TileWork tile_work(uint32_t pid, uint32_t gx, uint32_t gy,
-                                              uint32_t n_full, uint32_t pieces, int64_t nsb) {
+                                              uint32_t n_full, uint32_t pieces, int64_t nsb,
+                                              float* ws) {
+  __shared__ uint32_t claim_lds;
   TileWork w;
+  const uint32_t P = pieces & 0xFFFF, grade = (pieces >> 16) & 0xFF;
+  const bool claimed = grade && ws;
   w.split = pid >= n_full;
-  const uint32_t tile = w.split ? n_full + (pid - n_full) / pieces : pid;
-  const int64_t piece = w.split ? (pid - n_full) % pieces : 0;
-  const int64_t npieces = w.split ? pieces : 1;
+  uint32_t tile = pid, piece = 0;
+  const uint32_t nsplit = gx * gy - n_full;
+  uint32_t* claim = claimed ? reinterpret_cast<uint32_t*>(ws + (int64_t)nsplit * P * kSlabFloats)
+                            : nullptr;
+  if (claimed && pid == 0 && threadIdx.x == 0)
+    __hip_atomic_store(claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (w.split) {
+    uint32_t c = pid - n_full;
+    if (claimed) {
+      if (threadIdx.x == 0)
+        claim_lds = __hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) %
+                    (nsplit * P);
+      __syncthreads();
+      c = claim_lds;
+      tile = n_full + c % nsplit;
+      piece = c / nsplit;
+    } else {
+      tile = n_full + c / P;
+      piece = c % P;
+    }
+  }
   if (XCD_ORDER) {
     tile_of(tile, gx, gy, &w.bx, &w.by);
   } else {
     w.bx = tile % gx;
     w.by = tile / gx;
   }
-  w.s0 = nsb * piece / npieces;
-  w.s1 = nsb * (piece + 1) / npieces;
+  w.s0 = w.split ? tail_bound(nsb, P, grade, piece) : 0;
+  w.s1 = w.split ? tail_bound(nsb, P, grade, piece + 1) : nsb;
   w.bx = __builtin_amdgcn_readfirstlane(w.bx);
   w.by = __builtin_amdgcn_readfirstlane(w.by);
   w.s0 = __builtin_amdgcn_readfirstlane((int)w.s0);
   w.s1 = __builtin_amdgcn_readfirstlane((int)w.s1);
   w.split = __builtin_amdgcn_readfirstlane((int)w.split) != 0;
-  w.slab = __builtin_amdgcn_readfirstlane(w.split ? pid - n_full : 0u);
+  w.slab = __builtin_amdgcn_readfirstlane(w.split ? (tile - n_full) * P + piece : 0u);
   return w;
 }
 
@@ -548,7 +594,10 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
                                                            int64_t n, int64_t m, uint32_t gx,
                                                            uint32_t gy, uint32_t n_full,
                                                            uint32_t pieces, int xcd_order,
-                                                           int vec) {
+                                                           int vec, uint32_t* claim) {
+  // the GEMM before it on the stream has handed out all its claims: leave the word at 0
+  if (claim && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr uint32_t parts = kSlabTok / kReduceTok;
   const uint32_t t = n_full + blockIdx.x / parts, part = blockIdx.x % parts;
   uint32_t bx, by;
@@ -945,7 +994,8 @@ __global__ __launch_bounds__(256, Q6K_WG_PER_CU) void gemm_kernel(const uint8_t*
   k.loads_a = k.wave < kWgTokTiles;
   k.tt = k.wave & 1;                                    // token tile of this wave in the workgroup
   k.rp = k.wave >> 1;                                   // row-tile pair of this wave
-  const TileWork tw = tile_work<Q6K_GEMM01_XCD_ORDER != 0>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
+  const TileWork tw = tile_work<Q6K_GEMM01_XCD_ORDER != 0>(blockIdx.x, gx, gy, n_full, pieces,
+                                                           nchunk / 8, ws);
   const uint32_t c0 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * tw.s0));  // chunks [c0, c1)
   k.c1 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * tw.s1));
   k.nchunk = nchunk;
@@ -1275,7 +1325,7 @@ __global__ __launch_bounds__(64 * kFWaves, kFoldedWgPerCu) void folded_kernel(
     DotsOut dots, uint32_t gx, uint32_t gy, uint32_t n_full, uint32_t pieces) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing * kFSlot];
   const WgStamp stamp = wg_stamp();
-  const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8);
+  const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nchunk / 8, ws);
   const bool split = tw.split;
   const uint32_t bx = tw.bx, by = tw.by;
   const int64_t nsb = nchunk / 8;
@@ -1716,7 +1766,7 @@ __global__ __launch_bounds__(256, Q4K_WG_PER_CU) void q4k_gemm_kernel(
   k.loads_a = k.wave < kWgTokTiles;
   const int tt = k.wave & 1, rp = k.wave >> 1;
   const int64_t nsb = nchunk / 8;
-  const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nsb);
+  const TileWork tw = tile_work<true>(blockIdx.x, gx, gy, n_full, pieces, nsb, ws);
   const int64_t T = (int64_t)tw.bx * kWgTokTiles + tt;
   const int64_t R0 = (int64_t)tw.by * 4;
   const int64_t Ta = (int64_t)tw.bx * kWgTokTiles + (k.loads_a ? k.wave : 0);
@@ -1841,9 +1891,17 @@ int device_cus() {
 // `pieces` pieces each; nblocks workgroups in all.
 struct SplitPlan {
   int64_t n_full, pieces, nblocks;
+  uint32_t grade;  // tail_bound's grade of the split tiles' pieces (0: equal, static order)
 };
 
-q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitPlan* sp) {
+// tail_bound's grade of a claimed tail (tile_work): piece i of P weighs P - i.  On ffn_down the
+// layout-2 GEMM ran 1.6 % faster with it than with equal pieces in the static order (468.5
+// against 476.3 us, three alternating same-box runs each; weights P - i + 1: 471.4); the GEMMs of
+// layouts 0/1 and q4_K gained nothing (within +-0.3 %) and keep the static order.
+constexpr uint32_t kTailGrade = 1;
+
+q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, bool claim,
+                      SplitPlan* sp) {
   const int cus = device_cus();
   if (cus <= 0) return Q6K_EHIP;
   const int64_t ntiles = gx * gy, slots = (int64_t)wg_per_cu * cus;
@@ -1857,6 +1915,16 @@ q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, SplitP
   sp->n_full = pieces > 1 ? ntiles - rem : ntiles;
   sp->pieces = pieces;
   sp->nblocks = sp->n_full + (ntiles - sp->n_full) * pieces;
+  // Behind at least one whole round the split tiles' workgroups start staggered: claim their
+  // pieces, largest first, if every graded piece keeps a super-block.
+  sp->grade = 0;
+  if (claim && pieces > 1 && sp->n_full >= slots && pieces <= 0xFFFF) {
+    const uint32_t g = kTailGrade;
+    bool ok = true;
+    for (uint32_t j = 0; j < (uint32_t)pieces; ++j)
+      ok = ok && tail_bound(nsb, (uint32_t)pieces, g, j + 1) > tail_bound(nsb, (uint32_t)pieces, g, j);
+    if (ok) sp->grade = g;
+  }
   return sp->nblocks > INT32_MAX ? Q6K_ESIZE : Q6K_OK;
 }
 
@@ -1865,9 +1933,23 @@ static_assert(kTile * kFTok == kSlabTok && kTile * kWgTokTiles == kSlabTok,
 static_assert(kSlabTok % kReduceTok == 0 && kReduceTok * 128 == 256 * 4,
               "reducing workgroups cover whole tiles, 4 rows per thread");
 
-// Workspace bytes of a plan: one slab per piece of a split tile.
+// Workspace bytes of a plan: one slab per piece of a split tile, then (claimed tail) the 4-byte
+// claim word, in a 256-byte block of its own.
+constexpr size_t kClaimBytes = 256;
 inline size_t plan_workspace_bytes(const SplitPlan& sp) {
-  return (size_t)(sp.nblocks - sp.n_full) * (size_t)kSlabFloats * sizeof(float);
+  return (size_t)(sp.nblocks - sp.n_full) * (size_t)kSlabFloats * sizeof(float) +
+         (sp.grade ? kClaimBytes : 0);
+}
+
+// The claim word of a plan's workspace (after the slabs), or null.
+inline uint32_t* plan_claim_word(const SplitPlan& sp, float* ws) {
+  if (!sp.grade || !ws) return nullptr;
+  return reinterpret_cast<uint32_t*>(ws + (sp.nblocks - sp.n_full) * kSlabFloats);
+}
+
+// The pieces argument of the GEMM kernels: piece count and grade.
+inline uint32_t pieces_arg(const SplitPlan& sp) {
+  return (uint32_t)sp.pieces | (sp.grade << 16);
 }
 
 // The workspace of a launch that needs `need` bytes: 16-byte aligned, at least that large.
@@ -1888,7 +1970,8 @@ void reduce_split_tiles(const SplitPlan& sp, int64_t gx, int64_t gy, bool xcd_or
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(nsplit * (kSlabTok / kReduceTok))),
                        dim3(256), 0, s, ws, y, ldy, n, m, (uint32_t)gx, (uint32_t)gy,
                        (uint32_t)sp.n_full, (uint32_t)sp.pieces, xcd_order ? 1 : 0,
-                       aligned16(y) && ldy % 4 == 0 ? 1 : 0);
+                       aligned16(y) && ldy % 4 == 0 ? 1 : 0,
+                       plan_claim_word(sp, const_cast<float*>(ws)));
 }
 
 q6k_status launch_status() {
@@ -1944,7 +2027,7 @@ q6k_status gemm_plan(int64_t n, int64_t m, int64_t k, int layout, int64_t* gx, i
   *gy = round_up(m, kWgRow) / kWgRow;
   if (*gy > INT32_MAX || *gx > INT32_MAX) return Q6K_ESIZE;
   const int wg_per_cu = layout == Q6K_LAYOUT_FOLDED ? kFoldedWgPerCu : Q6K_WG_PER_CU;
-  return plan_split(*gx, *gy, wg_per_cu, k / 256, sp);
+  return plan_split(*gx, *gy, wg_per_cu, k / 256, layout == Q6K_LAYOUT_FOLDED, sp);
 }
 
 template <int OUT>
@@ -1992,7 +2075,7 @@ q6k_status gemm_common(const void* xq, size_t xq_bytes, const float* da, size_t 
   const dim3 grid((unsigned)sp.nblocks),
       block(layout == Q6K_LAYOUT_FOLDED ? 64 * kFWaves : 256);
   const uint32_t gx32 = (uint32_t)gx, gy32 = (uint32_t)gy, nf = (uint32_t)sp.n_full,
-                 pc = (uint32_t)sp.pieces;
+                 pc = pieces_arg(sp);
   if (layout == Q6K_LAYOUT_FOLDED) {
     const int vec_store = OUT == kOutY && aligned16(y) && ldy % 4 == 0;
     hipLaunchKernelGGL((folded_kernel<kDots>), grid, block, 0, s, a, da, wc, wsc, n, m, nchunk,
@@ -2054,7 +2137,7 @@ q6k_status q4k_gemm_plan(int64_t n, int64_t m, int64_t k, int64_t* gx, int64_t* 
   *gx = round_up(n, kWgTok) / kSlabTok;
   *gy = round_up(m, kWgRow) / kWgRow;
   if (*gy > 65535 || *gx > INT32_MAX) return Q6K_ESIZE;
-  return plan_split(*gx, *gy, Q4K_WG_PER_CU, k / 256, sp);
+  return plan_split(*gx, *gy, Q4K_WG_PER_CU, k / 256, false, sp);
 }
 
 template <bool DOTS>
@@ -2104,7 +2187,7 @@ q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, siz
   hipLaunchKernelGGL((q4k_gemm_kernel<DOTS>), dim3((unsigned)sp.nblocks), dim3(256), 0, s,
                      static_cast<const uint8_t*>(xq), dap, dasp, wc, ws, n, m, nchunk, y, ldy,
                      slabs, dots, (uint32_t)gx, (uint32_t)gy, (uint32_t)sp.n_full,
-                     (uint32_t)sp.pieces);
+                     pieces_arg(sp));
   if (!DOTS) reduce_split_tiles(sp, gx, gy, true, slabs, y, ldy, n, m, s);
   const q6k_status st = launch_status();
   if (st == Q6K_OK) g_q4k_launches.fetch_add(1, std::memory_order_relaxed);
@@ -2117,8 +2200,8 @@ q6k_status q4k_gemm_common(const void* xq, size_t xq_bytes, const float* da, siz
 // array's name as an address: each device's address comes from hipGetSymbolAddress, taken on the
 // first call on that device with the device current, and kept in scratch_addr.
 constexpr int64_t kScratchSlabs = 768;
-constexpr size_t kScratchBytes = (size_t)kScratchSlabs * kSlabFloats * sizeof(float);
-static __device__ __attribute__((aligned(256))) float scratch[kScratchSlabs * kSlabFloats];
+constexpr size_t kScratchBytes = (size_t)kScratchSlabs * kSlabFloats * sizeof(float) + kClaimBytes;
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
 
 constexpr int kMaxDevices = 64;
 std::atomic<void*> scratch_addr[kMaxDevices];

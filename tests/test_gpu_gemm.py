@@ -435,6 +435,43 @@ def test_workspace_rules_and_size():
     np.testing.assert_array_equal(got.view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
 
+def test_claimed_tail_workspace_size_and_garbage_counter():
+    """Layout 2 behind whole rounds hands its graded tail pieces out through a claim counter after
+    the slabs: q6k_gemm_workspace reports the slabs plus 256 bytes, and a caller workspace full of
+    garbage (NaN, so the counter's word too), then the same workspace again, give y bit for bit
+    equal to a binding-allocated one -- the launch sets the counter itself."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    from q6_int8_prefill_amd import _lib
+    L = _lib._lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slots = 2 * cus
+    gx = 2 * ((9 * slots) // (8 * 32))          # about 2.25 rounds of 32 row quads
+    n, m, k = gx * 64 - 104, 4096, 2048         # 2200 x 4096 x 2048 on 256 CUs
+    print(f"claimed tail n={n} m={m} k={k}", flush=True)
+    tiles = (-(-n // 128) * 2) * (m // 128)
+    rem = tiles % slots
+    assert tiles >= 2 * slots and rem
+    pieces = min(slots // rem, k // 256)
+    need = q6k.q6k_gemm_workspace(n, m, k, 2)
+    assert need == rem * pieces * 32768 + 256
+    raw = synthetic.weights(m, k, seed=81)
+    x = synthetic.activations(n, k, seed=82)
+    xq, da = gpu_util.quantize(x)
+    w = gpu_util.expand(raw, m, k, 2)
+    ref = gpu_util.gemm(xq, da, n, w, 2, m, k)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+    for rep in range(2):
+        y = torch.full((n, m), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+        st = L.q6k_gemm(xq.data_ptr(), xq.numel(), da.data_ptr(), da.numel() * 4, n,
+                        w.data_ptr(), w.numel(), 2, m, k, y.data_ptr(), y.numel() * 4, m,
+                        ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 def test_packed_layout_equals_expanded_bit_for_bit():
     """Layout 0 stages 4 (q - 32) and d*sc, so its MFMAs yield 4 D, every rescale product and
     accumulator is exactly 4 times layout 1's (scaling by a power of two commutes with rounding),
