@@ -472,6 +472,40 @@ def test_claimed_tail_workspace_size_and_garbage_counter():
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
+def test_claimed_tails_on_two_streams():
+    """Two layout-2 GEMMs with claimed tails in flight at once on two streams (default priority),
+    each with its own workspace, give their one-at-a-time results bit for bit, three times over:
+    each launch's claims come from its own workspace's counter."""
+    import torch
+    import gpu_util
+    import q6_int8_prefill_amd as q6k
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gx = 2 * ((9 * 2 * cus) // (8 * 32))
+    n, m, k = gx * 64 - 104, 4096, 2048
+    print(f"two streams n={n} m={m} k={k}", flush=True)
+    runs = []
+    for seed in (91, 93):
+        raw = synthetic.weights(m, k, seed=seed)
+        xq, da = gpu_util.quantize(synthetic.activations(n, k, seed=seed + 1))
+        w = gpu_util.expand(raw, m, k, 2)
+        ws = torch.empty(q6k.q6k_gemm_workspace(n, m, k, 2), dtype=torch.uint8,
+                         device=gpu_util.DEV)
+        assert ws.numel() % 32768 == 256                    # the tail is claimed
+        runs.append((xq, da, w, ws, gpu_util.gemm(xq, da, n, w, 2, m, k)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ys = []
+        for (xq, da, w, ws, _), st in zip(runs, streams):
+            y = torch.full((n, m), float("nan"), dtype=torch.float32, device=gpu_util.DEV)
+            ys.append(y)
+            with torch.cuda.stream(st):
+                q6k.q6k_gemm(xq, da, n, w, 2, m, k, y, workspace=ws)
+        torch.cuda.synchronize()
+        for y, (_, _, _, _, ref) in zip(ys, runs):
+            np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 def test_packed_layout_equals_expanded_bit_for_bit():
     """Layout 0 stages 4 (q - 32) and d*sc, so its MFMAs yield 4 D, every rescale product and
     accumulator is exactly 4 times layout 1's (scaling by a power of two commutes with rounding),

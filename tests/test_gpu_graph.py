@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("layout", [2, 1, 0])
-@pytest.mark.parametrize("n,m,k", [(2176, 4096, 2048), (200, 384, 2048)])
+@pytest.mark.parametrize("n,m,k", [(2176, 4096, 2048), (2200, 4096, 2048), (200, 384, 2048)])
 def test_captured_step_replays(n, m, k, layout):
     import torch
     import gpu_util
