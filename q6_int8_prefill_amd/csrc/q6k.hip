@@ -1922,7 +1922,8 @@ q6k_status plan_split(int64_t gx, int64_t gy, int wg_per_cu, int64_t nsb, bool c
     const uint32_t g = kTailGrade;
     bool ok = true;
     for (uint32_t j = 0; j < (uint32_t)pieces; ++j)
-      ok = ok && tail_bound(nsb, (uint32_t)pieces, g, j + 1) > tail_bound(nsb, (uint32_t)pieces, g, j);
+      ok = ok && tail_bound(nsb, (uint32_t)pieces, g, j + 1) >
+                     tail_bound(nsb, (uint32_t)pieces, g, j);
     if (ok) sp->grade = g;
   }
   return sp->nblocks > INT32_MAX ? Q6K_ESIZE : Q6K_OK;
