@@ -1,7 +1,8 @@
 """q6k_gemm_noalloc (the split-k workspace in the library's static device array) against q6k_gemm
-with a caller workspace, through the C ABI: bit for bit on two calls in a row, the first
-splitting every tile of a 512 x 4096 x 4096 problem (on layouts 0/1 into 768 pieces, the whole
-array), the second a smaller problem that must not see the first call's slabs."""
+with a caller workspace, through the C ABI: bit for bit on three calls in a row, each smaller
+than the one before -- 2200 x 4096 x 2048 (whole rounds, then a split tail that layout 2 claims
+through the counter after the slabs), 512 x 4096 x 4096 (every tile split, on layouts 0/1 into
+768 pieces: the whole array), and a small problem that must not see the earlier calls' slabs."""
 import ctypes
 
 import numpy as np
@@ -19,10 +20,10 @@ def test_noalloc_equals_workspace_call(layout):
     import q6_int8_prefill_amd as q6k
     from q6_int8_prefill_amd import _lib
     L = _lib._lib
-    for n, m, k in ((512, 4096, 4096), (200, 384, 2048)):
+    for n, m, k in ((2200, 4096, 2048), (512, 4096, 4096), (200, 384, 2048)):
         print(f"noalloc layout={layout} n={n} m={m} k={k}", flush=True)
         need = q6k.q6k_gemm_workspace(n, m, k, layout)
-        assert 0 < need <= 768 * 32768
+        assert 0 < need <= 768 * 32768 + 256
         raw = synthetic.weights(m, k, seed=n + k + layout, sc_lo=-128, sc_hi=127)
         x = synthetic.activations(n, k, seed=n + 3, kind="outlier")
         xq, da = gpu_util.quantize(x)
